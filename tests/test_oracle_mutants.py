@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one.
+
+Every mutant is a textual edit of one oracle function, re-executed in the oracle module's
+namespace and patched in for the duration of the check run. A mutant that no pin notices would
+mean that part of the oracle is unpinned.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.layer as OL
+from tests import oracle_pins
+
+MUTANTS = [
+    ("rmsnorm", "np.sqrt(ms + eps)", "np.sqrt(ms)"),
+    ("rmsnorm", "np.mean(x * x", "np.sum(x * x"),
+    ("rmsnorm", "np.sqrt(ms + eps) * gain", "np.sqrt(ms + eps)"),
+    ("rope", "a * cos - b * sin", "a * cos + b * sin"),
+    ("rope", "-2.0 * j / d", "-1.0 * j / d"),
+    ("rope", "a = v[..., :half]", "a = v[..., 0::2]"),
+    ("causal_attention", "np.arange(L)[None, :] <= q_pos[:, None]",
+     "np.arange(L)[None, :] <= q_pos[:, None] + 1"),
+    ("causal_attention", "h // group", "h % hkv"),
+    ("causal_attention", ") * scale", ")"),
+    ("silu", "np.exp(-z)", "np.exp(z)"),
+    ("swiglu", "w_gate_up[:d_ff])", "w_gate_up[d_ff:])"),
+    ("sequence_step", "pos_all = num_cached + np.arange(last)", "pos_all = np.arange(last)"),
+    ("sequence_step", "h2 = x_seq[sel] + linear(attn", "h2 = linear(attn"),
+    ("sequence_step", "v_new = linear(h1, v_w).reshape(last, hkv, d)",
+     "v_new = rope(linear(h1, v_w).reshape(last, hkv, d), pos_all, shape.rope_theta)"),
+    ("sequence_step", "h3 = rmsnorm(h2, w[\"mlp_norm\"], shape.rms_eps)", "h3 = h2"),
+    ("sequence_step", "out = h2 + linear(", "out = linear("),
+    ("sequence_step", "q_rot = rope(q, pos, shape.rope_theta)", "q_rot = q"),
+    ("kv_slot_addresses", "positions % block_size", "positions % (block_size + 1)"),
+    ("layer_step", "pos = c + np.arange(n)", "pos = np.arange(n)"),
+]
+
+
+def _mutant(fn_name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(OL, fn_name)))
+    fn = getattr(OL, fn_name)
+    if fn.__doc__:  # edit code, never the docstring
+        src = src.replace(fn.__doc__, "", 1)
+    assert old in src, f"mutation site not found in {fn_name}: {old!r}"
+    ns = dict(vars(OL))
+    exec(compile(src.replace(old, new, 1), f"<mutant {fn_name}>", "exec"), ns)
+    return ns[fn_name]
+
+
+@pytest.mark.parametrize("fn_name,old,new", MUTANTS, ids=[f"{m[0]}:{m[1][:24]}" for m in MUTANTS])
+def test_pins_catch_planted_mistake(monkeypatch, fn_name, old, new):
+    monkeypatch.setattr(OL, fn_name, _mutant(fn_name, old, new))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception:  # an assertion, or NaN/shape fallout of the mistake
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
