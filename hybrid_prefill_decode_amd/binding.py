@@ -1,0 +1,250 @@
+"""ctypes binding of libhybrid_layer.so: the C ABI of include/hybrid_layer.h with the same names.
+
+Argument marshalling only. Torch tensors supply device memory and the stream; every step of the
+layer runs in the library's HIP kernels. There is no fallback: if the shared library is missing
+or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhybrid_layer.so")
+
+HL_OK = 0
+HL_ERR_NULL, HL_ERR_SHAPE, HL_ERR_DESC, HL_ERR_BLOCK = -1, -2, -3, -4
+HL_ERR_ALIGN, HL_ERR_WORKSPACE, HL_ERR_HIP, HL_ERR_ARG = -5, -6, -7, -8
+HL_EPI_NONE, HL_EPI_RESIDUAL, HL_EPI_SWIGLU = 0, 1, 2
+BLOCK_SIZE = 16
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class BatchDesc(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(LayerCfg)), ("num_seqs", ctypes.c_int32),
+                ("num_tokens", ctypes.c_int32), ("q_start", ctypes.c_void_p),
+                ("num_cached", ctypes.c_void_p), ("h_q_start", _c_i32p),
+                ("h_num_cached", _c_i32p), ("x", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stream", ctypes.c_void_p), ("tap_q_rot", ctypes.c_void_p),
+                ("tap_attn_out", ctypes.c_void_p), ("tap_h2", ctypes.c_void_p)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")]
+
+
+class KvPages(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int64)]
+
+
+class BlockTable(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("h_table", _c_i32p),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+class HLError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+_lib = None
+
+# every function the header declares, with its ctypes signature
+_SIGS = {
+    "hl_version": ([], ctypes.c_int),
+    "hl_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "hl_workspace_bytes": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hybrid_layer_step": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(Weights),
+                           ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable), ctypes.c_void_p],
+                          ctypes.c_int),
+    "hl_rmsnorm": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p], ctypes.c_int),
+    "hl_gemm_bf16_nt": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "hl_gemm_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_rope_kv_append": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
+                           ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
+    "hl_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
+                      ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
+    "hl_prefill_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
+                              ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
+    "hl_decode_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
+                             ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               f"`python -m hybrid_prefill_decode_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(handle, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().hl_strerror(code).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != HL_OK:
+        raise HLError(rc, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def layer_cfg(shape, softmax_scale: float = 0.0) -> LayerCfg:
+    """LayerCfg from any object with hidden / n_q_heads / n_kv_heads / head_dim / d_ff
+    (and optionally rms_eps / rope_theta)."""
+    return LayerCfg(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
+                    getattr(shape, "block_size", BLOCK_SIZE), getattr(shape, "rms_eps", 1e-6),
+                    getattr(shape, "rope_theta", 10000.0), softmax_scale)
+
+
+class Batch:
+    """Batch descriptor arrays: host mirrors (numpy int32) plus device copies (torch)."""
+
+    def __init__(self, q_start, num_cached, table, device="cuda"):
+        import torch
+        self.h_q_start = np.ascontiguousarray(q_start, dtype=np.int32)
+        self.h_num_cached = np.ascontiguousarray(num_cached, dtype=np.int32)
+        self.h_table = np.ascontiguousarray(table, dtype=np.int32)
+        self.num_seqs = int(self.h_num_cached.shape[0])
+        self.num_tokens = int(self.h_q_start[-1]) if self.num_seqs else 0
+        self.max_blocks = int(self.h_table.shape[1]) if self.h_table.ndim == 2 else 1
+        self.q_start = torch.from_numpy(self.h_q_start).to(device)
+        self.num_cached = torch.from_numpy(self.h_num_cached).to(device)
+        self.table = torch.from_numpy(self.h_table).to(device)
+
+
+def _desc(cfg: LayerCfg, b: Batch, x=None, workspace=None, stream=None, taps=None,
+          with_stream: bool = True):
+    taps = taps or {}
+    d = BatchDesc()
+    d.cfg = ctypes.pointer(cfg)
+    d.num_seqs = b.num_seqs
+    d.num_tokens = b.num_tokens
+    d.q_start = _ptr(b.q_start)
+    d.num_cached = _ptr(b.num_cached)
+    d.h_q_start = b.h_q_start.ctypes.data_as(_c_i32p)
+    d.h_num_cached = b.h_num_cached.ctypes.data_as(_c_i32p)
+    d.x = _ptr(x)
+    d.workspace = _ptr(workspace)
+    d.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d.stream = _stream_ptr(stream) if with_stream else None
+    d.tap_q_rot = _ptr(taps.get("q_rot"))
+    d.tap_attn_out = _ptr(taps.get("attn_out"))
+    d.tap_h2 = _ptr(taps.get("h2"))
+    return d
+
+
+def _pages(k_pool, v_pool) -> KvPages:
+    return KvPages(_ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]))
+
+
+def _table(b: Batch) -> BlockTable:
+    return BlockTable(_ptr(b.table), b.h_table.ctypes.data_as(_c_i32p), b.max_blocks)
+
+
+def workspace_bytes(cfg: LayerCfg, b: Batch) -> int:
+    d = _desc(cfg, b, with_stream=False)
+    n = ctypes.c_size_t(0)
+    _check(lib().hl_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "hl_workspace_bytes")
+    return int(n.value)
+
+
+def alloc_workspace(cfg: LayerCfg, b: Batch, device="cuda"):
+    import torch
+    n = max(workspace_bytes(cfg, b), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def hybrid_layer_step(cfg: LayerCfg, b: Batch, x, w: Dict[str, object], k_pool, v_pool, out,
+                      workspace, stream=None, taps=None) -> None:
+    d = _desc(cfg, b, x, workspace, stream, taps)
+    wt = Weights(*(_ptr(w[k]) for k in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up",
+                                          "w_down")))
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hybrid_layer_step(ctypes.byref(d), ctypes.byref(wt), ctypes.byref(kv),
+                                   ctypes.byref(bt), _ptr(out)), "hybrid_layer_step")
+
+
+def rmsnorm(x, gain, y, eps: float, stream=None) -> None:
+    rows, cols = x.shape
+    _check(lib().hl_rmsnorm(_ptr(x), _ptr(gain), _ptr(y), rows, cols, eps, _stream_ptr(stream)),
+           "hl_rmsnorm")
+
+
+def gemm_bf16_nt(a, w, c, residual=None, epilogue: int = HL_EPI_NONE, workspace=None,
+                 stream=None) -> None:
+    m, k = a.shape
+    n = w.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hl_gemm_bf16_nt(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), m, n, k, epilogue,
+                                 _ptr(workspace), wsb, _stream_ptr(stream)), "hl_gemm_bf16_nt")
+
+
+def rope_kv_append(cfg: LayerCfg, b: Batch, qkv, q_rot, k_pool, v_pool, stream=None) -> None:
+    d = _desc(cfg, b, stream=stream)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hl_rope_kv_append(ctypes.byref(d), _ptr(qkv), _ptr(q_rot), ctypes.byref(kv),
+                                   ctypes.byref(bt)), "hl_rope_kv_append")
+
+
+def _attn(fn_name, cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream):
+    d = _desc(cfg, b, None, workspace, stream)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(getattr(lib(), fn_name)(ctypes.byref(d), _ptr(q_rot), ctypes.byref(kv),
+                                   ctypes.byref(bt), _ptr(attn_out)), fn_name)
+
+
+def attention(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream=None) -> None:
+    _attn("hl_attention", cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream)
+
+
+def prefill_attention(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream=None) -> None:
+    _attn("hl_prefill_attention", cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream)
+
+
+def decode_attention(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream=None) -> None:
+    _attn("hl_decode_attention", cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream)

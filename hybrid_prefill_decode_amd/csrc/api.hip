@@ -1,0 +1,356 @@
+// Host side of the C ABI: validation on the host mirrors, launch planning, workspace layout and
+// the composition of the layer step out of its phases. Nothing here synchronises the device or
+// allocates device memory; every launch goes onto the caller's stream.
+//
+// Step order (one pre-norm decoder layer over the hybrid token matrix):
+//   plan -> RMSNorm -> QKV GEMM -> RoPE + KV append -> prefill attention | decode attention + merge
+//   -> O GEMM (+x) -> RMSNorm -> gate/up GEMM (SwiGLU) -> down GEMM (+h2)
+// The linear phases see all tokens at once while attention splits by request kind, the
+// operator-level split of the "ConfluxServe" summary ("The big picture: what happens inside one
+// Transformer layer"), here as one GPU's share.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct HostPlan {
+  int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
+  // workspace byte offsets
+  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_h1 = 0, o_qkv = 0, o_qrot = 0,
+         o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0, total = 0;
+};
+
+int check_cfg(const hl_layer_cfg* c) {
+  if (!c) return HL_ERR_NULL;
+  if (c->head_dim != 64 && c->head_dim != 128) return HL_ERR_SHAPE;
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return HL_ERR_SHAPE;
+  if (c->n_q_heads / c->n_kv_heads > 16) return HL_ERR_SHAPE;
+  if (c->hidden <= 0 || c->hidden % 128) return HL_ERR_SHAPE;
+  if (c->d_ff <= 0 || c->d_ff % 64) return HL_ERR_SHAPE;
+  if ((c->n_q_heads * c->head_dim) % 64) return HL_ERR_SHAPE;
+  if (((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 128) return HL_ERR_SHAPE;
+  if (c->block_size != HL_BLOCK_SIZE) return HL_ERR_SHAPE;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->softmax_scale >= 0.f))
+    return HL_ERR_SHAPE;
+  return HL_OK;
+}
+
+// Descriptor checks that need only the host mirrors.
+int check_batch(const hl_batch_desc* b) {
+  if (!b || !b->cfg) return HL_ERR_NULL;
+  int rc = check_cfg(b->cfg);
+  if (rc) return rc;
+  if (b->num_seqs < 0 || b->num_tokens < 0) return HL_ERR_DESC;
+  if (b->num_seqs == 0) return b->num_tokens == 0 ? HL_OK : HL_ERR_DESC;
+  if (!b->h_q_start || !b->h_num_cached || !b->q_start || !b->num_cached) return HL_ERR_NULL;
+  if (b->h_q_start[0] != 0) return HL_ERR_DESC;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const int64_t qlen = (int64_t)b->h_q_start[s + 1] - b->h_q_start[s];
+    if (qlen < 1) return HL_ERR_DESC;
+    if (b->h_num_cached[s] < 0) return HL_ERR_DESC;
+    if ((int64_t)b->h_num_cached[s] + qlen > (int64_t)1 << 30) return HL_ERR_DESC;
+  }
+  if (b->h_q_start[b->num_seqs] != b->num_tokens) return HL_ERR_DESC;
+  return HL_OK;
+}
+
+int check_pages(const hl_batch_desc* b, const hl_kv_pages* kv, const hl_block_table* bt) {
+  if (!kv || !bt) return HL_ERR_NULL;
+  if (!kv->k || !kv->v || !bt->table || !bt->h_table) return HL_ERR_NULL;
+  if (!aligned16(kv->k) || !aligned16(kv->v) || !aligned16(bt->table)) return HL_ERR_ALIGN;
+  if (kv->num_blocks <= 0 || bt->max_blocks_per_seq <= 0) return HL_ERR_BLOCK;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const int64_t kv_len = (int64_t)b->h_num_cached[s] + (b->h_q_start[s + 1] - b->h_q_start[s]);
+    const int64_t need = (kv_len + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+    if (need > bt->max_blocks_per_seq) return HL_ERR_BLOCK;
+    const int32_t* row = bt->h_table + (size_t)s * bt->max_blocks_per_seq;
+    for (int64_t j = 0; j < need; ++j)
+      if (row[j] < 0 || (int64_t)row[j] >= kv->num_blocks) return HL_ERR_BLOCK;
+  }
+  return HL_OK;
+}
+
+// Pages per decode work unit: the smallest power of two in [32, 256] that keeps the decode grid
+// within 16K workgroups (one partial costs about 1/split of the unit's KV bytes in extra traffic).
+int pick_split(const hl_batch_desc* b) {
+  const int hkv = b->cfg->n_kv_heads;
+  for (int sp = 32; sp <= 256; sp *= 2) {
+    int64_t units = 0;
+    for (int s = 0; s < b->num_seqs; ++s) {
+      if (b->h_q_start[s + 1] - b->h_q_start[s] != 1) continue;
+      const int64_t pages = ((int64_t)b->h_num_cached[s] + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+      units += (pages + sp - 1) / sp;
+    }
+    if (units * hkv <= 16384 || sp == 256) return sp;
+  }
+  return 256;
+}
+
+void make_plan(const hl_batch_desc* b, HostPlan* p) {
+  const hl_layer_cfg& c = *b->cfg;
+  *p = HostPlan{};
+  p->split_pages = pick_split(b);
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const int qlen = b->h_q_start[s + 1] - b->h_q_start[s];
+    if (qlen == 1) {
+      const int pages = (b->h_num_cached[s] + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+      p->n_dec_units += (pages + p->split_pages - 1) / p->split_pages;
+      p->n_dec_seqs += 1;
+    } else {
+      p->n_pre_tiles += (qlen + hl::kPrefillQTile - 1) / hl::kPrefillQTile;
+    }
+  }
+  const size_t T = (size_t)b->num_tokens;
+  const size_t qd = (size_t)c.n_q_heads * c.head_dim;
+  const size_t g = (size_t)(c.n_q_heads / c.n_kv_heads);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p->o_dec_units = take(sizeof(int32_t) * 2 * (size_t)p->n_dec_units);
+  p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
+  p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);
+  p->o_h1 = take(2 * T * c.hidden);
+  p->o_qkv = take(2 * T * (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim);
+  p->o_qrot = take(2 * T * qd);
+  p->o_attn = take(2 * T * qd);
+  p->o_h2 = take(2 * T * c.hidden);
+  p->o_mlp = take(2 * T * c.d_ff);
+  p->o_part = take(sizeof(float) * (size_t)p->n_dec_units * c.n_kv_heads * g * (c.head_dim + 2));
+  p->total = off;
+}
+
+hl::Plan device_plan(const HostPlan& hp, void* ws) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  hl::Plan p;
+  p.dec_units = reinterpret_cast<int32_t*>(base + hp.o_dec_units);
+  p.dec_seqs = reinterpret_cast<int32_t*>(base + hp.o_dec_seqs);
+  p.pre_tiles = reinterpret_cast<int32_t*>(base + hp.o_pre_tiles);
+  p.dec_part = reinterpret_cast<float*>(base + hp.o_part);
+  p.n_dec_units = hp.n_dec_units;
+  p.n_dec_seqs = hp.n_dec_seqs;
+  p.n_pre_tiles = hp.n_pre_tiles;
+  p.split_pages = hp.split_pages;
+  p.max_pre_kv = 0;
+  return p;
+}
+
+// Validation shared by every entry point that takes a batch; fills the host plan.
+int prepare(const hl_batch_desc* b, const hl_kv_pages* kv, const hl_block_table* bt,
+            HostPlan* hp) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (b->num_seqs == 0) return HL_OK;
+  if (!aligned16(b->q_start) || !aligned16(b->num_cached)) return HL_ERR_ALIGN;
+  rc = check_pages(b, kv, bt);
+  if (rc) return rc;
+  make_plan(b, hp);
+  if (!b->workspace || b->workspace_bytes < hp->total) return HL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(b->workspace) & (kAlign - 1)) return HL_ERR_ALIGN;
+  for (const void* t : {(const void*)b->tap_q_rot, (const void*)b->tap_attn_out,
+                        (const void*)b->tap_h2})
+    if (t && !aligned16(t)) return HL_ERR_ALIGN;
+  return HL_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? HL_OK : HL_ERR_HIP; }
+
+struct Buffers {
+  hl_bf16 *h1, *qkv, *qrot, *attn, *h2, *mlp;
+};
+
+Buffers buffers(const hl_batch_desc* b, const HostPlan& hp) {
+  uint8_t* base = static_cast<uint8_t*>(b->workspace);
+  Buffers B;
+  B.h1 = reinterpret_cast<hl_bf16*>(base + hp.o_h1);
+  B.qkv = reinterpret_cast<hl_bf16*>(base + hp.o_qkv);
+  B.qrot = b->tap_q_rot ? b->tap_q_rot : reinterpret_cast<hl_bf16*>(base + hp.o_qrot);
+  B.attn = b->tap_attn_out ? b->tap_attn_out : reinterpret_cast<hl_bf16*>(base + hp.o_attn);
+  B.h2 = b->tap_h2 ? b->tap_h2 : reinterpret_cast<hl_bf16*>(base + hp.o_h2);
+  B.mlp = reinterpret_cast<hl_bf16*>(base + hp.o_mlp);
+  return B;
+}
+
+int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_kv_pages* kv,
+                  const hl_block_table* bt, hl_bf16* attn_out, const HostPlan& hp,
+                  bool do_prefill, bool do_decode) {
+  hipStream_t st = static_cast<hipStream_t>(b->stream);
+  const hl::Plan dp = device_plan(hp, b->workspace);
+  int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, hp.split_pages,
+                                  hl::kPrefillQTile, dp, st));
+  if (rc) return rc;
+  if (do_prefill) {
+    rc = hip_rc(hl::launch_prefill_attention(*b->cfg, b->q_start, b->num_cached, q_rot, kv->k,
+                                             kv->v, kv->num_blocks, bt->table,
+                                             bt->max_blocks_per_seq, dp, attn_out, st));
+    if (rc) return rc;
+  }
+  if (do_decode) {
+    rc = hip_rc(hl::launch_decode_attention(*b->cfg, b->q_start, b->num_cached, q_rot, kv->k,
+                                            kv->v, kv->num_blocks, bt->table,
+                                            bt->max_blocks_per_seq, dp, attn_out, st));
+  }
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hl_version(void) { return HL_VERSION; }
+
+const char* hl_strerror(int code) {
+  switch (code) {
+    case HL_OK: return "ok";
+    case HL_ERR_NULL: return "a required pointer is NULL";
+    case HL_ERR_SHAPE: return "unsupported layer dimensions";
+    case HL_ERR_DESC: return "invalid batch descriptor (q_start / num_cached / num_tokens)";
+    case HL_ERR_BLOCK: return "block table too short or block id out of range";
+    case HL_ERR_ALIGN: return "device pointer not 16-byte aligned (workspace: 256-byte)";
+    case HL_ERR_WORKSPACE: return "workspace missing or too small";
+    case HL_ERR_HIP: return "HIP kernel launch failed";
+    case HL_ERR_ARG: return "invalid argument";
+    default: return "unknown error code";
+  }
+}
+
+int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes) {
+  if (!bytes) return HL_ERR_NULL;
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  HostPlan hp;
+  if (batch->num_seqs == 0) {
+    *bytes = 0;
+    return HL_OK;
+  }
+  make_plan(batch, &hp);
+  *bytes = hp.total;
+  return HL_OK;
+}
+
+int hl_rmsnorm(const hl_bf16* x, const hl_bf16* gain, hl_bf16* y, int32_t rows, int32_t cols,
+               float eps, void* stream) {
+  if (!x || !gain || !y) return HL_ERR_NULL;
+  if (rows < 0 || cols <= 0 || cols % 8 || !(eps >= 0.f)) return HL_ERR_ARG;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(y)) return HL_ERR_ALIGN;
+  return hip_rc(hl::launch_rmsnorm(x, gain, y, rows, cols, eps, static_cast<hipStream_t>(stream)));
+}
+
+int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, size_t* bytes) {
+  if (!bytes) return HL_ERR_NULL;
+  *bytes = hl::gemm_workspace_bytes(m, n, k, epilogue);
+  return HL_OK;
+}
+
+int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
+                    int32_t m, int32_t n, int32_t k, int32_t epilogue, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!a || !w || !c) return HL_ERR_NULL;
+  if (epilogue != HL_EPI_NONE && epilogue != HL_EPI_RESIDUAL && epilogue != HL_EPI_SWIGLU)
+    return HL_ERR_ARG;
+  if (epilogue == HL_EPI_RESIDUAL && !residual) return HL_ERR_NULL;
+  if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(c) || (residual && !aligned16(residual)))
+    return HL_ERR_ALIGN;
+  return hip_rc(hl::launch_gemm(a, w, c, residual, m, n, k, epilogue, workspace, workspace_bytes,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,
+                      hl_kv_pages* kv, const hl_block_table* bt) {
+  HostPlan hp;
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (batch->num_seqs == 0) return HL_OK;
+  if (!qkv || !q_rot) return HL_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(q_rot)) return HL_ERR_ALIGN;
+  rc = check_pages(batch, kv, bt);
+  if (rc) return rc;
+  (void)hp;
+  return hip_rc(hl::launch_rope_append(*batch->cfg, batch->num_seqs, batch->num_tokens,
+                                       batch->q_start, batch->num_cached, qkv, q_rot, kv->k,
+                                       kv->v, kv->num_blocks, bt->table, bt->max_blocks_per_seq,
+                                       static_cast<hipStream_t>(batch->stream)));
+}
+
+static int attention_entry(const hl_batch_desc* batch, const hl_bf16* q_rot,
+                           const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                           bool pre, bool dec) {
+  HostPlan hp;
+  int rc = prepare(batch, kv, bt, &hp);
+  if (rc) return rc;
+  if (batch->num_seqs == 0) return HL_OK;
+  if (!q_rot || !attn_out) return HL_ERR_NULL;
+  if (!aligned16(q_rot) || !aligned16(attn_out)) return HL_ERR_ALIGN;
+  return run_attention(batch, q_rot, kv, bt, attn_out, hp, pre, dec);
+}
+
+int hl_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
+                 const hl_block_table* bt, hl_bf16* attn_out) {
+  return attention_entry(batch, q_rot, kv, bt, attn_out, true, true);
+}
+int hl_prefill_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
+                         const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out) {
+  return attention_entry(batch, q_rot, kv, bt, attn_out, true, false);
+}
+int hl_decode_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
+                        const hl_block_table* bt, hl_bf16* attn_out) {
+  return attention_entry(batch, q_rot, kv, bt, attn_out, false, true);
+}
+
+int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
+                      const hl_block_table* bt, hl_bf16* out) {
+  HostPlan hp;
+  int rc = prepare(batch, kv, bt, &hp);
+  if (rc) return rc;
+  if (batch->num_seqs == 0) return HL_OK;
+  if (!w || !out || !batch->x) return HL_ERR_NULL;
+  if (!aligned16(batch->x)) return HL_ERR_ALIGN;
+  if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
+    return HL_ERR_NULL;
+  for (const void* p : {(const void*)w->attn_norm, (const void*)w->w_qkv, (const void*)w->w_o,
+                        (const void*)w->mlp_norm, (const void*)w->w_gate_up,
+                        (const void*)w->w_down, (const void*)out})
+    if (!aligned16(p)) return HL_ERR_ALIGN;
+  if ((const void*)out == (const void*)batch->x) return HL_ERR_ARG;
+
+  const hl_layer_cfg& c = *batch->cfg;
+  const int T = batch->num_tokens;
+  const int qkv_cols = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int qd = c.n_q_heads * c.head_dim;
+  hipStream_t st = static_cast<hipStream_t>(batch->stream);
+  const Buffers B = buffers(batch, hp);
+
+  if ((rc = hip_rc(hl::launch_rmsnorm(batch->x, w->attn_norm, B.h1, T, c.hidden, c.rms_eps, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_qkv, B.qkv, nullptr, T, qkv_cols, c.hidden,
+                                   HL_EPI_NONE, nullptr, 0, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_rope_append(c, batch->num_seqs, T, batch->q_start,
+                                          batch->num_cached, B.qkv, B.qrot, kv->k, kv->v,
+                                          kv->num_blocks, bt->table, bt->max_blocks_per_seq, st))))
+    return rc;
+  if ((rc = run_attention(batch, B.qrot, kv, bt, B.attn, hp, true, true))) return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, batch->x, T, c.hidden, qd,
+                                   HL_EPI_RESIDUAL, nullptr, 0, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_rmsnorm(B.h2, w->mlp_norm, B.h1, T, c.hidden, c.rms_eps, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, nullptr, T, 2 * c.d_ff, c.hidden,
+                                   HL_EPI_SWIGLU, nullptr, 0, st))))
+    return rc;
+  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, B.h2, T, c.hidden, c.d_ff,
+                                HL_EPI_RESIDUAL, nullptr, 0, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Device-side primitives shared by the gfx950 kernels of the hybrid layer step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hybrid_layer.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define HL_DEV __device__ __forceinline__
+
+// bf16 <-> fp32. bf16 is the top half of an fp32; the narrowing rounds to nearest even.
+HL_DEV float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+HL_DEV float bf_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+HL_DEV float bf_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+HL_DEV uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+HL_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+HL_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Matrix-core products (CDNA4): D = A B + C with 8 bf16 of A and of B per lane.
+HL_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+HL_DEV f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+HL_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+HL_DEV float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// Internal launchers (each returns hipSuccess or the launch error).
+namespace hl {
+
+struct Plan {
+  // device work lists inside the workspace
+  int32_t* dec_units;      // [n_dec_units][2]: (seq, first page)
+  int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
+  int32_t* pre_tiles;      // [n_pre_tiles][2]: (seq, first query row within the sequence)
+  float* dec_part;         // [n_dec_units][Hkv][group][head_dim + 2] partial (o, m, l)
+  int32_t n_dec_units, n_dec_seqs, n_pre_tiles;
+  int32_t split_pages;     // pages per decode work unit
+  int32_t max_pre_kv;      // longest key range of any prefill tile (host-side estimate)
+};
+
+hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
+                       int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
+hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
+                          int32_t cols, float eps, hipStream_t st);
+hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* res,
+                       int32_t m, int32_t n, int32_t k, int32_t epi, void* ws, size_t ws_bytes,
+                       hipStream_t st);
+size_t gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epi);
+hipError_t launch_rope_append(const hl_layer_cfg& cfg, int32_t num_seqs, int32_t num_tokens,
+                              const int32_t* q_start, const int32_t* num_cached,
+                              const hl_bf16* qkv, hl_bf16* q_rot, hl_bf16* kpool,
+                              hl_bf16* vpool, int64_t num_blocks, const int32_t* table,
+                              int32_t max_blocks, hipStream_t st);
+hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
+                                    const int32_t* num_cached, const hl_bf16* q_rot,
+                                    const hl_bf16* kpool, const hl_bf16* vpool,
+                                    int64_t num_blocks, const int32_t* table, int32_t max_blocks,
+                                    const Plan& plan, hl_bf16* attn_out, hipStream_t st);
+hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
+                                   const int32_t* num_cached, const hl_bf16* q_rot,
+                                   const hl_bf16* kpool, const hl_bf16* vpool,
+                                   int64_t num_blocks, const int32_t* table, int32_t max_blocks,
+                                   const Plan& plan, hl_bf16* attn_out, hipStream_t st);
+
+constexpr int kPrefillQTile = 128;  // query rows per prefill work tile
+
+}  // namespace hl

@@ -1,0 +1,209 @@
+/*
+ * hybrid_layer.h - C ABI of one transformer-layer forward step over a hybrid batch on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation. A hybrid batch stacks the new tokens of prompt chunks and of decoding requests
+ * into one token matrix. The linear layers (QKV, output projection, SwiGLU MLP) multiply that
+ * whole matrix by the same weights, so the weights are read once for both phases; attention then
+ * splits, because each request attends only to its own keys and values ("ConfluxServe:
+ * Reconciling Resource Utilization and Parallelism Efficiency across Prefill and Decode in LLM
+ * Serving", sections "The big picture: what happens inside one Transformer layer" and "Why can
+ * linear layers be batched but attention cannot?"). Every request brings a start position (tokens
+ * already in the KV cache) and a count of new tokens; prompt chunks write their keys and values
+ * into the paged cache and attend causally to everything cached for their request, decodes
+ * append one token ("Chunked prefill (stall-free batching), explained", "How it works, step by
+ * step"). A query at absolute position p sees keys 0..p; query head h reads KV head
+ * h / (n_q_heads / n_kv_heads) ("7.8 Disaggregated Prefill/Decode & Chunked Prefill", "Attention
+ * on Partial KV Caches" and its GQA exercise).
+ *
+ * Layer definition (pre-norm, no biases):
+ *   h1  = RMSNorm(x) * attn_norm                      RMSNorm(z) = z / sqrt(mean(z^2) + eps)
+ *   qkv = h1 W_qkv^T            -> q [T, Hq, d], k, v [T, Hkv, d]
+ *   q, k rotated at position num_cached[s] + i: pair (j, j + d/2) turns by p * theta^(-2j/d)
+ *   k, v appended to the paged cache; o = causal softmax(q K^T * scale) V per request
+ *   h2  = x + o W_o^T
+ *   out = h2 + (silu(h3 W_gate^T) * (h3 W_up^T)) W_down^T,   h3 = RMSNorm(h2) * mlp_norm
+ * A sequence with q_len == 1 takes the decode path (split-KV attention); q_len > 1 takes the
+ * prefill path (tiled causal attention). Both produce the same mathematics.
+ *
+ * Numbers: bf16 storage (raw bits, round-to-nearest-even), fp32 accumulation and fp32 softmax.
+ *
+ * Memory. Every pointer marked "device" is HIP device memory of the current device, 16-byte
+ * aligned. "host" pointers are ordinary host memory, read only during the call. The caller
+ * allocates and frees everything (weights, cache pools, tables, x, out, workspace, stream); the
+ * library allocates nothing and keeps no state between calls.
+ *
+ * Execution. Calls are asynchronous: they validate on the host, enqueue kernels on `stream` and
+ * return. Results are valid once the stream has completed. No call synchronises the device.
+ * Calls with distinct workspaces may run concurrently on different streams.
+ *
+ * Errors. Every entry point returns HL_OK (0) or a negative HL_ERR_* code. Validation reads only
+ * the host mirrors and happens before anything is enqueued: on a validation error nothing is
+ * launched and nothing is written.
+ */
+#ifndef HYBRID_LAYER_H
+#define HYBRID_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HL_VERSION 1
+#define HL_BLOCK_SIZE 16 /* tokens per KV page */
+
+enum {
+  HL_OK = 0,
+  HL_ERR_NULL = -1,      /* a required pointer is NULL */
+  HL_ERR_SHAPE = -2,     /* unsupported layer dimensions (see hl_layer_cfg) */
+  HL_ERR_DESC = -3,      /* bad batch descriptor: q_len < 1, q_start not starting at 0 or not
+                            increasing, q_start[S] != num_tokens, num_cached < 0 */
+  HL_ERR_BLOCK = -4,     /* a sequence needs more than max_blocks_per_seq pages, or a used
+                            block id lies outside [0, num_blocks) */
+  HL_ERR_ALIGN = -5,     /* a device pointer is not 16-byte aligned */
+  HL_ERR_WORKSPACE = -6, /* workspace NULL or smaller than hl_workspace_bytes() */
+  HL_ERR_HIP = -7,       /* a kernel launch failed */
+  HL_ERR_ARG = -8        /* other invalid argument (sizes, epilogue id) */
+};
+
+typedef uint16_t hl_bf16; /* raw bfloat16 bits */
+
+/* Layer dimensions. Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0 and
+ * n_q_heads / n_kv_heads <= 16; hidden % 64 == 0; d_ff % 64 == 0; n_q_heads * head_dim % 64 == 0;
+ * block_size == HL_BLOCK_SIZE. softmax_scale == 0 means 1 / sqrt(head_dim). */
+typedef struct {
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t d_ff;
+  int32_t block_size;
+  float rms_eps;
+  float rope_theta;
+  float softmax_scale;
+} hl_layer_cfg;
+
+/* One hybrid batch. Sequence s owns token rows q_start[s] .. q_start[s+1]-1 of x and out; those
+ * rows are its new tokens at positions num_cached[s] .. num_cached[s] + q_len - 1. Rows may come
+ * in any sequence order (the benchmarks put prompt chunks first, then decodes).
+ * q_start / num_cached are given twice: on the device (read by kernels) and as host mirrors
+ * (validation and launch planning, so the call never waits for the device); both must hold the
+ * same values. The tap pointers, when non-NULL, receive copies of intermediate tensors:
+ * tap_q_rot [T, Hq*d] (rotated queries), tap_attn_out [T, Hq*d] (attention output before W_o),
+ * tap_h2 [T, hidden] (residual stream after attention). */
+typedef struct {
+  const hl_layer_cfg* cfg;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  const int32_t* q_start;      /* device [num_seqs + 1] */
+  const int32_t* num_cached;   /* device [num_seqs] */
+  const int32_t* h_q_start;    /* host   [num_seqs + 1] */
+  const int32_t* h_num_cached; /* host   [num_seqs] */
+  const hl_bf16* x;            /* device [num_tokens, hidden] */
+  void* workspace;             /* device, hl_workspace_bytes() bytes, 256-byte aligned */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t; NULL = the null stream */
+  hl_bf16* tap_q_rot;          /* device, optional */
+  hl_bf16* tap_attn_out;       /* device, optional */
+  hl_bf16* tap_h2;             /* device, optional */
+} hl_batch_desc;
+
+/* Weights, all device, row-major [out_features, in_features] (each row one output feature). */
+typedef struct {
+  const hl_bf16* attn_norm; /* [hidden] */
+  const hl_bf16* w_qkv;     /* [(Hq + 2 Hkv) d, hidden]: q rows, then k rows, then v rows */
+  const hl_bf16* w_o;       /* [hidden, Hq d] */
+  const hl_bf16* mlp_norm;  /* [hidden] */
+  const hl_bf16* w_gate_up; /* [2 d_ff, hidden]: the d_ff gate rows, then the d_ff up rows */
+  const hl_bf16* w_down;    /* [hidden, d_ff] */
+} hl_weights;
+
+/* Paged KV cache of this layer. Each (block, kv head) page is one contiguous 4 KB run (for
+ * d = 128), as the head-before-token layout of "Gescheiden Prefill en Decode" (section on
+ * sharded KV cache transfers) keeps a head's page contiguous:
+ *   k: [num_blocks][n_kv_heads][16 tokens][head_dim]   (token-major page: K rows)
+ *   v: [num_blocks][n_kv_heads][head_dim][16 tokens]   (dim-major page: V columns)
+ * Keys are stored after the rotary embedding. The step writes only the slots of its new tokens;
+ * every other byte is left as it was. Pages written by one step must not be shared between
+ * sequences. */
+typedef struct {
+  hl_bf16* k;
+  hl_bf16* v;
+  int64_t num_blocks;
+} hl_kv_pages;
+
+/* Block table: row s maps logical page j of sequence s (positions 16j .. 16j+15) to a physical
+ * block id. Device copy for the kernels, host mirror for validation; entries beyond
+ * ceil((num_cached + q_len) / 16) of a row are never read. */
+typedef struct {
+  const int32_t* table;   /* device [num_seqs, max_blocks_per_seq] */
+  const int32_t* h_table; /* host   [num_seqs, max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+} hl_block_table;
+
+/* ---- the step ------------------------------------------------------------------------------ */
+
+/* One forward pass of the layer over the hybrid batch: writes out [num_tokens, hidden] (device)
+ * and appends the batch's new K/V rows into kv. `out` must not alias x, the cache or the
+ * workspace. Returns HL_OK or an HL_ERR_* code (nothing launched on a validation error). */
+int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* weights, hl_kv_pages* kv,
+                      const hl_block_table* block_table, hl_bf16* out);
+
+/* Workspace the step (and the phase entries) need for this batch, from the host mirrors only.
+ * Writes the byte count to *bytes. */
+int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes);
+
+/* Static text for an HL_* code; never NULL. */
+const char* hl_strerror(int code);
+
+/* HL_VERSION of the library. */
+int hl_version(void);
+
+/* ---- the phases the step is composed of (same conventions; used by tests and benchmarks) --- */
+
+/* y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain, rows x cols, all device bf16.
+ * cols % 8 == 0. */
+int hl_rmsnorm(const hl_bf16* x, const hl_bf16* gain, hl_bf16* y, int32_t rows, int32_t cols,
+               float eps, void* stream);
+
+/* Token-batched linear layer C = A W^T with A [m, k] and W [n, k] (both k-contiguous), bf16 in,
+ * fp32 accumulation, bf16 out. epilogue:
+ *   HL_EPI_NONE     c [m, n] = A W^T
+ *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + A W^T
+ *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
+ *                   c [m, f] = silu(A W_gate^T) * (A W_up^T)
+ * Requirements: k % 64 == 0, n % 64 == 0 (n % 128 == 0 for SWIGLU), m >= 1. `workspace` may be
+ * NULL; when given (hl_gemm_workspace_bytes) small-m shapes may use a split-k schedule. */
+enum { HL_EPI_NONE = 0, HL_EPI_RESIDUAL = 1, HL_EPI_SWIGLU = 2 };
+int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
+                    int32_t m, int32_t n, int32_t k, int32_t epilogue, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, size_t* bytes);
+
+/* Rotary embedding of q and k and KV append. qkv [num_tokens, (Hq + 2 Hkv) d] (device, the QKV
+ * projection output); writes q_rot [num_tokens, Hq d] and the new K (rotated) and V rows into
+ * their pages: position p of sequence s goes to block table[s][p / 16], slot p % 16. */
+int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,
+                      hl_kv_pages* kv, const hl_block_table* block_table);
+
+/* Attention of every sequence of the batch over its cached keys plus its new ones (the new K/V
+ * must already be in the cache, as hl_rope_kv_append leaves them). q_rot [T, Hq d] device;
+ * writes attn_out [T, Hq d]. Uses the batch workspace. hl_attention runs both paths;
+ * hl_prefill_attention only rows of sequences with q_len > 1, hl_decode_attention only rows of
+ * sequences with q_len == 1 (other rows are left untouched). */
+int hl_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
+                 const hl_block_table* block_table, hl_bf16* attn_out);
+int hl_prefill_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
+                         const hl_kv_pages* kv, const hl_block_table* block_table,
+                         hl_bf16* attn_out);
+int hl_decode_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
+                        const hl_kv_pages* kv, const hl_block_table* block_table,
+                        hl_bf16* attn_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_LAYER_H */

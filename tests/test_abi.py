@@ -1,0 +1,182 @@
+"""C-ABI library: it loads without a GPU, exports every symbol the header declares, and rejects
+invalid calls on the host before anything is launched (CPU only; no compute call is made).
+
+A validation failure is detected on the host mirrors and returns its own code; had the call gone
+on to launch a kernel on this GPU-less machine it would have come back as HL_ERR_HIP instead, so
+each expected code also shows that nothing was launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from hybrid_prefill_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hybrid_layer.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hl_[a-z_0-9]+|hybrid_layer_step)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("hybrid_layer_step", "hl_workspace_bytes", "hl_strerror", "hl_version",
+              "hl_rmsnorm", "hl_gemm_bf16_nt", "hl_rope_kv_append", "hl_attention",
+              "hl_prefill_attention", "hl_decode_attention"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"{n} declared in include/hybrid_layer.h but not exported"
+    # the binding wraps the same set, under the same names
+    assert set(_declared_functions()) == set(B._SIGS)
+
+
+def test_version_and_strerror():
+    assert B.lib().hl_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
+        s = B.strerror(code)
+        assert isinstance(s, str) and s
+
+
+# ---------------------------------------------------------------------- host-forced failures
+
+def _fake_batch(seqs, shape=None, table=None, pool=64):
+    """Descriptor pieces backed by CPU memory: validation never dereferences device pointers."""
+    shape = shape or workloads.SHAPES["tiny"]
+    spec = workloads.custom_spec(shape, seqs, seed=1, pool_slack=1.0)
+    if table is None:
+        table, pool = workloads.block_table(spec)
+    b = B.Batch(spec.q_start, spec.num_cached, table, device="cpu")
+    return spec, b, pool
+
+
+def _step(spec, b, pool, ws_bytes=None, cfg=None, x_off=0, out=None):
+    cfg = cfg or B.layer_cfg(spec.shape)
+    s = spec.shape
+    x = torch.zeros(max(spec.num_tokens, 1) * s.hidden + 64, dtype=torch.bfloat16)
+    kp = torch.zeros(pool * s.n_kv_heads * 16 * s.head_dim, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    need = B.workspace_bytes(cfg, b) if ws_bytes is None else ws_bytes
+    ws = torch.zeros(max(need, 1) + 512, dtype=torch.uint8)
+    # 256-byte aligned view of the workspace
+    off = (-ws.data_ptr()) % 256
+    d = B._desc(cfg, b, None, None, None, with_stream=False)
+    d.x = x.data_ptr() + x_off
+    d.workspace = ws.data_ptr() + off
+    d.workspace_bytes = need
+    w = torch.zeros(4096, dtype=torch.bfloat16)
+    wt = B.Weights(*([w.data_ptr()] * 6))
+    kv = B.KvPages(kp.data_ptr(), vp.data_ptr(), pool)
+    bt = B.BlockTable(b.table.data_ptr(), b.h_table.ctypes.data_as(B._c_i32p), b.max_blocks)
+    o = torch.zeros_like(x) if out is None else out
+    return B.lib().hybrid_layer_step(ctypes.byref(d), ctypes.byref(wt), ctypes.byref(kv),
+                                     ctypes.byref(bt), o.data_ptr())
+
+
+def test_rejects_bad_block_id():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    b.h_table[1, 0] = pool  # one past the pool
+    assert _step(spec, b, pool) == B.HL_ERR_BLOCK
+    b.h_table[1, 0] = -1
+    assert _step(spec, b, pool) == B.HL_ERR_BLOCK
+
+
+def test_rejects_row_too_short_for_context():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    # sequence 0 needs ceil(24 / 16) = 2 pages; a 1-column table cannot hold it
+    short = np.ascontiguousarray(b.h_table[:, :1])
+    b2 = B.Batch(spec.q_start, spec.num_cached, short, device="cpu")
+    assert _step(spec, b2, pool) == B.HL_ERR_BLOCK
+
+
+def test_rejects_empty_query_and_bad_q_start():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    b.h_q_start[:] = [0, 4, 4]  # q_len = 0 for sequence 1
+    assert _step(spec, b, pool, ws_bytes=1 << 20) == B.HL_ERR_DESC
+    b.h_q_start[:] = [1, 4, 5]  # does not start at 0
+    assert _step(spec, b, pool, ws_bytes=1 << 20) == B.HL_ERR_DESC
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    b.h_num_cached[0] = -3
+    assert _step(spec, b, pool, ws_bytes=1 << 20) == B.HL_ERR_DESC
+
+
+def test_rejects_misaligned_pointer():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    assert _step(spec, b, pool, x_off=2) == B.HL_ERR_ALIGN
+
+
+def test_rejects_small_workspace():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    need = B.workspace_bytes(B.layer_cfg(spec.shape), b)
+    assert need > 0
+    assert _step(spec, b, pool, ws_bytes=need - 256) == B.HL_ERR_WORKSPACE
+
+
+def test_rejects_bad_shapes():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    bad = [
+        workloads.LayerShape(256, 5, 2, 64, 512),    # Hq % Hkv != 0
+        workloads.LayerShape(256, 4, 2, 96, 512),    # head_dim not 64 / 128
+        workloads.LayerShape(200, 4, 2, 64, 512),    # hidden % 128 != 0
+        workloads.LayerShape(256, 4, 2, 64, 500),    # d_ff % 64 != 0
+        workloads.LayerShape(256, 34, 2, 64, 512),   # group of 17 heads
+    ]
+    for s in bad:
+        assert _step(spec, b, pool, cfg=B.layer_cfg(s), ws_bytes=1 << 24) == B.HL_ERR_SHAPE, s
+    cfg = B.layer_cfg(spec.shape)
+    cfg.block_size = 32
+    assert _step(spec, b, pool, cfg=cfg, ws_bytes=1 << 24) == B.HL_ERR_SHAPE
+
+
+def test_rejects_out_aliasing_x_and_null_weights():
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    cfg = B.layer_cfg(spec.shape)
+    d = B._desc(cfg, b, None, None, None, with_stream=False)
+    assert B.lib().hybrid_layer_step(ctypes.byref(d), None, None, None, None) in (
+        B.HL_ERR_NULL, B.HL_ERR_WORKSPACE)
+
+
+def test_empty_batch_is_a_no_op():
+    cfg = B.layer_cfg(workloads.SHAPES["tiny"])
+    b = B.Batch(np.array([0]), np.zeros(0), np.full((1, 1), -1), device="cpu")
+    assert B.workspace_bytes(cfg, b) == 0
+    d = B._desc(cfg, b, None, None, None, with_stream=False)
+    assert B.lib().hybrid_layer_step(ctypes.byref(d), None, None, None, None) == B.HL_OK
+
+
+def test_workspace_bytes_matches_plan_of_all_workloads():
+    for cfgid in range(1, 6):
+        spec = workloads.make_spec(cfgid)
+        table, pool = workloads.block_table(spec)
+        b = B.Batch(spec.q_start, spec.num_cached, table, device="cpu")
+        n = B.workspace_bytes(B.layer_cfg(spec.shape), b)
+        s = spec.shape
+        T = spec.num_tokens
+        floor = 2 * T * (2 * s.hidden + s.qkv_cols + 2 * s.n_q_heads * s.head_dim + s.d_ff)
+        assert floor <= n < floor + (1 << 30), (cfgid, n, floor)
+
+
+def test_gemm_and_rmsnorm_argument_checks():
+    t = torch.zeros(64 * 128, dtype=torch.bfloat16)
+    p = t.data_ptr()
+    L = B.lib()
+    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 100, 64, 0, None, 0, None) == B.HL_ERR_ARG  # n % 128
+    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 60, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
+    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 64, 7, None, 0, None) == B.HL_ERR_ARG  # epilogue
+    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 64, 1, None, 0, None) == B.HL_ERR_NULL  # residual
+    assert L.hl_gemm_bf16_nt(p + 2, p, p, None, 8, 128, 64, 0, None, 0, None) == B.HL_ERR_ALIGN
+    assert L.hl_rmsnorm(p, p, p, 4, 12, 1e-6, None) == B.HL_ERR_ARG
+    assert L.hl_rmsnorm(None, p, p, 4, 16, 1e-6, None) == B.HL_ERR_NULL

@@ -1,0 +1,298 @@
+"""GPU parity: every phase and the whole hybrid layer step against the fp64 oracle, through the
+C ABI. Tolerance (from the step's bf16 storage / fp32 accumulation): max|gpu - ref| <=
+1e-2 * max|ref| per output tensor, attention checked separately on prompt-chunk rows and decode
+rows. KV placement is bit-exact: the set of written (block, head, slot) addresses equals the
+oracle's, and every other byte of both pools is unchanged.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layer as OL
+import workloads
+from hybrid_prefill_decode_amd import binding as B
+from tests._gpu import (DeviceCase, assert_close, bits, changed_slots, make_pools, rel_err, say,
+                        SENTINEL)
+from tests._util import f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _randn(shape, seed, std=1.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(*shape, generator=g, device=DEV) * std).to(torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------- phases
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 64), (68, 512, 256), (130, 384, 320), (257, 256, 128),
+                                   (1040, 1024, 512)])
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
+def test_gemm_vs_oracle(m, n, k, epi):
+    say(f"gemm m={m} n={n} k={k} epi={epi}")
+    a = _randn((m, k), 1 + m)
+    w = _randn((n, k), 2 + n, 0.05)
+    res = _randn((m, n // 2 if epi == B.HL_EPI_SWIGLU else n), 3 + k)
+    out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
+    c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt(a, w, c, res if epi == B.HL_EPI_RESIDUAL else None, epi)
+    torch.cuda.synchronize()
+    A, W = f64(a), f64(w)
+    if epi == B.HL_EPI_SWIGLU:
+        ref = OL.swiglu(A, W, n // 2)
+    else:
+        ref = OL.linear(A, W)
+        if epi == B.HL_EPI_RESIDUAL:
+            ref = ref + f64(res)
+    assert_close(f64(c), ref, "gemm")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (68, 256), (5, 8192), (3, 20480)])
+def test_rmsnorm_vs_oracle(rows, cols):
+    say(f"rmsnorm rows={rows} cols={cols}")
+    x = _randn((rows, cols), 10 + cols)
+    g = (1.0 + _randn((cols,), 11, 0.1).float()).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    B.rmsnorm(x, g, y, 1e-6)
+    torch.cuda.synchronize()
+    assert_close(f64(y), OL.rmsnorm(f64(x), f64(g), 1e-6), "rmsnorm")
+
+
+def _attention_inputs(spec, seed):
+    """Pools holding seeded K/V for every position 0..c+n-1 (the state after the append) and a
+    seeded q_rot, so attention is checked on its own."""
+    s = spec.shape
+    table, pool = workloads.block_table(spec)
+    full = workloads.custom_spec(s, [(c + n, n) for c, n in spec.seqs], spec.seed)
+    kp, vp = make_pools(full, table, pool, DEV)
+    q = _randn((spec.num_tokens, s.n_q_heads * s.head_dim), seed)
+    return table, pool, full, kp, vp, q
+
+
+def _oracle_attention(spec, full, q):
+    s = spec.shape
+    ref = np.zeros((spec.num_tokens, s.n_q_heads * s.head_dim))
+    Q = f64(q).reshape(spec.num_tokens, s.n_q_heads, s.head_dim)
+    for si, (c, n) in enumerate(spec.seqs):
+        k, v = workloads.cached_kv(full, si, DEV)
+        r0 = int(spec.q_start[si])
+        pos = c + np.arange(n)
+        o = OL.causal_attention(Q[r0:r0 + n], f64(k), f64(v), pos, 1.0 / math.sqrt(s.head_dim))
+        ref[r0:r0 + n] = o.reshape(n, -1)
+    return ref
+
+
+ATTN_CASES = {
+    "cfg1": (workloads.SHAPES["tiny"], None),
+    "ragged": (workloads.SHAPES["tiny"], [(0, 2), (3, 129), (45, 1), (0, 1), (15, 1), (16, 1),
+                                          (31, 33), (1000, 1), (511, 1)]),
+    "g16_d128": (workloads.LayerShape(2048, 16, 1, 128, 512), [(100, 77), (600, 1), (17, 1)]),
+    "g5_d128": (workloads.LayerShape(1280, 10, 2, 128, 512), [(40, 300), (2047, 1), (2048, 1)]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ATTN_CASES))
+def test_attention_paths_vs_oracle(case):
+    shape, seqs = ATTN_CASES[case]
+    spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 77)
+    say(f"attention {case}: seqs={spec.seqs[:6]}")
+    table, pool, full, kp, vp, q = _attention_inputs(spec, 5)
+    cfg = B.layer_cfg(spec.shape)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
+    ws = B.alloc_workspace(cfg, b, DEV)
+    out = torch.full_like(q, float("nan"))
+    B.attention(cfg, b, q, kp, vp, out, ws)
+    torch.cuda.synchronize()
+    ref = _oracle_attention(spec, full, q)
+    got = f64(out)
+    pre = np.concatenate([np.arange(spec.q_start[i], spec.q_start[i + 1])
+                          for i, (c, n) in enumerate(spec.seqs) if n > 1] or [np.zeros(0, int)])
+    dec = np.array([spec.q_start[i] for i, (c, n) in enumerate(spec.seqs) if n == 1], dtype=int)
+    if pre.size:
+        assert_close(got[pre], ref[pre], "prefill attention rows")
+    if dec.size:
+        assert_close(got[dec], ref[dec], "decode attention rows")
+    # each path alone writes only its own rows
+    out2 = torch.full_like(q, float("nan"))
+    B.decode_attention(cfg, b, q, kp, vp, out2, ws)
+    torch.cuda.synchronize()
+    g2 = f64(out2)
+    if pre.size:
+        assert np.isnan(g2[pre]).all()
+    if dec.size:
+        assert np.array_equal(g2[dec], got[dec])
+
+
+def test_rope_kv_append_vs_oracle():
+    spec = workloads.custom_spec(workloads.SHAPES["tiny"], [(64, 64), (32, 1), (57, 1), (0, 3),
+                                                            (4095, 1), (100000, 1)], 5, pool_slack=1.0)
+    say(f"rope+append seqs={spec.seqs}")
+    s = spec.shape
+    table, pool = workloads.block_table(spec)
+    cfg = B.layer_cfg(s)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
+    kp = torch.full((pool, s.n_kv_heads, 16, s.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vp = torch.full((pool, s.n_kv_heads, s.head_dim, 16), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp0, vp0 = kp.clone(), vp.clone()
+    qkv = _randn((spec.num_tokens, s.qkv_cols), 9)
+    q_rot = torch.empty(spec.num_tokens, s.n_q_heads * s.head_dim, dtype=torch.bfloat16, device=DEV)
+    B.rope_kv_append(cfg, b, qkv, q_rot, kp, vp)
+    torch.cuda.synchronize()
+    Q = f64(qkv)
+    hq, hkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+    expect_slots = set()
+    for si, (c, n) in enumerate(spec.seqs):
+        r0 = int(spec.q_start[si])
+        pos = c + np.arange(n)
+        rows = Q[r0:r0 + n]
+        qr = OL.rope(rows[:, :hq * d].reshape(n, hq, d), pos, s.rope_theta)
+        kr = OL.rope(rows[:, hq * d:(hq + hkv) * d].reshape(n, hkv, d), pos, s.rope_theta)
+        vv = rows[:, (hq + hkv) * d:].reshape(n, hkv, d)
+        assert_close(f64(q_rot[r0:r0 + n]).reshape(n, hq, d), qr, f"q_rot seq {si}")
+        blk, slot = OL.kv_slot_addresses(table[si], pos, 16)
+        gk = f64(kp[torch.from_numpy(blk).to(DEV), :, torch.from_numpy(slot).to(DEV), :])
+        gv = f64(vp[torch.from_numpy(blk).to(DEV), :, :, torch.from_numpy(slot).to(DEV)])
+        assert_close(gk, kr, f"k rows seq {si}")
+        # V is copied, not recomputed: bit-exact with the input bf16
+        assert np.array_equal(gv, vv), f"v rows seq {si}"
+        for bb, ss in zip(blk.tolist(), slot.tolist()):
+            for h in range(hkv):
+                expect_slots.add((bb, h, ss))
+    got_slots = changed_slots(kp0, kp, vp0, vp)
+    assert got_slots == expect_slots
+    # nothing else moved: the untouched bytes are still the sentinel
+    mask_k = torch.ones(pool, hkv, 16, dtype=torch.bool, device=DEV)
+    for (bb, h, ss) in expect_slots:
+        mask_k[bb, h, ss] = False
+    assert bool((bits(kp)[mask_k] == SENTINEL).all())
+    assert bool((bits(vp).permute(0, 1, 3, 2)[mask_k] == SENTINEL).all())
+
+
+# ------------------------------------------------------------------------------- whole step
+
+def _check_full_step(case, label):
+    spec = case.spec
+    s = spec.shape
+    kp0, vp0 = case.kp.clone(), case.vp.clone()
+    case.step()
+    torch.cuda.synchronize()
+    x, w, cached = case.oracle_host()
+    ref = OL.layer_step(s, x, w, spec.seqs, [cached[i] for i in range(spec.num_seqs)], case.table)
+    got = f64(case.out)
+    assert_close(got, ref["out"], f"{label} out")
+    assert_close(f64(case.taps["h2"]), ref["h2"], f"{label} h2")
+    assert_close(f64(case.taps["q_rot"]).reshape(ref["q_rot"].shape), ref["q_rot"], f"{label} q_rot")
+    att = f64(case.taps["attn_out"])
+    pre = np.concatenate([np.arange(spec.q_start[i], spec.q_start[i + 1])
+                          for i, (c, n) in enumerate(spec.seqs) if n > 1] or [np.zeros(0, int)])
+    dec = np.array([spec.q_start[i] for i, (c, n) in enumerate(spec.seqs) if n == 1], dtype=int)
+    if pre.size:
+        assert_close(att[pre], ref["attn_out"][pre], f"{label} attn prefill rows")
+    if dec.size:
+        assert_close(att[dec], ref["attn_out"][dec], f"{label} attn decode rows")
+    # placement: exactly the oracle's (block, head, slot) set changed, with the oracle's values
+    a = ref["kv_addr"]
+    expect = {(int(bb), h, int(ss)) for bb, ss in zip(a[:, 2], a[:, 3]) for h in range(s.n_kv_heads)}
+    assert changed_slots(kp0, case.kp, vp0, case.vp) == expect
+    bt = torch.from_numpy(a[:, 2]).to(DEV)
+    sl = torch.from_numpy(a[:, 3]).to(DEV)
+    assert_close(f64(case.kp[bt, :, sl, :]), ref["k_new"], f"{label} new K rows")
+    assert_close(f64(case.vp[bt, :, :, sl]), ref["v_new"], f"{label} new V rows")
+    return ref
+
+
+def test_step_tiny_workload_full():
+    say("step cfg1 full")
+    case = DeviceCase(workloads.make_spec(1), DEV)
+    _check_full_step(case, "cfg1")
+
+
+def test_step_tiny_with_norm_gains():
+    say("step cfg1 gains")
+    case = DeviceCase(workloads.make_spec(1), DEV, gain_jitter=0.2)
+    _check_full_step(case, "cfg1-gains")
+
+
+def test_step_ragged_small_layer():
+    shape = workloads.LayerShape(512, 8, 2, 128, 1024)
+    spec = workloads.custom_spec(shape, [(0, 200), (37, 129), (0, 1), (1234, 1), (16, 1), (5, 2)], 31)
+    say(f"step ragged {spec.seqs}")
+    _check_full_step(DeviceCase(spec, DEV), "ragged")
+
+
+def test_step_deterministic_and_block_permutation_invariant():
+    say("step determinism / permutation")
+    spec = workloads.make_spec(1)
+    c1 = DeviceCase(spec, DEV)
+    c1.step()
+    out1 = c1.out.clone()
+    k1, v1 = c1.kp.clone(), c1.vp.clone()
+    c1.step()  # appends are idempotent: the second run sees the same cache
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out1), bits(c1.out))
+    assert torch.equal(bits(k1), bits(c1.kp)) and torch.equal(bits(v1), bits(c1.vp))
+    c2 = DeviceCase(spec, DEV, permute_seed=4242)
+    assert not np.array_equal(c2.table, c1.table)
+    c2.step()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out1), bits(c2.out))
+
+
+# ------------------------------------------------------------------------------- full sizes
+
+def _sampled_check(case, label, n_dec_samples=4, pre_rows=(0, 1, 63, 64, 127, 128, 129)):
+    """Full-size step on the GPU; the oracle recomputes sampled rows one request at a time."""
+    spec = case.spec
+    s = spec.shape
+    case.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(spec.seed)
+    dec_ids = [i for i, (c, n) in enumerate(spec.seqs) if n == 1]
+    pre_ids = [i for i, (c, n) in enumerate(spec.seqs) if n > 1]
+    picks = []
+    if dec_ids:
+        longest = max(dec_ids, key=lambda i: spec.seqs[i][0])
+        shortest = min(dec_ids, key=lambda i: spec.seqs[i][0])
+        extra = list(rng.choice(dec_ids, size=min(n_dec_samples, len(dec_ids)), replace=False))
+        picks = sorted(set([longest, shortest] + [int(e) for e in extra]))
+    x, w, cached = case.oracle_host(picks + pre_ids)
+    out = f64(case.out)
+    att = f64(case.taps["attn_out"])
+    for si in pre_ids:
+        c, n = spec.seqs[si]
+        rows = sorted(set(r for r in pre_rows if r < n) | {n - 1, n // 2})
+        r0 = int(spec.q_start[si])
+        ref = OL.sequence_step(s, x[r0:r0 + n], w, c, *cached[si], rows=rows)
+        g_rows = r0 + np.array(ref["rows"])
+        assert_close(out[g_rows], ref["out"], f"{label} prefill seq {si} out rows {rows}")
+        assert_close(att[g_rows], ref["attn_out"], f"{label} prefill seq {si} attn rows")
+    for si in picks:
+        c, n = spec.seqs[si]
+        r0 = int(spec.q_start[si])
+        ref = OL.sequence_step(s, x[r0:r0 + 1], w, c, *cached[si])
+        assert_close(out[r0:r0 + 1], ref["out"], f"{label} decode seq {si} (ctx {c}) out")
+        assert_close(att[r0:r0 + 1], ref["attn_out"], f"{label} decode seq {si} attn")
+
+
+@pytest.mark.parametrize("cfgid,variant", [(2, "mixed"), (3, "mixed"), (4, "mixed"),
+                                           (4, "prefill_only"), (4, "decode_only"), (5, "mixed")])
+def test_step_full_size_sampled(cfgid, variant):
+    spec = workloads.make_spec(cfgid, variant)
+    say(f"step full size {spec.name}: T={spec.num_tokens} seqs={spec.num_seqs}")
+    case = DeviceCase(spec, DEV)
+    _sampled_check(case, spec.name)
+    del case
+    torch.cuda.empty_cache()
