@@ -1,0 +1,269 @@
+"""Benchmark of the hybrid layer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload cfg2] [--no-cpu-baseline]
+
+A step is one hybrid_layer_step over one synthetic hybrid batch, inputs resident in HBM. The
+default workload is the Qwen3-8B-shaped layer (hidden 4096, 32/8 heads, head_dim 128, d_ff 12288)
+with one 1024-token prompt chunk at prefix 0 plus 16 decodes at context 8192 (seeded synthetic
+values; paged 16-token KV with a random block table). Prints ONE JSON line.
+
+Besides the whole-step throughput it times every phase through its own entry point with HIP
+events on the launch stream, and reports the dominant kernel (the gate/up GEMM with the SwiGLU
+epilogue) against the bf16 matrix-core peak, the decode attention against HBM peak, and the fp64
+oracle timed on the host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+
+
+def algorithmic_counts(spec):
+    """Work the method must do (no padding, causal-visible pairs only, KV read once per KV head)."""
+    s = spec.shape
+    T = spec.num_tokens
+    d, hq, hkv = s.head_dim, s.n_q_heads, s.n_kv_heads
+    gemm = {
+        "qkv": 2.0 * T * s.hidden * s.qkv_cols,
+        "o": 2.0 * T * hq * d * s.hidden,
+        "gate_up": 2.0 * T * s.hidden * 2 * s.d_ff,
+        "down": 2.0 * T * s.d_ff * s.hidden,
+    }
+    pairs = 0
+    dec_bytes = 0
+    for c, n in spec.seqs:
+        if n > 1:
+            pairs += n * c + n * (n + 1) // 2
+        else:
+            dec_bytes += (c + 1) * hkv * d * 2 * 2
+    return {
+        "gemm_flops": gemm,
+        "weight_bytes": 2.0 * s.weight_params,
+        "prefill_attn_flops": 4.0 * d * hq * pairs,
+        "decode_kv_bytes": float(dec_bytes),
+    }
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_prefill_decode_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(profile_txt, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", profile_txt)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0].strip() in ("source_hash", "hbm_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2", help="cfg1..cfg5, cfg4_prefill_only, cfg4_decode_only")
+    ap.add_argument("--phase-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the hybrid layer step; multi-GPU runs "
+              "(sequence-parallel prefill exchange) are not part of this build. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from hybrid_prefill_decode_amd import binding as B
+    from hybrid_prefill_decode_amd import kvcache
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = "cuda"
+    name = args.workload
+    if name.startswith("cfg4_"):
+        spec = workloads.make_spec(4, name[len("cfg4_"):])
+    else:
+        spec = workloads.make_spec(int(name[3:]))
+    s = spec.shape
+    T = spec.num_tokens
+    table, pool = workloads.block_table(spec)
+    cfg = B.layer_cfg(s)
+    batch = B.Batch(spec.q_start, spec.num_cached, table, dev)
+    x = workloads.hidden_states(spec, dev)
+    w = workloads.weights(spec, dev)
+    kp, vp = kvcache.alloc_pools(pool, s.n_kv_heads, s.head_dim, dev, fill=0.0)
+    for si, (c, _) in enumerate(spec.seqs):
+        if c:
+            k, v = workloads.cached_kv(spec, si, dev)
+            kvcache.write_positions(kp, vp, table[si], range(c), k, v)
+    out = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
+    ws = B.alloc_workspace(cfg, batch, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.hybrid_layer_step(cfg, batch, x, w, kp, vp, out, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-phase timing through the phase entry points (same kernels as the step)
+    qd = s.n_q_heads * s.head_dim
+    h1 = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
+    rs = torch.empty(T, dtype=torch.float32, device=dev)
+    q_rot = torch.empty(T, qd, dtype=torch.bfloat16, device=dev)
+    attn = torch.empty(T, qd, dtype=torch.bfloat16, device=dev)
+    h2 = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
+    mlp = torch.empty(T, s.d_ff, dtype=torch.bfloat16, device=dev)
+    has_pre = any(n > 1 for _, n in spec.seqs)
+    has_dec = any(n == 1 for _, n in spec.seqs)
+    phases = [
+        ("qkv_rope_append", lambda: B.qkv_rope_append(cfg, batch, x, w, q_rot, kp, vp, ws, stream)),
+    ]
+    if has_pre:
+        phases.append(("prefill_attention",
+                       lambda: B.prefill_attention(cfg, batch, q_rot, kp, vp, attn, ws, stream)))
+    if has_dec:
+        phases.append(("decode_attention",
+                       lambda: B.decode_attention(cfg, batch, q_rot, kp, vp, attn, ws, stream)))
+    phases += [
+        ("gemm_o", lambda: B.gemm_bf16_nt(attn, w["w_o"], h2, x, B.HL_EPI_RESIDUAL, stream=stream)),
+        ("rms_scale_mlp", lambda: B.rms_scale(h2, w["mlp_norm"], h1, rs, s.rms_eps, stream)),
+        ("gemm_gate_up", lambda: B.gemm_bf16_nt(h1, w["w_gate_up"], mlp, None, B.HL_EPI_SWIGLU,
+                                                stream=stream, row_scale=rs)),
+        ("gemm_down", lambda: B.gemm_bf16_nt(mlp, w["w_down"], out, h2, B.HL_EPI_RESIDUAL, stream=stream)),
+    ]
+    phase_us = {}
+    for pname, fn in phases:
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.phase_reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        phase_us[pname] = 1000.0 * a.elapsed_time(b) / args.phase_reps
+
+    cnt = algorithmic_counts(spec)
+    # the QKV projection phase also holds its prep pass and the RoPE / append epilogue
+    gemm_us = sum(phase_us[k] for k in ("qkv_rope_append", "gemm_o", "gemm_gate_up", "gemm_down"))
+    gemm_tflops = sum(cnt["gemm_flops"].values()) / (gemm_us * 1e-6) / 1e12
+    dec_gbps = (cnt["decode_kv_bytes"] / (phase_us["decode_attention"] * 1e-6) / 1e9
+                if has_dec else None)
+    pre_tflops = (cnt["prefill_attn_flops"] / (phase_us["prefill_attention"] * 1e-6) / 1e12
+                  if has_pre else None)
+
+    gu_flops = cnt["gemm_flops"]["gate_up"]
+    gu_tflops = gu_flops / (phase_us["gemm_gate_up"] * 1e-6) / 1e12
+    src_hash = kernel_source_hash(["gemm.hip", "common.h"])
+    traffic = read_traffic(f"gemm_gate_up_{name}_pmc.txt", src_hash)
+
+    result = {
+        "metric": "hybrid layer-step tokens/s; GEMM MFMA util % + decode-attn HBM GB/s vs peak",
+        "value": round(T / (ms_step / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and cached K/V, N(0,0.02^2) weights; random block table)",
+        "config": {"workload": workloads.describe(spec), "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "kernel": "gemm_bf16_nt<SwiGLU> (gate/up projection)",
+            "bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "algorithmic_flops_per_launch": gu_flops,
+            "avg_launch_us": round(phase_us["gemm_gate_up"], 2),
+        },
+        "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
+        "gemm_mfma_util": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "gemm_tflops": round(gemm_tflops, 1),
+        "decode_attn_hbm_gbps": None if dec_gbps is None else round(dec_gbps, 1),
+        "decode_attn_hbm_frac": None if dec_gbps is None else round(dec_gbps / PEAK_HBM_GBPS, 4),
+        "prefill_attn_tflops": None if pre_tflops is None else round(pre_tflops, 1),
+        "wall_s_timed": round(t_wall, 3),
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, x, w, table, dev, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(spec, x, w, table, dev, budget_s):
+    """The fp64 oracle on the host cores over the same batch (inputs already in host fp64)."""
+    import numpy as np
+    import torch
+
+    import oracle.layer as OL
+    import workloads
+
+    f = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    xh = f(x)
+    wh = {k: f(v) for k, v in w.items()}
+    cached = []
+    for si in range(spec.num_seqs):
+        k, v = workloads.cached_kv(spec, si, dev)
+        cached.append((f(k), f(v)))
+    cores = torch.get_num_threads()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            cores = max(blas)
+    except Exception:
+        pass
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OL.layer_step(spec.shape, xh, wh, spec.seqs, cached, table)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 5:
+            break
+    return {"value": round(reps * spec.num_tokens / el, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"whole {spec.name} batch ({spec.num_tokens} tokens), {reps} oracle step(s) "
+                      f"in {el:.1f} s, fp64 numpy, inputs already in host memory"}
+
+
+if __name__ == "__main__":
+    main()

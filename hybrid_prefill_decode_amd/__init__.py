@@ -6,6 +6,7 @@ csrc/); `binding` exposes the same entry points to Python with torch tensors as 
 from . import binding  # noqa: F401
 from .binding import (  # noqa: F401
     Batch, HLError, LayerCfg, alloc_workspace, attention, decode_attention, gemm_bf16_nt,
-    hybrid_layer_step, layer_cfg, prefill_attention, rmsnorm, rope_kv_append, strerror,
+    hybrid_layer_step, layer_cfg, prefill_attention, qkv_rope_append, rms_scale, rmsnorm,
+    rope_kv_append, strerror,
     workspace_bytes,
 )

@@ -75,8 +75,13 @@ _SIGS = {
     "hl_rmsnorm": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                     ctypes.c_int32, ctypes.c_float, ctypes.c_void_p], ctypes.c_int),
     "hl_gemm_bf16_nt": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
+                        ctypes.c_int),
+    "hl_rms_scale": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p], ctypes.c_int),
+    "hl_qkv_rope_append": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(Weights), ctypes.c_void_p,
+                            ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_gemm_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "hl_rope_kv_append": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
@@ -199,8 +204,7 @@ def alloc_workspace(cfg: LayerCfg, b: Batch, device="cuda"):
 def hybrid_layer_step(cfg: LayerCfg, b: Batch, x, w: Dict[str, object], k_pool, v_pool, out,
                       workspace, stream=None, taps=None) -> None:
     d = _desc(cfg, b, x, workspace, stream, taps)
-    wt = Weights(*(_ptr(w[k]) for k in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up",
-                                          "w_down")))
+    wt = _weights(w)
     kv = _pages(k_pool, v_pool)
     bt = _table(b)
     _check(lib().hybrid_layer_step(ctypes.byref(d), ctypes.byref(wt), ctypes.byref(kv),
@@ -214,12 +218,34 @@ def rmsnorm(x, gain, y, eps: float, stream=None) -> None:
 
 
 def gemm_bf16_nt(a, w, c, residual=None, epilogue: int = HL_EPI_NONE, workspace=None,
-                 stream=None) -> None:
+                 stream=None, row_scale=None) -> None:
     m, k = a.shape
     n = w.shape[0]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().hl_gemm_bf16_nt(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), m, n, k, epilogue,
-                                 _ptr(workspace), wsb, _stream_ptr(stream)), "hl_gemm_bf16_nt")
+    _check(lib().hl_gemm_bf16_nt(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), _ptr(row_scale), m,
+                                 n, k, epilogue, _ptr(workspace), wsb, _stream_ptr(stream)),
+           "hl_gemm_bf16_nt")
+
+
+def rms_scale(x, gain, xg, row_scale, eps: float, stream=None) -> None:
+    rows, cols = x.shape
+    _check(lib().hl_rms_scale(_ptr(x), _ptr(gain), _ptr(xg), _ptr(row_scale), rows, cols, eps,
+                              _stream_ptr(stream)), "hl_rms_scale")
+
+
+def _weights(w) -> Weights:
+    return Weights(*(_ptr(w.get(k)) for k in ("attn_norm", "w_qkv", "w_o", "mlp_norm",
+                                                "w_gate_up", "w_down")))
+
+
+def qkv_rope_append(cfg: LayerCfg, b: Batch, x, w, q_rot, k_pool, v_pool, workspace,
+                    stream=None) -> None:
+    d = _desc(cfg, b, x, workspace, stream)
+    wt = _weights(w)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hl_qkv_rope_append(ctypes.byref(d), ctypes.byref(wt), _ptr(q_rot),
+                                    ctypes.byref(kv), ctypes.byref(bt)), "hl_qkv_rope_append")
 
 
 def rope_kv_append(cfg: LayerCfg, b: Batch, qkv, q_rot, k_pool, v_pool, stream=None) -> None:

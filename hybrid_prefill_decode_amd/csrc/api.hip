@@ -3,8 +3,11 @@
 // allocates device memory; every launch goes onto the caller's stream.
 //
 // Step order (one pre-norm decoder layer over the hybrid token matrix):
-//   plan -> RMSNorm -> QKV GEMM -> RoPE + KV append -> prefill attention | decode attention + merge
-//   -> O GEMM (+x) -> RMSNorm -> gate/up GEMM (SwiGLU) -> down GEMM (+h2)
+//   plan -> prep(x) -> QKV GEMM with RoPE + KV-append epilogue
+//   -> prefill attention | decode attention + merge -> O GEMM (+x)
+//   -> prep(h2) -> gate/up GEMM (SwiGLU) -> down GEMM (+h2)
+// prep writes bf16(x * gain) and the RMSNorm row factor, which the next GEMM applies to its fp32
+// accumulators (see prep.hip).
 // The linear phases see all tokens at once while attention splits by request kind, the
 // operator-level split of the "ConfluxServe" summary ("The big picture: what happens inside one
 // Transformer layer"), here as one GPU's share.
@@ -24,8 +27,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 struct HostPlan {
   int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
   // workspace byte offsets
-  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_h1 = 0, o_qkv = 0, o_qrot = 0,
-         o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0, total = 0;
+  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
+         o_blk = 0, o_cs = 0, o_qlo = 0, o_qrot = 0, o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0, total = 0;
 };
 
 int check_cfg(const hl_layer_cfg* c) {
@@ -121,8 +124,12 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
   p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);
   p->o_h1 = take(2 * T * c.hidden);
-  p->o_qkv = take(2 * T * (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim);
+  p->o_rs = take(4 * T);
+  p->o_pos = take(4 * T);
+  p->o_blk = take(4 * T);
+  p->o_cs = take(8 * T * (size_t)(c.head_dim / 2));
   p->o_qrot = take(2 * T * qd);
+  p->o_qlo = take(2 * T * qd);
   p->o_attn = take(2 * T * qd);
   p->o_h2 = take(2 * T * c.hidden);
   p->o_mlp = take(2 * T * c.d_ff);
@@ -166,14 +173,21 @@ int prepare(const hl_batch_desc* b, const hl_kv_pages* kv, const hl_block_table*
 int hip_rc(hipError_t e) { return e == hipSuccess ? HL_OK : HL_ERR_HIP; }
 
 struct Buffers {
-  hl_bf16 *h1, *qkv, *qrot, *attn, *h2, *mlp;
+  hl_bf16 *h1, *qrot, *qlo, *attn, *h2, *mlp;
+  float* rs;
+  int32_t *pos, *blk;
+  float2* cs;
 };
 
 Buffers buffers(const hl_batch_desc* b, const HostPlan& hp) {
   uint8_t* base = static_cast<uint8_t*>(b->workspace);
   Buffers B;
   B.h1 = reinterpret_cast<hl_bf16*>(base + hp.o_h1);
-  B.qkv = reinterpret_cast<hl_bf16*>(base + hp.o_qkv);
+  B.rs = reinterpret_cast<float*>(base + hp.o_rs);
+  B.qlo = reinterpret_cast<hl_bf16*>(base + hp.o_qlo);
+  B.pos = reinterpret_cast<int32_t*>(base + hp.o_pos);
+  B.blk = reinterpret_cast<int32_t*>(base + hp.o_blk);
+  B.cs = reinterpret_cast<float2*>(base + hp.o_cs);
   B.qrot = b->tap_q_rot ? b->tap_q_rot : reinterpret_cast<hl_bf16*>(base + hp.o_qrot);
   B.attn = b->tap_attn_out ? b->tap_attn_out : reinterpret_cast<hl_bf16*>(base + hp.o_attn);
   B.h2 = b->tap_h2 ? b->tap_h2 : reinterpret_cast<hl_bf16*>(base + hp.o_h2);
@@ -181,9 +195,43 @@ Buffers buffers(const hl_batch_desc* b, const HostPlan& hp) {
   return B;
 }
 
-int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_kv_pages* kv,
-                  const hl_block_table* bt, hl_bf16* attn_out, const HostPlan& hp,
-                  bool do_prefill, bool do_decode) {
+hl::GemmEpi plain_epi(int kind, const hl_bf16* residual, const float* row_scale) {
+  hl::GemmEpi e{};
+  e.kind = kind;
+  e.residual = residual;
+  e.row_scale = row_scale;
+  return e;
+}
+
+// prep(x) + QKV GEMM with the RoPE / KV-append epilogue.
+int run_qkv(const hl_batch_desc* b, const hl_weights* w, hl_bf16* q_rot, const hl_kv_pages* kv,
+            const hl_block_table* bt, const Buffers& B) {
+  const hl_layer_cfg& c = *b->cfg;
+  hipStream_t st = static_cast<hipStream_t>(b->stream);
+  hl::TokenInfo ti{b->q_start, b->num_cached, b->num_seqs, bt->table, bt->max_blocks_per_seq,
+                   kv->num_blocks, c.head_dim, c.rope_theta, B.pos, B.blk, B.cs};
+  int rc = hip_rc(hl::launch_prep(b->x, w->attn_norm, B.h1, B.rs, b->num_tokens, c.hidden,
+                                  c.rms_eps, &ti, st));
+  if (rc) return rc;
+  hl::GemmEpi e = plain_epi(hl::kEpiRopeAppend, nullptr, B.rs);
+  e.n_q_heads = c.n_q_heads;
+  e.n_kv_heads = c.n_kv_heads;
+  e.head_dim = c.head_dim;
+  e.q_rot = q_rot;
+  e.q_lo = B.qlo;
+  e.kpool = kv->k;
+  e.vpool = kv->v;
+  e.tok_pos = B.pos;
+  e.tok_blk = B.blk;
+  e.rope_cs = B.cs;
+  const int qkv_cols = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  return hip_rc(hl::launch_gemm(B.h1, w->w_qkv, nullptr, b->num_tokens, qkv_cols, c.hidden, e,
+                                nullptr, 0, st));
+}
+
+int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                  const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                  const HostPlan& hp, bool do_prefill, bool do_decode) {
   hipStream_t st = static_cast<hipStream_t>(b->stream);
   const hl::Plan dp = device_plan(hp, b->workspace);
   int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, hp.split_pages,
@@ -196,7 +244,7 @@ int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_kv_page
     if (rc) return rc;
   }
   if (do_decode) {
-    rc = hip_rc(hl::launch_decode_attention(*b->cfg, b->q_start, b->num_cached, q_rot, kv->k,
+    rc = hip_rc(hl::launch_decode_attention(*b->cfg, b->q_start, b->num_cached, q_rot, q_lo, kv->k,
                                             kv->v, kv->num_blocks, bt->table,
                                             bt->max_blocks_per_seq, dp, attn_out, st));
   }
@@ -252,9 +300,18 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
   return HL_OK;
 }
 
+int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_scale,
+                 int32_t rows, int32_t cols, float eps, void* stream) {
+  if (!x || !gain || !xg || !row_scale) return HL_ERR_NULL;
+  if (rows < 0 || cols <= 0 || cols % 8 || !(eps >= 0.f)) return HL_ERR_ARG;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(xg)) return HL_ERR_ALIGN;
+  return hip_rc(hl::launch_prep(x, gain, xg, row_scale, rows, cols, eps, nullptr,
+                                static_cast<hipStream_t>(stream)));
+}
+
 int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
-                    int32_t m, int32_t n, int32_t k, int32_t epilogue, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!a || !w || !c) return HL_ERR_NULL;
   if (epilogue != HL_EPI_NONE && epilogue != HL_EPI_RESIDUAL && epilogue != HL_EPI_SWIGLU)
     return HL_ERR_ARG;
@@ -262,8 +319,8 @@ int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf1
   if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c) || (residual && !aligned16(residual)))
     return HL_ERR_ALIGN;
-  return hip_rc(hl::launch_gemm(a, w, c, residual, m, n, k, epilogue, workspace, workspace_bytes,
-                                static_cast<hipStream_t>(stream)));
+  return hip_rc(hl::launch_gemm(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),
+                                workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,
@@ -283,6 +340,19 @@ int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q
                                        static_cast<hipStream_t>(batch->stream)));
 }
 
+int hl_qkv_rope_append(const hl_batch_desc* batch, const hl_weights* w, hl_bf16* q_rot,
+                       hl_kv_pages* kv, const hl_block_table* bt) {
+  HostPlan hp;
+  int rc = prepare(batch, kv, bt, &hp);
+  if (rc) return rc;
+  if (batch->num_seqs == 0) return HL_OK;
+  if (!w || !w->attn_norm || !w->w_qkv || !q_rot || !batch->x) return HL_ERR_NULL;
+  if (!aligned16(w->attn_norm) || !aligned16(w->w_qkv) || !aligned16(q_rot) ||
+      !aligned16(batch->x))
+    return HL_ERR_ALIGN;
+  return run_qkv(batch, w, q_rot, kv, bt, buffers(batch, hp));
+}
+
 static int attention_entry(const hl_batch_desc* batch, const hl_bf16* q_rot,
                            const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
                            bool pre, bool dec) {
@@ -292,7 +362,7 @@ static int attention_entry(const hl_batch_desc* batch, const hl_bf16* q_rot,
   if (batch->num_seqs == 0) return HL_OK;
   if (!q_rot || !attn_out) return HL_ERR_NULL;
   if (!aligned16(q_rot) || !aligned16(attn_out)) return HL_ERR_ALIGN;
-  return run_attention(batch, q_rot, kv, bt, attn_out, hp, pre, dec);
+  return run_attention(batch, q_rot, nullptr, kv, bt, attn_out, hp, pre, dec);
 }
 
 int hl_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
@@ -326,31 +396,23 @@ int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pag
 
   const hl_layer_cfg& c = *batch->cfg;
   const int T = batch->num_tokens;
-  const int qkv_cols = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_q_heads * c.head_dim;
   hipStream_t st = static_cast<hipStream_t>(batch->stream);
   const Buffers B = buffers(batch, hp);
 
-  if ((rc = hip_rc(hl::launch_rmsnorm(batch->x, w->attn_norm, B.h1, T, c.hidden, c.rms_eps, st))))
+  if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B))) return rc;
+  if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true))) return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
+                                   plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), nullptr, 0, st))))
     return rc;
-  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_qkv, B.qkv, nullptr, T, qkv_cols, c.hidden,
-                                   HL_EPI_NONE, nullptr, 0, st))))
+  if ((rc = hip_rc(hl::launch_prep(B.h2, w->mlp_norm, B.h1, B.rs, T, c.hidden, c.rms_eps,
+                                   nullptr, st))))
     return rc;
-  if ((rc = hip_rc(hl::launch_rope_append(c, batch->num_seqs, T, batch->q_start,
-                                          batch->num_cached, B.qkv, B.qrot, kv->k, kv->v,
-                                          kv->num_blocks, bt->table, bt->max_blocks_per_seq, st))))
+  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, T, 2 * c.d_ff, c.hidden,
+                                   plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), nullptr, 0, st))))
     return rc;
-  if ((rc = run_attention(batch, B.qrot, kv, bt, B.attn, hp, true, true))) return rc;
-  if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, batch->x, T, c.hidden, qd,
-                                   HL_EPI_RESIDUAL, nullptr, 0, st))))
-    return rc;
-  if ((rc = hip_rc(hl::launch_rmsnorm(B.h2, w->mlp_norm, B.h1, T, c.hidden, c.rms_eps, st))))
-    return rc;
-  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, nullptr, T, 2 * c.d_ff, c.hidden,
-                                   HL_EPI_SWIGLU, nullptr, 0, st))))
-    return rc;
-  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, B.h2, T, c.hidden, c.d_ff,
-                                HL_EPI_RESIDUAL, nullptr, 0, st));
+  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
+                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), nullptr, 0, st));
 }
 
 }  // extern "C"

@@ -14,6 +14,9 @@
 //   * the tiny products run on v_mfma_f32_16x16x32_bf16 with the page's 16 tokens as the M side:
 //     S^T = K Q^T (columns = query heads) and O^T = V^T P^T, whose k-slot order is the register
 //     order of S^T, so P never leaves registers; V pages are dim-major, so V^T is a plain load;
+//   * q may come as two bf16 halves (q_rot + q_lo); the scores then take both products, which
+//     costs nothing here (the matrix cores idle on this bandwidth-bound phase) and removes the
+//     rounding of q from the result;
 //   * softmax state (m, l, o) is fp32 in the exp2 domain; the waves' states are merged in LDS and
 //     one partial per unit goes to the workspace; a second kernel merges the partials of a
 //     sequence: m* = max m_j, l* = sum l_j 2^(m_j - m*), o = sum o_j 2^(m_j - m*) / l*.
@@ -28,10 +31,10 @@ constexpr int kWaves = kThreads / 64;
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ num_cached,
-    const hl_bf16* __restrict__ q_rot, const hl_bf16* __restrict__ kpool,
-    const hl_bf16* __restrict__ vpool, long long num_blocks, const int32_t* __restrict__ table,
-    int max_blocks, const int32_t* __restrict__ units, int split_pages, int Hq, int Hkv,
-    float scale_log2, float* __restrict__ part) {
+    const hl_bf16* __restrict__ q_rot, const hl_bf16* __restrict__ q_lo,
+    const hl_bf16* __restrict__ kpool, const hl_bf16* __restrict__ vpool, long long num_blocks,
+    const int32_t* __restrict__ table, int max_blocks, const int32_t* __restrict__ units,
+    int split_pages, int Hq, int Hkv, float scale_log2, float* __restrict__ part) {
   __shared__ float sh_o[kWaves][D][16];
   __shared__ float sh_m[kWaves][16];
   __shared__ float sh_l[kWaves][16];
@@ -49,13 +52,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
   const size_t page_elems = (size_t)HL_BLOCK_SIZE * D;
 
   // Q^T operand: lane (lg, col) holds head col, d = 32 ks + 8 lg .. +7
-  u32x4 qf[D / 32];
+  u32x4 qf[D / 32], ql[D / 32];
+  const bool two_part = q_lo != nullptr;
   {
     const bool ok = col < g;
-    const hl_bf16* qp = q_rot + ((size_t)row * Hq + kvh * g + (ok ? col : 0)) * D + 8 * lg;
+    const size_t off = ((size_t)row * Hq + kvh * g + (ok ? col : 0)) * D + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = ok ? *reinterpret_cast<const u32x4*>(qp + 32 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qf[ks] = ok ? *reinterpret_cast<const u32x4*>(q_rot + off + 32 * ks) : u32x4{0, 0, 0, 0};
+      ql[ks] = (ok && two_part) ? *reinterpret_cast<const u32x4*>(q_lo + off + 32 * ks)
+                                : u32x4{0, 0, 0, 0};
+    }
   }
 
   f32x4 o[D / 16];
@@ -95,6 +102,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     for (int ks = 0; ks < D / 32; ++ks) {
       sa = mfma16x16x32(ka[ks], qf[ks], sa);
       sb = mfma16x16x32(kb[ks], qf[ks], sb);
+    }
+    if (two_part) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        sa = mfma16x16x32(ka[ks], ql[ks], sa);
+        sb = mfma16x16x32(kb[ks], ql[ks], sb);
+      }
     }
     // lane (lg, col) holds tokens 4 lg + i of both pages for head col
     const int tok_a = pa * HL_BLOCK_SIZE + 4 * lg;
@@ -209,6 +223,7 @@ namespace hl {
 
 hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
                                    const int32_t* num_cached, const hl_bf16* q_rot,
+                                   const hl_bf16* q_lo,
                                    const hl_bf16* kpool, const hl_bf16* vpool,
                                    int64_t num_blocks, const int32_t* table, int32_t max_blocks,
                                    const Plan& plan, hl_bf16* attn_out, hipStream_t st) {
@@ -219,14 +234,14 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   const dim3 mgrid(plan.n_dec_seqs, cfg.n_kv_heads);
   if (cfg.head_dim == 128) {
     hipLaunchKernelGGL(decode_attn_kernel<128>, grid, block, 0, st, q_start, num_cached, q_rot,
-                       kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
+                       q_lo, kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
                        plan.split_pages, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
                        plan.dec_part);
     hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, block, 0, st, q_start, plan.dec_seqs,
                        plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads, attn_out);
   } else {
     hipLaunchKernelGGL(decode_attn_kernel<64>, grid, block, 0, st, q_start, num_cached, q_rot,
-                       kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
+                       q_lo, kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
                        plan.split_pages, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
                        plan.dec_part);
     hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, block, 0, st, q_start, plan.dec_seqs,

@@ -52,13 +52,47 @@ struct Plan {
   int32_t max_pre_kv;      // longest key range of any prefill tile (host-side estimate)
 };
 
+// Per-token data of one step (filled by the first prep pass, read by the QKV GEMM epilogue).
+struct TokenInfo {
+  const int32_t* q_start;
+  const int32_t* num_cached;
+  int32_t num_seqs;
+  const int32_t* table;
+  int32_t max_blocks;
+  int64_t num_blocks;
+  int32_t head_dim;
+  float rope_theta;
+  int32_t* tok_pos;   // [T] absolute position
+  int32_t* tok_blk;   // [T] physical block of that position (-1 if out of range)
+  float2* rope_cs;    // [T][head_dim / 2] (cos, sin)
+};
+
+// Epilogue of the token-batched GEMM.
+constexpr int kEpiRopeAppend = 3;  // internal: rotate q/k, write q_rot and the K/V pages
+struct GemmEpi {
+  int32_t kind;               // HL_EPI_NONE / RESIDUAL / SWIGLU / kEpiRopeAppend
+  const hl_bf16* residual;    // RESIDUAL: [m, n]
+  const float* row_scale;     // optional [m]: acc *= row_scale[row] before the epilogue math
+  // kEpiRopeAppend
+  int32_t n_q_heads, n_kv_heads, head_dim;
+  hl_bf16* q_rot;
+  hl_bf16* q_lo;              // optional: bf16(q - bf16(q)), the rounding residue of q_rot
+  hl_bf16* kpool;
+  hl_bf16* vpool;
+  const int32_t* tok_pos;
+  const int32_t* tok_blk;
+  const float2* rope_cs;
+};
+
+hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* rscale,
+                       int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
+                       hipStream_t st);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
                        int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
 hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
                           int32_t cols, float eps, hipStream_t st);
-hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* res,
-                       int32_t m, int32_t n, int32_t k, int32_t epi, void* ws, size_t ws_bytes,
-                       hipStream_t st);
+hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,
+                       int32_t k, const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epi);
 hipError_t launch_rope_append(const hl_layer_cfg& cfg, int32_t num_seqs, int32_t num_tokens,
                               const int32_t* q_start, const int32_t* num_cached,
@@ -72,6 +106,7 @@ hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_st
                                     const Plan& plan, hl_bf16* attn_out, hipStream_t st);
 hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
                                    const int32_t* num_cached, const hl_bf16* q_rot,
+                                   const hl_bf16* q_lo,
                                    const hl_bf16* kpool, const hl_bf16* vpool,
                                    int64_t num_blocks, const int32_t* table, int32_t max_blocks,
                                    const Plan& plan, hl_bf16* attn_out, hipStream_t st);

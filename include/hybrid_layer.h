@@ -168,21 +168,35 @@ int hl_version(void);
 int hl_rmsnorm(const hl_bf16* x, const hl_bf16* gain, hl_bf16* y, int32_t rows, int32_t cols,
                float eps, void* stream);
 
-/* Token-batched linear layer C = A W^T with A [m, k] and W [n, k] (both k-contiguous), bf16 in,
- * fp32 accumulation, bf16 out. epilogue:
- *   HL_EPI_NONE     c [m, n] = A W^T
- *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + A W^T
+/* RMSNorm split into its two factors, for a following linear layer: xg[r, :] = x[r, :] * gain
+ * (bf16) and row_scale[r] = 1 / sqrt(mean(x[r, :]^2) + eps) (fp32 [rows]), so that
+ * RMSNorm(x) W^T = row_scale * (xg W^T) with no rounding of the normalised row. cols % 8 == 0. */
+int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_scale,
+                 int32_t rows, int32_t cols, float eps, void* stream);
+
+/* Token-batched linear layer C = s * (A W^T) with A [m, k] and W [n, k] (both k-contiguous), bf16
+ * in, fp32 accumulation, bf16 out; s = row_scale[row] (fp32 [m]) or 1 when row_scale is NULL.
+ * epilogue:
+ *   HL_EPI_NONE     c [m, n] = s * A W^T
+ *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + s * A W^T
  *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
- *                   c [m, f] = silu(A W_gate^T) * (A W_up^T)
- * Requirements: k % 64 == 0, n % 64 == 0 (n % 128 == 0 for SWIGLU), m >= 1. `workspace` may be
- * NULL; when given (hl_gemm_workspace_bytes) small-m shapes may use a split-k schedule. */
+ *                   c [m, f] = silu(s * A W_gate^T) * (s * A W_up^T)
+ * Requirements: k % 64 == 0, n % 128 == 0, m >= 0. `workspace` may be NULL (reserved for
+ * split-k schedules; hl_gemm_workspace_bytes gives the size). */
 enum { HL_EPI_NONE = 0, HL_EPI_RESIDUAL = 1, HL_EPI_SWIGLU = 2 };
 int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
-                    int32_t m, int32_t n, int32_t k, int32_t epilogue, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
+                    void* workspace, size_t workspace_bytes, void* stream);
 int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, size_t* bytes);
 
-/* Rotary embedding of q and k and KV append. qkv [num_tokens, (Hq + 2 Hkv) d] (device, the QKV
+/* First half of the layer up to attention, as the step runs it: RMSNorm of batch->x (gain
+ * w->attn_norm), the QKV projection (w->w_qkv) and, in the same kernel's epilogue, the rotary
+ * embedding of q and k and the append of the new K/V rows into their pages. Writes q_rot
+ * [num_tokens, Hq d] (device). Uses the batch workspace. */
+int hl_qkv_rope_append(const hl_batch_desc* batch, const hl_weights* weights, hl_bf16* q_rot,
+                       hl_kv_pages* kv, const hl_block_table* block_table);
+
+/* Rotary embedding of q and k and KV append, on its own. qkv [num_tokens, (Hq + 2 Hkv) d] (device, the QKV
  * projection output); writes q_rot [num_tokens, Hq d] and the new K (rotated) and V rows into
  * their pages: position p of sequence s goes to block table[s][p / 16], slot p % 16. */
 int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,

@@ -31,7 +31,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("hybrid_layer_step", "hl_workspace_bytes", "hl_strerror", "hl_version",
-              "hl_rmsnorm", "hl_gemm_bf16_nt", "hl_rope_kv_append", "hl_attention",
+              "hl_rmsnorm", "hl_rms_scale", "hl_gemm_bf16_nt", "hl_qkv_rope_append",
+              "hl_rope_kv_append", "hl_attention",
               "hl_prefill_attention", "hl_decode_attention"):
         assert n in names, n
 
@@ -165,7 +166,7 @@ def test_workspace_bytes_matches_plan_of_all_workloads():
         n = B.workspace_bytes(B.layer_cfg(spec.shape), b)
         s = spec.shape
         T = spec.num_tokens
-        floor = 2 * T * (2 * s.hidden + s.qkv_cols + 2 * s.n_q_heads * s.head_dim + s.d_ff)
+        floor = 2 * T * (2 * s.hidden + 2 * s.n_q_heads * s.head_dim + s.d_ff)
         assert floor <= n < floor + (1 << 30), (cfgid, n, floor)
 
 
@@ -173,10 +174,13 @@ def test_gemm_and_rmsnorm_argument_checks():
     t = torch.zeros(64 * 128, dtype=torch.bfloat16)
     p = t.data_ptr()
     L = B.lib()
-    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 100, 64, 0, None, 0, None) == B.HL_ERR_ARG  # n % 128
-    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 60, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
-    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 64, 7, None, 0, None) == B.HL_ERR_ARG  # epilogue
-    assert L.hl_gemm_bf16_nt(p, p, p, None, 8, 128, 64, 1, None, 0, None) == B.HL_ERR_NULL  # residual
-    assert L.hl_gemm_bf16_nt(p + 2, p, p, None, 8, 128, 64, 0, None, 0, None) == B.HL_ERR_ALIGN
+    g = L.hl_gemm_bf16_nt
+    assert g(p, p, p, None, None, 8, 100, 64, 0, None, 0, None) == B.HL_ERR_ARG  # n % 128
+    assert g(p, p, p, None, None, 8, 128, 60, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
+    assert g(p, p, p, None, None, 8, 128, 64, 7, None, 0, None) == B.HL_ERR_ARG  # epilogue
+    assert g(p, p, p, None, None, 8, 128, 64, 1, None, 0, None) == B.HL_ERR_NULL  # residual
+    assert g(p + 2, p, p, None, None, 8, 128, 64, 0, None, 0, None) == B.HL_ERR_ALIGN
     assert L.hl_rmsnorm(p, p, p, 4, 12, 1e-6, None) == B.HL_ERR_ARG
     assert L.hl_rmsnorm(None, p, p, 4, 16, 1e-6, None) == B.HL_ERR_NULL
+    assert L.hl_rms_scale(p, p, p, None, 4, 16, 1e-6, None) == B.HL_ERR_NULL
+    assert L.hl_rms_scale(p, p, p, p, 4, 12, 1e-6, None) == B.HL_ERR_ARG

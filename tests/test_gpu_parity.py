@@ -41,16 +41,21 @@ def _randn(shape, seed, std=1.0):
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (68, 512, 256), (130, 384, 320), (257, 256, 128),
                                    (1040, 1024, 512)])
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
-def test_gemm_vs_oracle(m, n, k, epi):
-    say(f"gemm m={m} n={n} k={k} epi={epi}")
+@pytest.mark.parametrize("scaled", [False, True])
+def test_gemm_vs_oracle(m, n, k, epi, scaled):
+    say(f"gemm m={m} n={n} k={k} epi={epi} row_scale={scaled}")
     a = _randn((m, k), 1 + m)
     w = _randn((n, k), 2 + n, 0.05)
     res = _randn((m, n // 2 if epi == B.HL_EPI_SWIGLU else n), 3 + k)
+    rs = (0.5 + torch.rand(m, generator=torch.Generator(device=DEV).manual_seed(m), device=DEV)) \
+        if scaled else None
     out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
     c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
-    B.gemm_bf16_nt(a, w, c, res if epi == B.HL_EPI_RESIDUAL else None, epi)
+    B.gemm_bf16_nt(a, w, c, res if epi == B.HL_EPI_RESIDUAL else None, epi, row_scale=rs)
     torch.cuda.synchronize()
     A, W = f64(a), f64(w)
+    if scaled:
+        A = A * f64(rs)[:, None]  # s * (A W^T) == (s A) W^T
     if epi == B.HL_EPI_SWIGLU:
         ref = OL.swiglu(A, W, n // 2)
     else:
@@ -69,6 +74,67 @@ def test_rmsnorm_vs_oracle(rows, cols):
     B.rmsnorm(x, g, y, 1e-6)
     torch.cuda.synchronize()
     assert_close(f64(y), OL.rmsnorm(f64(x), f64(g), 1e-6), "rmsnorm")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (68, 4096), (3, 20480)])
+def test_rms_scale_vs_oracle(rows, cols):
+    say(f"rms_scale rows={rows} cols={cols}")
+    x = _randn((rows, cols), 20 + cols)
+    g = (1.0 + _randn((cols,), 21, 0.1).float()).to(torch.bfloat16)
+    xg = torch.empty_like(x)
+    r = torch.empty(rows, dtype=torch.float32, device=DEV)
+    B.rms_scale(x, g, xg, r, 1e-6)
+    torch.cuda.synchronize()
+    assert_close(f64(xg) * f64(r)[:, None], OL.rmsnorm(f64(x), f64(g), 1e-6), "r * xg")
+    # with unit gain the scaled row is the input itself, bit for bit
+    one = torch.ones(cols, dtype=torch.bfloat16, device=DEV)
+    B.rms_scale(x, one, xg, r, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(xg), bits(x))
+
+
+QKV_CASES = {
+    "cfg1": (workloads.SHAPES["tiny"], None),
+    "d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 130), (70000, 1), (33, 1), (15, 17)]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(QKV_CASES))
+def test_qkv_rope_append_vs_oracle(case):
+    shape, seqs = QKV_CASES[case]
+    spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 3)
+    say(f"qkv+rope+append {case}: {spec.seqs}")
+    s = spec.shape
+    table, pool = workloads.block_table(spec)
+    cfg = B.layer_cfg(s)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
+    x = workloads.hidden_states(spec, DEV)
+    w = workloads.weights(spec, DEV, gain_jitter=0.1)
+    kp = torch.full((pool, s.n_kv_heads, 16, s.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vp = torch.full((pool, s.n_kv_heads, s.head_dim, 16), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp0, vp0 = kp.clone(), vp.clone()
+    q_rot = torch.empty(spec.num_tokens, s.n_q_heads * s.head_dim, dtype=torch.bfloat16, device=DEV)
+    ws = B.alloc_workspace(cfg, b, DEV)
+    B.qkv_rope_append(cfg, b, x, w, q_rot, kp, vp, ws)
+    torch.cuda.synchronize()
+    hq, hkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+    h1 = OL.rmsnorm(f64(x), f64(w["attn_norm"]), s.rms_eps)
+    qkv = OL.linear(h1, f64(w["w_qkv"]))
+    expect = set()
+    for si, (c, n) in enumerate(spec.seqs):
+        r0 = int(spec.q_start[si])
+        pos = c + np.arange(n)
+        rows = qkv[r0:r0 + n]
+        qr = OL.rope(rows[:, :hq * d].reshape(n, hq, d), pos, s.rope_theta)
+        kr = OL.rope(rows[:, hq * d:(hq + hkv) * d].reshape(n, hkv, d), pos, s.rope_theta)
+        vv = rows[:, (hq + hkv) * d:].reshape(n, hkv, d)
+        assert_close(f64(q_rot[r0:r0 + n]).reshape(n, hq, d), qr, f"q_rot seq {si}")
+        blk, slot = OL.kv_slot_addresses(table[si], pos, 16)
+        tb, ts = torch.from_numpy(blk).to(DEV), torch.from_numpy(slot).to(DEV)
+        assert_close(f64(kp[tb, :, ts, :]), kr, f"K rows seq {si}")
+        assert_close(f64(vp[tb, :, :, ts]), vv, f"V rows seq {si}")
+        expect |= {(int(bb), h, int(ss)) for bb, ss in zip(blk, slot) for h in range(hkv)}
+    assert changed_slots(kp0, kp, vp0, vp) == expect
 
 
 def _attention_inputs(spec, seed):
