@@ -39,7 +39,7 @@ int check_cfg(const hl_layer_cfg* c) {
   if (c->hidden <= 0 || c->hidden % 128) return HL_ERR_SHAPE;
   if (c->d_ff <= 0 || c->d_ff % 64) return HL_ERR_SHAPE;
   if ((c->n_q_heads * c->head_dim) % 64) return HL_ERR_SHAPE;
-  if (((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 128) return HL_ERR_SHAPE;
+  if (((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 256) return HL_ERR_SHAPE;
   if (c->block_size != HL_BLOCK_SIZE) return HL_ERR_SHAPE;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->softmax_scale >= 0.f))
     return HL_ERR_SHAPE;
@@ -82,10 +82,19 @@ int check_pages(const hl_batch_desc* b, const hl_kv_pages* kv, const hl_block_ta
 }
 
 // Pages per decode work unit: the smallest power of two in [32, 256] that keeps the decode grid
-// within 16K workgroups (one partial costs about 1/split of the unit's KV bytes in extra traffic).
+// within 16K workgroups (one partial costs about 1/split of the unit's KV bytes in extra traffic)
+// and no sequence above kMaxUnitsPerSeq units.
 int pick_split(const hl_batch_desc* b) {
   const int hkv = b->cfg->n_kv_heads;
-  for (int sp = 32; sp <= 256; sp *= 2) {
+  int64_t max_pages = 0;
+  for (int s = 0; s < b->num_seqs; ++s)
+    if (b->h_q_start[s + 1] - b->h_q_start[s] == 1)
+      max_pages = std::max<int64_t>(max_pages, ((int64_t)b->h_num_cached[s] + HL_BLOCK_SIZE) / HL_BLOCK_SIZE);
+  // no sequence may need more than kMaxUnitsPerSeq units (its merge weights live in LDS)
+  int floor_sp = 32;
+  while ((max_pages + floor_sp - 1) / floor_sp > hl::kMaxUnitsPerSeq) floor_sp *= 2;
+  if (floor_sp > 256) return floor_sp;
+  for (int sp = floor_sp; sp <= 256; sp *= 2) {
     int64_t units = 0;
     for (int s = 0; s < b->num_seqs; ++s) {
       if (b->h_q_start[s + 1] - b->h_q_start[s] != 1) continue;
@@ -120,7 +129,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
     off += align_up(bytes);
     return o;
   };
-  p->o_dec_units = take(sizeof(int32_t) * 2 * (size_t)p->n_dec_units);
+  p->o_dec_units = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_units);
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
   p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);
   p->o_h1 = take(2 * T * c.hidden);

@@ -17,9 +17,13 @@
 //   * q may come as two bf16 halves (q_rot + q_lo); the scores then take both products, which
 //     costs nothing here (the matrix cores idle on this bandwidth-bound phase) and removes the
 //     rounding of q from the result;
-//   * softmax state (m, l, o) is fp32 in the exp2 domain; the waves' states are merged in LDS and
-//     one partial per unit goes to the workspace; a second kernel merges the partials of a
-//     sequence: m* = max m_j, l* = sum l_j 2^(m_j - m*), o = sum o_j 2^(m_j - m*) / l*.
+//   * softmax state (m, l, o) is fp32 in the exp2 domain; the waves' states are merged in LDS. A
+//     sequence with one unit writes its row directly. Otherwise each unit writes a partial to the
+//     workspace and a second kernel merges them (m* = max m_j, l* = sum l_j 2^(m_j - m*),
+//     o = sum o_j 2^(m_j - m*) / l*), with the per-unit weights computed once in LDS and the
+//     partial loads independent. (Merging in the last-finishing workgroup instead needs an
+//     agent-scope release per workgroup, which writes back the XCD's L2 and costs more than the
+//     extra launch.)
 // Tokens past the sequence end are masked (scores by select, values zeroed on load).
 #include "common.h"
 
@@ -34,12 +38,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     const hl_bf16* __restrict__ q_rot, const hl_bf16* __restrict__ q_lo,
     const hl_bf16* __restrict__ kpool, const hl_bf16* __restrict__ vpool, long long num_blocks,
     const int32_t* __restrict__ table, int max_blocks, const int32_t* __restrict__ units,
-    int split_pages, int Hq, int Hkv, float scale_log2, float* __restrict__ part) {
+    const int32_t* __restrict__ dec_seqs, int split_pages,
+    int Hq, int Hkv, float scale_log2, float* __restrict__ part, hl_bf16* __restrict__ attn_out) {
   __shared__ float sh_o[kWaves][D][16];
   __shared__ float sh_m[kWaves][16];
   __shared__ float sh_l[kWaves][16];
   const int unit = blockIdx.x, kvh = blockIdx.y;
-  const int s = units[2 * unit], pg0 = units[2 * unit + 1];
+  const int s = units[3 * unit], pg0 = units[3 * unit + 1], di = units[3 * unit + 2];
+  const int u0 = dec_seqs[3 * di + 1], nu = dec_seqs[3 * di + 2];
   const int row = q_start[s];
   const int kv_len = num_cached[s] + 1;
   const int npages = (kv_len + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
@@ -171,6 +177,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     for (int i = 0; i < 4; ++i) sh_o[wave][16 * mt + 4 * lg + i][col] = o[mt][i];
   __syncthreads();
 
+  // this unit's combined state for every head of the group
+  if (nu == 1) {
+    for (int e = tid; e < g * D; e += kThreads) {
+      const int hh = e / D, d = e - hh * D;
+      float mx = -1e30f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sh_m[w][hh]);
+      float acc = 0.f, lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = exp2f(sh_m[w][hh] - mx);
+        acc += sh_o[w][d][hh] * sc;
+        lsum += sh_l[w][hh] * sc;
+      }
+      attn_out[((size_t)row * Hq + kvh * g + hh) * D + d] = (hl_bf16)f2bf(acc / lsum);
+    }
+    return;
+  }
   float* dst = part + ((size_t)unit * Hkv + kvh) * g * (D + 2);
   for (int e = tid; e < g * D; e += kThreads) {
     const int hh = e / D, d = e - hh * D;
@@ -192,28 +216,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
   }
 }
 
-// Merge the split partials of each decode sequence and write its attention row.
+// Merge the split partials of each multi-unit decode sequence and write its attention row.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ dec_seqs,
     const float* __restrict__ part, int Hq, int Hkv, hl_bf16* __restrict__ attn_out) {
-  const int i = blockIdx.x, kvh = blockIdx.y;
-  const int s = dec_seqs[3 * i], u0 = dec_seqs[3 * i + 1], nu = dec_seqs[3 * i + 2];
+  __shared__ float sh_w[hl::kMaxUnitsPerSeq * 16];
+  __shared__ float sh_mx[16], sh_lt[16];
+  const int di = blockIdx.x, kvh = blockIdx.y;
+  const int s = dec_seqs[3 * di], u0 = dec_seqs[3 * di + 1], nu = dec_seqs[3 * di + 2];
+  if (nu == 1) return;  // written directly by the decode kernel
   const int g = Hq / Hkv;
   const int row = q_start[s];
-  for (int e = threadIdx.x; e < g * D; e += kThreads) {
-    const int hh = e / D, d = e - hh * D;
+  const int tid = threadIdx.x;
+  const size_t ustride = (size_t)Hkv * g * (D + 2);
+  const float* base = part + ((size_t)u0 * Hkv + kvh) * g * (D + 2);
+  // m of every (unit, head) into LDS, then per-head max, weights and l*
+  for (int e = tid; e < nu * g; e += kThreads) {
+    const int u = e / g, hh = e - u * g;
+    sh_w[u * 16 + hh] = base[u * ustride + hh * (D + 2) + D];
+  }
+  __syncthreads();
+  if (tid < g) {
     float mx = -1e30f;
-    for (int u = 0; u < nu; ++u)
-      mx = fmaxf(mx, part[(((size_t)(u0 + u) * Hkv + kvh) * g + hh) * (D + 2) + D]);
-    float acc = 0.f, lsum = 0.f;
-    for (int u = 0; u < nu; ++u) {
-      const float* p = part + (((size_t)(u0 + u) * Hkv + kvh) * g + hh) * (D + 2);
-      const float sc = exp2f(p[D] - mx);
-      acc += p[d] * sc;
-      lsum += p[D + 1] * sc;
-    }
-    attn_out[((size_t)row * Hq + kvh * g + hh) * D + d] = (hl_bf16)f2bf(acc / lsum);
+    for (int u = 0; u < nu; ++u) mx = fmaxf(mx, sh_w[u * 16 + tid]);
+    sh_mx[tid] = mx;
+  }
+  __syncthreads();
+  for (int e = tid; e < nu * g; e += kThreads) {
+    const int u = e / g, hh = e - u * g;
+    sh_w[u * 16 + hh] = exp2f(sh_w[u * 16 + hh] - sh_mx[hh]);
+  }
+  __syncthreads();
+  if (tid < g) {
+    float lt = 0.f;
+    for (int u = 0; u < nu; ++u) lt += base[u * ustride + tid * (D + 2) + D + 1] * sh_w[u * 16 + tid];
+    sh_lt[tid] = lt;
+  }
+  __syncthreads();
+  for (int e = tid; e < g * D; e += kThreads) {
+    const int hh = e / D, d = e - hh * D;
+    const float* p = base + hh * (D + 2) + d;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int u = 0; u < nu; ++u) acc += p[u * ustride] * sh_w[u * 16 + hh];
+    attn_out[((size_t)row * Hq + kvh * g + hh) * D + d] = (hl_bf16)f2bf(acc / sh_lt[hh]);
   }
 }
 
@@ -231,21 +278,22 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   const float scale = cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(plan.n_dec_units, cfg.n_kv_heads), block(kThreads);
-  const dim3 mgrid(plan.n_dec_seqs, cfg.n_kv_heads);
   if (cfg.head_dim == 128) {
     hipLaunchKernelGGL(decode_attn_kernel<128>, grid, block, 0, st, q_start, num_cached, q_rot,
                        q_lo, kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
-                       plan.split_pages, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       plan.dec_part);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, block, 0, st, q_start, plan.dec_seqs,
-                       plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads, attn_out);
+                       plan.dec_seqs, plan.split_pages, cfg.n_q_heads,
+                       cfg.n_kv_heads, scale_log2, plan.dec_part, attn_out);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(plan.n_dec_seqs, cfg.n_kv_heads), block, 0,
+                       st, q_start, plan.dec_seqs, plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads,
+                       attn_out);
   } else {
     hipLaunchKernelGGL(decode_attn_kernel<64>, grid, block, 0, st, q_start, num_cached, q_rot,
                        q_lo, kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
-                       plan.split_pages, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       plan.dec_part);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, block, 0, st, q_start, plan.dec_seqs,
-                       plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads, attn_out);
+                       plan.dec_seqs, plan.split_pages, cfg.n_q_heads,
+                       cfg.n_kv_heads, scale_log2, plan.dec_part, attn_out);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(plan.n_dec_seqs, cfg.n_kv_heads), block, 0,
+                       st, q_start, plan.dec_seqs, plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads,
+                       attn_out);
   }
   return hipGetLastError();
 }

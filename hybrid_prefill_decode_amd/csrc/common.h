@@ -43,7 +43,7 @@ namespace hl {
 
 struct Plan {
   // device work lists inside the workspace
-  int32_t* dec_units;      // [n_dec_units][2]: (seq, first page)
+  int32_t* dec_units;      // [n_dec_units][3]: (seq, first page, decode index)
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
   int32_t* pre_tiles;      // [n_pre_tiles][2]: (seq, first query row within the sequence)
   float* dec_part;         // [n_dec_units][Hkv][group][head_dim + 2] partial (o, m, l)
@@ -89,6 +89,7 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
                        hipStream_t st);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
                        int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
+constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
 hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
                           int32_t cols, float eps, hipStream_t st);
 hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,

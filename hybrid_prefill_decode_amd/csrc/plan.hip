@@ -4,7 +4,7 @@
 // offset num_cached), the two kinds a chunked-prefill iteration mixes ("Chunked prefill
 // (stall-free batching), explained", "How it works, step by step"). One 1024-thread workgroup
 // classifies the sequences and scans their work counts:
-//   decode unit  = (sequence, first page) covering `split_pages` KV pages of one sequence;
+//   decode unit  = (sequence, first page, decode index) covering `split_pages` KV pages;
 //   decode entry = (sequence, first unit, unit count) for the split merge;
 //   prefill tile = (sequence, first query row) covering `q_tile` query rows, emitted last tile
 //                  first so the tiles with the longest key range are dispatched first.
@@ -59,8 +59,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     const int off_t = base_t + block_exclusive_scan(tiles, buf, &tot_t);
     if (is_dec) {
       for (int u = 0; u < units; ++u) {
-        dec_units[2 * (off_u + u)] = s;
-        dec_units[2 * (off_u + u) + 1] = u * split_pages;
+        dec_units[3 * (off_u + u)] = s;
+        dec_units[3 * (off_u + u) + 1] = u * split_pages;
+        dec_units[3 * (off_u + u) + 2] = off_d;
       }
       dec_seqs[3 * off_d] = s;
       dec_seqs[3 * off_d + 1] = off_u;
