@@ -149,6 +149,9 @@ def main():
     attn = torch.empty(T, qd, dtype=torch.bfloat16, device=dev)
     h2 = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
     mlp = torch.empty(T, s.d_ff, dtype=torch.bfloat16, device=dev)
+    # the step hands the O and down projections its workspace (stream-K schedule); so do these
+    gws = torch.empty(B.gemm_workspace_bytes(T, s.hidden, s.d_ff, B.HL_EPI_RESIDUAL),
+                      dtype=torch.uint8, device=dev)
     has_pre = any(n > 1 for _, n in spec.seqs)
     has_dec = any(n == 1 for _, n in spec.seqs)
     phases = [
@@ -161,11 +164,13 @@ def main():
         phases.append(("decode_attention",
                        lambda: B.decode_attention(cfg, batch, q_rot, kp, vp, attn, ws, stream)))
     phases += [
-        ("gemm_o", lambda: B.gemm_bf16_nt(attn, w["w_o"], h2, x, B.HL_EPI_RESIDUAL, stream=stream)),
+        ("gemm_o", lambda: B.gemm_bf16_nt(attn, w["w_o"], h2, x, B.HL_EPI_RESIDUAL,
+                                          workspace=gws, stream=stream)),
         ("rms_scale_mlp", lambda: B.rms_scale(h2, w["mlp_norm"], h1, rs, s.rms_eps, stream)),
         ("gemm_gate_up", lambda: B.gemm_bf16_nt(h1, w["w_gate_up"], mlp, None, B.HL_EPI_SWIGLU,
                                                 stream=stream, row_scale=rs)),
-        ("gemm_down", lambda: B.gemm_bf16_nt(mlp, w["w_down"], out, h2, B.HL_EPI_RESIDUAL, stream=stream)),
+        ("gemm_down", lambda: B.gemm_bf16_nt(mlp, w["w_down"], out, h2, B.HL_EPI_RESIDUAL,
+                                             workspace=gws, stream=stream)),
     ]
     phase_us = {}
     for pname, fn in phases:

@@ -227,6 +227,13 @@ def gemm_bf16_nt(a, w, c, residual=None, epilogue: int = HL_EPI_NONE, workspace=
            "hl_gemm_bf16_nt")
 
 
+def gemm_workspace_bytes(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE) -> int:
+    v = ctypes.c_size_t(0)
+    _check(lib().hl_gemm_workspace_bytes(m, n, k, epilogue, ctypes.byref(v)),
+           "hl_gemm_workspace_bytes")
+    return int(v.value)
+
+
 def rms_scale(x, gain, xg, row_scale, eps: float, stream=None) -> None:
     rows, cols = x.shape
     _check(lib().hl_rms_scale(_ptr(x), _ptr(gain), _ptr(xg), _ptr(row_scale), rows, cols, eps,

@@ -28,7 +28,9 @@ struct HostPlan {
   int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
   // workspace byte offsets
   size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
-         o_blk = 0, o_cs = 0, o_qlo = 0, o_qrot = 0, o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0, total = 0;
+         o_blk = 0, o_cs = 0, o_qlo = 0, o_qrot = 0, o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0,
+         o_gemm = 0, total = 0;
+  size_t gemm_bytes = 0;
 };
 
 int check_cfg(const hl_layer_cfg* c) {
@@ -143,6 +145,8 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
   p->o_h2 = take(2 * T * c.hidden);
   p->o_mlp = take(2 * T * c.d_ff);
   p->o_part = take(sizeof(float) * (size_t)p->n_dec_units * c.n_kv_heads * g * (c.head_dim + 2));
+  p->gemm_bytes = hl::gemm_workspace_bytes(b->num_tokens, c.hidden, c.d_ff, HL_EPI_RESIDUAL);
+  p->o_gemm = take(p->gemm_bytes);
   p->total = off;
 }
 
@@ -183,6 +187,8 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? HL_OK : HL_ERR_HIP; }
 
 struct Buffers {
   hl_bf16 *h1, *qrot, *qlo, *attn, *h2, *mlp;
+  void* gemm_ws;
+  size_t gemm_bytes;
   float* rs;
   int32_t *pos, *blk;
   float2* cs;
@@ -201,6 +207,8 @@ Buffers buffers(const hl_batch_desc* b, const HostPlan& hp) {
   B.attn = b->tap_attn_out ? b->tap_attn_out : reinterpret_cast<hl_bf16*>(base + hp.o_attn);
   B.h2 = b->tap_h2 ? b->tap_h2 : reinterpret_cast<hl_bf16*>(base + hp.o_h2);
   B.mlp = reinterpret_cast<hl_bf16*>(base + hp.o_mlp);
+  B.gemm_ws = base + hp.o_gemm;
+  B.gemm_bytes = hp.gemm_bytes;
   return B;
 }
 
@@ -412,7 +420,8 @@ int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pag
   if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B))) return rc;
   if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true))) return rc;
   if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
-                                   plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), nullptr, 0, st))))
+                                   plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), B.gemm_ws,
+                                   B.gemm_bytes, st))))
     return rc;
   if ((rc = hip_rc(hl::launch_prep(B.h2, w->mlp_norm, B.h1, B.rs, T, c.hidden, c.rms_eps,
                                    nullptr, st))))
@@ -421,7 +430,8 @@ int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pag
                                    plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), nullptr, 0, st))))
     return rc;
   return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
-                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), nullptr, 0, st));
+                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
+                                B.gemm_bytes, st));
 }
 
 }  // extern "C"

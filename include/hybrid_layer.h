@@ -181,8 +181,10 @@ int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_
  *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + s * A W^T
  *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
  *                   c [m, f] = silu(s * A W_gate^T) * (s * A W_up^T)
- * Requirements: k % 64 == 0, n % 128 == 0, m >= 0. `workspace` may be NULL (reserved for
- * split-k schedules; hl_gemm_workspace_bytes gives the size). */
+ * Requirements: k % 64 == 0, n % 128 == 0, m >= 0. `workspace` (device, may be NULL): when it
+ * holds hl_gemm_workspace_bytes() bytes, shapes with fewer output tiles than compute units run a
+ * stream-K schedule (partial tiles in the workspace, summed by a fix-up pass); without it they run
+ * one tile per workgroup. Results agree to fp32 summation order either way. */
 enum { HL_EPI_NONE = 0, HL_EPI_RESIDUAL = 1, HL_EPI_SWIGLU = 2 };
 int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
                     const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
