@@ -30,13 +30,18 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags. The prefill attention kernel takes maxima over raw matrix-core scores;
+# masked scores are -inf, never NaN, so fmax needs no NaN canonicalisation of its inputs.
+EXTRA_FLAGS = {"attention_prefill.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is noise
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -13,17 +13,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define HL_DEV __device__ __forceinline__
 
-// bf16 <-> fp32. bf16 is the top half of an fp32; the narrowing rounds to nearest even.
+// bf16 <-> fp32. bf16 is the top half of an fp32. Narrowing uses the CDNA4 packed conversion
+// (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN), one instruction for two values.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 HL_DEV float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 HL_DEV float bf_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 HL_DEV float bf_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
-HL_DEV uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+HL_DEV uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-HL_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+HL_DEV uint32_t f2bf(float f) { return pack_bf2(f, 0.f) & 0xffffu; }
 
 HL_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -33,6 +33,15 @@ HL_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 HL_DEV f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32). Softmax weights use it with x <= 8; results
+// below 2^-126 may flush to zero, a change below 2^-126 relative to the largest weight.
+HL_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// c + a.lo * b.lo + a.hi * b.hi over bf16 pairs, accumulated in fp32 (v_dot2_f32_bf16)
+HL_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
 }
 
 HL_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
