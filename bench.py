@@ -87,12 +87,18 @@ def main():
     ap.add_argument("--phase-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-phase", default=None,
+                    help="profiling aid: after set-up run only this phase --phase-reps times "
+                         "(qkv_rope_append, prefill_attention, decode_attention, gemm_o, "
+                         "rms_scale_mlp, gemm_gate_up, gemm_down) and print its timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="profiling aid: run a plain elementwise copy (read N MiB, write N MiB) "
+                         "--phase-reps times, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the hybrid layer step; multi-GPU runs "
-              "(sequence-parallel prefill exchange) are not part of this build. Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures the hybrid layer step on one GPU; the library has no multi-GPU "
+              "path (sharding is described, not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -104,6 +110,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = "cuda"
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 19  # bf16 elements in N MiB
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.phase_reps):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 2 * n, "bytes_written": 2 * n,
+                          "reps": args.phase_reps}), flush=True)
+        return
     name = args.workload
     if name.startswith("cfg4_"):
         spec = workloads.make_spec(4, name[len("cfg4_"):])
@@ -128,9 +144,12 @@ def main():
     def step():
         B.hybrid_layer_step(cfg, batch, x, w, kp, vp, out, ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    if args.only_phase is None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+    else:
+        args.steps = 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -139,7 +158,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = e0.elapsed_time(e1) / max(args.steps, 1)
 
     # ---- per-phase timing through the phase entry points (same kernels as the step)
     qd = s.n_q_heads * s.head_dim
@@ -172,6 +191,10 @@ def main():
         ("gemm_down", lambda: B.gemm_bf16_nt(mlp, w["w_down"], out, h2, B.HL_EPI_RESIDUAL,
                                              workspace=gws, stream=stream)),
     ]
+    if args.only_phase is not None:
+        phases = [p for p in phases if p[0] == args.only_phase]
+        if not phases:
+            raise SystemExit(f"no phase {args.only_phase} in this workload")
     phase_us = {}
     for pname, fn in phases:
         fn()
@@ -183,6 +206,11 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         phase_us[pname] = 1000.0 * a.elapsed_time(b) / args.phase_reps
+    if args.only_phase is not None:
+        print(json.dumps({"only_phase": args.only_phase, "workload": name,
+                          "reps": args.phase_reps, "avg_us": round(phase_us[args.only_phase], 2)}),
+              flush=True)
+        return
 
     cnt = algorithmic_counts(spec)
     # the QKV projection phase also holds its prep pass and the RoPE / append epilogue
