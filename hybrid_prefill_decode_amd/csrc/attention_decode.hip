@@ -43,7 +43,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
   __shared__ float sh_o[kWaves][D][16];
   __shared__ float sh_m[kWaves][16];
   __shared__ float sh_l[kWaves][16];
-  const int unit = blockIdx.x, kvh = blockIdx.y;
+  // KV head fastest in dispatch order: the Hkv workgroups of a unit read the Hkv adjacent
+  // 4 KB pieces of each block at about the same time
+  const int kvh = blockIdx.x % Hkv, unit = blockIdx.x / Hkv;
   const int s = units[3 * unit], pg0 = units[3 * unit + 1], di = units[3 * unit + 2];
   const int u0 = dec_seqs[3 * di + 1], nu = dec_seqs[3 * di + 2];
   const int row = q_start[s];
@@ -76,44 +78,47 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
   for (int i = 0; i < D / 16; ++i) o[i] = f32x4{};
   float m_run = -1e30f, l_run = 0.f;
 
-  for (int pa = pg0 + 2 * wave; pa < pg_end; pa += 2 * kWaves) {
+  // Software pipeline over this wave's page pairs (pairs p = pg0 + 2 wave + 8 i): while pair i
+  // is computed, the K/V loads of pair i + 1 and the block-table reads of pair i + 2 are in
+  // flight, so a wave never waits on a load it has just issued. Past the last pair the loads
+  // repeat the unit's last page (in bounds) and their results are not used.
+  struct Pair {
+    u32x4 k[2][D / 32];
+    u32x2 v[2][D / 16];
+  };
+  auto tbl = [&](int pa, int* blk) {
+    const int p0 = min(pa, pg_end - 1), p1 = min(pa + 1, pg_end - 1);
+    blk[0] = trow[p0];
+    blk[1] = trow[p1];
+  };
+  auto load = [&](const int* blk, Pair& P) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool in = blk[h] >= 0 && (long long)blk[h] < num_blocks;
+      const size_t base = ((size_t)(in ? blk[h] : 0) * Hkv + kvh) * page_elems;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        P.k[h][ks] = *reinterpret_cast<const u32x4*>(kpool + base + (size_t)col * D + 32 * ks + 8 * lg);
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+        P.v[h][mt] = *reinterpret_cast<const u32x2*>(vpool + base + (size_t)(16 * mt + col) * HL_BLOCK_SIZE + 4 * lg);
+    }
+  };
+  auto compute = [&](int pa, const int* blk, Pair& P) {
     const int pb = pa + 1;
-    const bool b_ok = pb < pg_end;
-    const int blk_a = trow[pa];
-    const int blk_b = b_ok ? trow[pb] : blk_a;
-    const bool a_in = blk_a >= 0 && (long long)blk_a < num_blocks;
-    const bool b_in = b_ok && blk_b >= 0 && (long long)blk_b < num_blocks;
-    const size_t base_a = ((size_t)(a_in ? blk_a : 0) * Hkv + kvh) * page_elems;
-    const size_t base_b = ((size_t)(b_in ? blk_b : 0) * Hkv + kvh) * page_elems;
-
-    // K rows: lane (lg, tok = col) reads d = 32 ks + 8 lg .. +7 of token col
-    u32x4 ka[D / 32], kb[D / 32];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const size_t off = (size_t)col * D + 32 * ks + 8 * lg;
-      ka[ks] = a_in ? *reinterpret_cast<const u32x4*>(kpool + base_a + off) : u32x4{0, 0, 0, 0};
-      kb[ks] = b_in ? *reinterpret_cast<const u32x4*>(kpool + base_b + off) : u32x4{0, 0, 0, 0};
-    }
-    // V^T: lane (lg, d-row col) reads tokens 4 lg .. 4 lg + 3 of page a and of page b
-    u32x2 va[D / 16], vb[D / 16];
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      const size_t off = (size_t)(16 * mt + col) * HL_BLOCK_SIZE + 4 * lg;
-      va[mt] = a_in ? *reinterpret_cast<const u32x2*>(vpool + base_a + off) : u32x2{0, 0};
-      vb[mt] = b_in ? *reinterpret_cast<const u32x2*>(vpool + base_b + off) : u32x2{0, 0};
-    }
-
+    const bool a_in = blk[0] >= 0 && (long long)blk[0] < num_blocks;
+    const bool b_in = pb < pg_end && blk[1] >= 0 && (long long)blk[1] < num_blocks;
     f32x4 sa = f32x4{}, sb = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      sa = mfma16x16x32(ka[ks], qf[ks], sa);
-      sb = mfma16x16x32(kb[ks], qf[ks], sb);
+      sa = mfma16x16x32(P.k[0][ks], qf[ks], sa);
+      sb = mfma16x16x32(P.k[1][ks], qf[ks], sb);
     }
     if (two_part) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        sa = mfma16x16x32(ka[ks], ql[ks], sa);
-        sb = mfma16x16x32(kb[ks], ql[ks], sb);
+        sa = mfma16x16x32(P.k[0][ks], ql[ks], sa);
+        sb = mfma16x16x32(P.k[1][ks], ql[ks], sb);
       }
     }
     // lane (lg, col) holds tokens 4 lg + i of both pages for head col
@@ -129,28 +134,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     tmax = wave_max_xor(tmax, 16);
     tmax = wave_max_xor(tmax, 32);
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = exp2f(sa[i] - m_new);
-      sb[i] = exp2f(sb[i] - m_new);
+      sa[i] = fast_exp2(sa[i] - m_new);
+      sb[i] = fast_exp2(sb[i] - m_new);
       psum += sa[i] + sb[i];
     }
     l_run = l_run * alpha + psum;
-    // zero V of tokens past the end (their weight is 0, the slot may hold anything)
-    if (tok_b + 4 > kv_len) {
+    // zero V of tokens past the end or of a page that is not used (weight 0, the slot may
+    // hold anything)
+    if (tok_b + 4 > kv_len || !a_in || !b_in) {
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const uint32_t ma = ((tok_a + 2 * e < kv_len) ? 0xffffu : 0u) |
-                              ((tok_a + 2 * e + 1 < kv_len) ? 0xffff0000u : 0u);
+          const uint32_t ma = ((a_in && tok_a + 2 * e < kv_len) ? 0xffffu : 0u) |
+                              ((a_in && tok_a + 2 * e + 1 < kv_len) ? 0xffff0000u : 0u);
           const uint32_t mb = ((b_in && tok_b + 2 * e < kv_len) ? 0xffffu : 0u) |
                               ((b_in && tok_b + 2 * e + 1 < kv_len) ? 0xffff0000u : 0u);
-          va[mt][e] &= ma;
-          vb[mt][e] &= mb;
+          P.v[0][mt][e] &= ma;
+          P.v[1][mt][e] &= mb;
         }
       }
     }
@@ -160,7 +166,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) {
       o[mt] *= alpha;
-      o[mt] = mfma16x16x32(u32x4{va[mt][0], va[mt][1], vb[mt][0], vb[mt][1]}, pt, o[mt]);
+      o[mt] = mfma16x16x32(u32x4{P.v[0][mt][0], P.v[0][mt][1], P.v[1][mt][0], P.v[1][mt][1]}, pt,
+                           o[mt]);
+    }
+  };
+
+  const int first = pg0 + 2 * wave;
+  if (first < pg_end) {
+    int blk_cur[2], blk_nxt[2], blk_nn[2];
+    Pair cur, nxt;
+    tbl(first, blk_cur);
+    load(blk_cur, cur);
+    tbl(first + 2 * kWaves, blk_nxt);
+    for (int pa = first; pa < pg_end; pa += 2 * kWaves) {
+      load(blk_nxt, nxt);
+      tbl(pa + 4 * kWaves, blk_nn);
+      compute(pa, blk_cur, cur);
+      cur = nxt;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        blk_cur[h] = blk_nxt[h];
+        blk_nxt[h] = blk_nn[h];
+      }
     }
   }
 
@@ -277,7 +304,7 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   if (plan.n_dec_units <= 0) return hipSuccess;
   const float scale = cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
   const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(plan.n_dec_units, cfg.n_kv_heads), block(kThreads);
+  const dim3 grid(cfg.n_kv_heads * plan.n_dec_units), block(kThreads);
   if (cfg.head_dim == 128) {
     hipLaunchKernelGGL(decode_attn_kernel<128>, grid, block, 0, st, q_start, num_cached, q_rot,
                        q_lo, kpool, vpool, (long long)num_blocks, table, max_blocks, plan.dec_units,
