@@ -45,6 +45,12 @@ int check_cfg(const hl_layer_cfg* c) {
   if (c->block_size != HL_BLOCK_SIZE) return HL_ERR_SHAPE;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->softmax_scale >= 0.f))
     return HL_ERR_SHAPE;
+  // the GEMMs address their operands with 32-bit element offsets
+  const int64_t qkv_cols = (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+  const int64_t widest = std::max<int64_t>({qkv_cols, 2 * (int64_t)c->d_ff, c->hidden});
+  if (widest * std::max<int64_t>({(int64_t)c->hidden, (int64_t)c->d_ff,
+                                  (int64_t)c->n_q_heads * c->head_dim}) > (int64_t)UINT32_MAX)
+    return HL_ERR_SHAPE;
   return HL_OK;
 }
 
@@ -64,6 +70,11 @@ int check_batch(const hl_batch_desc* b) {
     if ((int64_t)b->h_num_cached[s] + qlen > (int64_t)1 << 30) return HL_ERR_DESC;
   }
   if (b->h_q_start[b->num_seqs] != b->num_tokens) return HL_ERR_DESC;
+  // token rows of every GEMM operand stay within 32-bit element offsets
+  const hl_layer_cfg* c = b->cfg;
+  const int64_t row = std::max<int64_t>({(int64_t)c->hidden, (int64_t)c->d_ff,
+                                         (int64_t)c->n_q_heads * c->head_dim});
+  if ((int64_t)b->num_tokens * row > (int64_t)UINT32_MAX) return HL_ERR_DESC;
   return HL_OK;
 }
 
@@ -83,29 +94,71 @@ int check_pages(const hl_batch_desc* b, const hl_kv_pages* kv, const hl_block_ta
   return HL_OK;
 }
 
-// Pages per decode work unit: the smallest power of two in [32, 256] that keeps the decode grid
-// within 16K workgroups (one partial costs about 1/split of the unit's KV bytes in extra traffic)
-// and no sequence above kMaxUnitsPerSeq units.
-int pick_split(const hl_batch_desc* b) {
-  const int hkv = b->cfg->n_kv_heads;
-  int64_t max_pages = 0;
-  for (int s = 0; s < b->num_seqs; ++s)
-    if (b->h_q_start[s + 1] - b->h_q_start[s] == 1)
-      max_pages = std::max<int64_t>(max_pages, ((int64_t)b->h_num_cached[s] + HL_BLOCK_SIZE) / HL_BLOCK_SIZE);
-  // no sequence may need more than kMaxUnitsPerSeq units (its merge weights live in LDS)
-  int floor_sp = 32;
-  while ((max_pages + floor_sp - 1) / floor_sp > hl::kMaxUnitsPerSeq) floor_sp *= 2;
-  if (floor_sp > 256) return floor_sp;
-  for (int sp = floor_sp; sp <= 256; sp *= 2) {
-    int64_t units = 0;
-    for (int s = 0; s < b->num_seqs; ++s) {
-      if (b->h_q_start[s + 1] - b->h_q_start[s] != 1) continue;
-      const int64_t pages = ((int64_t)b->h_num_cached[s] + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
-      units += (pages + sp - 1) / sp;
-    }
-    if (units * hkv <= 16384 || sp == 256) return sp;
+// Compute units of the current device (queried once per process; every supported device is
+// the same part).
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
   }
-  return 256;
+  return cus;
+}
+
+// Pages per decode work unit. A unit of n pages costs about n + kUnitOverhead page-times (query
+// load, state merge, partial write and merge read), and two workgroups run per compute unit (the
+// kernel's register budget), so `slots` units run at once. With equal-length decodes the units
+// run in whole rounds: cost = rounds * (largest unit + overhead). Otherwise the grid drains as a
+// list schedule: cost = total work / slots + the largest unit (its worst-case tail). Candidates
+// are a fixed ladder plus ceil(P_max / u) for small u (which tiles equal lengths exactly); the
+// cheapest wins, ties to the larger unit (fewer partials). No sequence may need more than
+// kMaxUnitsPerSeq units (its merge weights live in LDS).
+int pick_split(const hl_batch_desc* b) {
+  constexpr int64_t kUnitOverhead = 6;
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t hkv = b->cfg->n_kv_heads;
+  std::vector<int64_t> pages;
+  int64_t max_pages = 0, min_pages = INT64_MAX;
+  for (int s = 0; s < b->num_seqs; ++s)
+    if (b->h_q_start[s + 1] - b->h_q_start[s] == 1) {
+      const int64_t p = ((int64_t)b->h_num_cached[s] + HL_BLOCK_SIZE) / HL_BLOCK_SIZE;
+      pages.push_back(p);
+      max_pages = std::max(max_pages, p);
+      min_pages = std::min(min_pages, p);
+    }
+  if (pages.empty()) return 32;
+  const bool uniform = min_pages == max_pages;
+  const int64_t sp_min =
+      std::max<int64_t>(8, (max_pages + hl::kMaxUnitsPerSeq - 1) / hl::kMaxUnitsPerSeq);
+  const int64_t sp_max = std::max<int64_t>(sp_min, std::min<int64_t>(max_pages, 1 << 20));
+  std::vector<int64_t> cand = {8,  12,  16,  20,  24,  28,  32,  40,  48,   56,   64,  80,
+                               96, 112, 128, 160, 192, 256, 320, 384, 512, 768, 1024};
+  for (int64_t u = 1; u <= 64; ++u) cand.push_back((max_pages + u - 1) / u);
+  int64_t best_sp = sp_min;
+  double best_cost = -1.0;
+  for (int64_t sp : cand) {
+    sp = std::min(std::max(sp, sp_min), sp_max);
+    int64_t units = 0;
+    for (int64_t p : pages) units += (p + sp - 1) / sp;
+    const int64_t job = std::min(sp, max_pages) + kUnitOverhead;
+    double cost;
+    if (uniform) {
+      cost = (double)((units * hkv + slots - 1) / slots) * (double)job;
+    } else {
+      double work = 0.0;
+      for (int64_t p : pages) work += (double)(p + kUnitOverhead * ((p + sp - 1) / sp));
+      cost = work * (double)hkv / (double)slots + (double)job;
+    }
+    if (best_cost < 0.0 || cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && sp > best_sp)) {
+      best_cost = cost;
+      best_sp = sp;
+    }
+  }
+  return (int)best_sp;
 }
 
 void make_plan(const hl_batch_desc* b, HostPlan* p) {
@@ -334,6 +387,7 @@ int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf1
     return HL_ERR_ARG;
   if (epilogue == HL_EPI_RESIDUAL && !residual) return HL_ERR_NULL;
   if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
+  if ((int64_t)m * k > (int64_t)UINT32_MAX || (int64_t)n * k > (int64_t)UINT32_MAX) return HL_ERR_ARG;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c) || (residual && !aligned16(residual)))
     return HL_ERR_ALIGN;
   return hip_rc(hl::launch_gemm(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),

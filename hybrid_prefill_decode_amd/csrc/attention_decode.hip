@@ -179,8 +179,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(
     load(blk_cur, cur);
     tbl(first + 2 * kWaves, blk_nxt);
     for (int pa = first; pa < pg_end; pa += 2 * kWaves) {
-      load(blk_nxt, nxt);
+      // table reads first: the load counter drains in issue order, so the next iteration can
+      // wait for them without waiting for this iteration's K/V loads
       tbl(pa + 4 * kWaves, blk_nn);
+      load(blk_nxt, nxt);
       compute(pa, blk_cur, cur);
       cur = nxt;
 #pragma unroll

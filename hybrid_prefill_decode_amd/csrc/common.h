@@ -62,6 +62,7 @@ struct Plan {
 };
 
 // Per-token data of one step (filled by the first prep pass, read by the QKV GEMM epilogue).
+constexpr int32_t kDecodeBit = 1 << 30;  // positions are below 2^30 (checked on the host)
 struct TokenInfo {
   const int32_t* q_start;
   const int32_t* num_cached;
@@ -71,7 +72,7 @@ struct TokenInfo {
   int64_t num_blocks;
   int32_t head_dim;
   float rope_theta;
-  int32_t* tok_pos;   // [T] absolute position
+  int32_t* tok_pos;   // [T] absolute position, | kDecodeBit for a decode token (q_len == 1)
   int32_t* tok_blk;   // [T] physical block of that position (-1 if out of range)
   float2* rope_cs;    // [T][head_dim / 2] (cos, sin)
 };

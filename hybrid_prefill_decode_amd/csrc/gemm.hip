@@ -4,16 +4,18 @@
 // over the whole token matrix reads each weight once for both phases ("ConfluxServe" summary,
 // "Why can linear layers be batched but attention cannot?").
 //
-// Main loop (512 threads = 8 waves, 2 per SIMD; K advances 64 per tile). A and W tiles are staged
-// through LDS in 128-byte rows whose 16-byte chunks are XOR-swizzled with (row / 2) mod 8, which
-// keeps every 16-lane group of a fragment read on distinct banks. Each wave owns a grid of
-// v_mfma_f32_32x32x16_bf16 blocks. One register staging set: while the matrix cores work on tile
-// t, the wave reads the fragments of the next k16 step (double-buffered fragments) and, during the
-// last step, writes tile t+1 into the other LDS buffer and issues the global loads of tile t+2;
-// sched_group_barrier threads these memory instructions between the MFMAs instead of leaving them
-// in phases of their own (measured on gfx950: ~1.3x over a phased loop). Tiles are dealt so that
-// consecutive tile ids land on the same XCD (workgroups go to the 8 XCDs round-robin) and, within
-// an XCD, the M tiles of one N column run together, so a weight tile is fetched from HBM once.
+// Main loop (256 threads = 4 waves, one per SIMD; K advances 64 per tile). Each wave owns a
+// (BM/2) x (BN/2) block of v_mfma_f32_32x32x16_bf16 outputs whose fp32 accumulators live in the
+// accumulation registers (256 of them for a 256 x 256 tile), so the 256 ordinary registers stay
+// free for fragments and staging. A and W tiles are staged through LDS in 128-byte rows whose
+// 16-byte chunks are XOR-swizzled with (row / 2) mod 8, which keeps every 16-lane group of a
+// fragment read on distinct banks. Per tile: k16 steps 0..2 each carry the fragment reads of
+// the next step and a third of the tile's staging work (LDS writes of tile t+1 from registers,
+// global loads of tile t+2 into them), issued one per MFMA in an order pinned with sched_barrier;
+// the barrier sits before step 3, whose MFMAs hide the fragment reads of the next tile's step 0.
+// Tiles are dealt so that consecutive tile ids land on the same XCD (workgroups go to the 8 XCDs
+// round-robin) and, within an XCD, the M tiles of one N column run together, so a weight tile is
+// fetched from HBM once.
 //
 // Schedules. Wide GEMMs run one tile per workgroup. Narrow ones (N = hidden for the O and down
 // projections leaves fewer tiles than compute units) run stream-K: exactly one workgroup per CU,
@@ -31,7 +33,7 @@ namespace {
 using hl::GemmEpi;
 using hl::kEpiRopeAppend;
 
-constexpr int BK = 64, kThreads = 512, kWaves = 8;
+constexpr int BK = 64, kThreads = 256;
 
 // 128-byte LDS rows (64 bf16 of K); 16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 7)
 HL_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
@@ -51,16 +53,17 @@ struct Sched {
   float* part;             // stream-K: [grid][2][BM * BN] fp32 pieces
 };
 
-template <int BM, int BN, int WAVES_M>
+template <int BM, int BN>
 struct Cfg {
-  static constexpr int WAVES_N = kWaves / WAVES_M;
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
   static constexpr int MT = WM / 32, NT = WN / 32;
   static constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + W_BYTES;
   static constexpr int A_CH = A_BYTES / 16 / kThreads, W_CH = W_BYTES / 16 / kThreads;
   static constexpr int NCH = A_CH + W_CH;
+  static constexpr int PER = (NCH + 2) / 3;  // staging chunks per k16 step 0..2
   static constexpr int MAIN_LDS = 2 * STAGE;
+  static_assert(A_CH * kThreads * 16 == A_BYTES && W_CH * kThreads * 16 == W_BYTES, "staging");
 };
 
 // Row of the W tile that feeds block t of wave column wn (SwiGLU pairs gate block t with up
@@ -73,113 +76,118 @@ HL_DEV int w_block_row(int wn, int t) {
 }
 
 // One tile's K range [kb, ke) into acc (acc zeroed here).
-template <int EPI, int BM, int BN, int WAVES_M>
+template <int EPI, int BM, int BN>
 HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N,
                      int K, int mt, int nt, int kb, int ke, uint8_t* smem,
-                     f32x16 (&acc)[Cfg<BM, BN, WAVES_M>::MT][Cfg<BM, BN, WAVES_M>::NT]) {
-  using C = Cfg<BM, BN, WAVES_M>;
-  constexpr int MT = C::MT, NT = C::NT, NCH = C::NCH, A_CH = C::A_CH, NMF = MT * NT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+                     f32x16 (&acc)[Cfg<BM, BN>::MT][Cfg<BM, BN>::NT]) {
+  using C = Cfg<BM, BN>;
+  constexpr int MT = C::MT, NT = C::NT, NCH = C::NCH, A_CH = C::A_CH, PER = C::PER;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int m0 = mt * BM;
   const int half_n = N >> 1;
 
-  // Global sources. Rows past M read row M-1: a C row depends only on its own A row and padded
-  // C rows are never stored, so the loads need no branch.
-  const hl_bf16* src[NCH];
-  int dst_off[NCH];
+  // Staging: chunk i of a thread is row (tid / 8) + 32 i of the A tile (i < A_CH) or of the W
+  // tile, 16-byte column tid % 8. Rows past M read row M-1: a C row depends only on its own A
+  // row and padded C rows are never stored, so the loads need no branch. Offsets are 32-bit
+  // element counts (the host bounds M K and N K below 2^31); the W row bases are wave-uniform.
+  const int srow = tid >> 3, sch8 = (tid & 7) * 8;
+  uint32_t a_off[A_CH];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    if (i < A_CH) {
-      const int q = tid + kThreads * i, row = q >> 3, ch = q & 7;
-      src[i] = A + (size_t)min(m0 + row, M - 1) * K + ch * 8;
-      dst_off[i] = swz(row, ch);
-    } else {
-      const int q = tid + kThreads * (i - A_CH), row = q >> 3, ch = q & 7;
-      int wr;
-      if (EPI == HL_EPI_SWIGLU)
-        wr = (row < BN / 2) ? nt * (BN / 2) + row : half_n + nt * (BN / 2) + (row - BN / 2);
-      else
-        wr = nt * BN + row;
-      src[i] = W + (size_t)wr * K + ch * 8;
-      dst_off[i] = C::A_BYTES + swz(row, ch);
-    }
+  for (int i = 0; i < A_CH; ++i) a_off[i] = (uint32_t)min(m0 + srow + 32 * i, M - 1) * K + sch8;
+  const uint32_t w_thr = (uint32_t)srow * K + sch8;
+  auto gsrc = [&](int i, int k0) {
+    if (i < A_CH) return reinterpret_cast<const u32x4*>(A + (a_off[i] + (uint32_t)k0));
+    const int j = i - A_CH;  // W rows 32 j .. 32 j + 31 of the tile
+    int wr0;
+    if (EPI == HL_EPI_SWIGLU)
+      wr0 = (32 * j < BN / 2) ? nt * (BN / 2) + 32 * j : half_n + nt * (BN / 2) + 32 * j - BN / 2;
+    else
+      wr0 = nt * BN + 32 * j;
+    return reinterpret_cast<const u32x4*>(W + ((uint32_t)wr0 * K + w_thr + (uint32_t)k0));
+  };
+  // 32 rows are 4096 bytes and keep the swizzle phase, so chunk i lands 4096 i past chunk 0
+  const int dst0 = swz(srow, tid & 7);
+  auto dst = [&](int i) { return i < A_CH ? dst0 + 4096 * i : C::A_BYTES + dst0 + 4096 * (i - A_CH); };
+  // fragment offsets per k16 step: A block i at + 4096 i, W block t at + 128 * w_block_row(t)
+  int fa_off[BK / 16], fw_off[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    fa_off[ks] = swz(wm * C::WM + (lane & 31), 2 * ks + (lane >> 5));
+    fw_off[ks] = C::A_BYTES + swz(lane & 31, 2 * ks + (lane >> 5));
   }
-  int a_off[MT], w_off[NT];
+  int w_row[NT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) a_off[i] = wm * C::WM + i * 32 + (lane & 31);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) w_off[t] = w_block_row<EPI, BN, C::WN, NT>(wn, t) + (lane & 31);
+  for (int t = 0; t < NT; ++t) w_row[t] = 128 * w_block_row<EPI, BN, C::WN, NT>(wn, t);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x16{};
 
-  const int last = (ke - 1) * BK;
   u32x4 rg[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) rg[i] = *reinterpret_cast<const u32x4*>(src[i] + kb * BK);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(smem + dst_off[i]) = rg[i];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    rg[i] = *reinterpret_cast<const u32x4*>(src[i] + min((kb + 1) * BK, last));
-  __syncthreads();
+  u32x4 fa[2][MT], fw[2][NT];
+  // fragment q of a step: A block q (q < MT) or W block q - MT
+  auto rd1 = [&](const uint8_t* base, int set, int ks, int q) {
+    if (q < MT) fa[set][q] = *reinterpret_cast<const u32x4*>(base + fa_off[ks] + 4096 * q);
+    else fw[set][q - MT] = *reinterpret_cast<const u32x4*>(base + fw_off[ks] + w_row[q - MT]);
+  };
 
+  const int last = (ke - 1) * BK;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) rg[i] = *gsrc(i, kb * BK);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(smem + dst(i)) = rg[i];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) rg[i] = *gsrc(i, min((kb + 1) * BK, last));
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MT + NT; ++q) rd1(smem, 0, 0, q);
+
+  // Each k16 step issues, in this order and pinned by sched_barrier: MFMA q, fragment read q of
+  // the next step (q < MT + NT), and for steps 0..2 one staging pair (LDS write of tile t+1,
+  // global load of tile t+2). Step 3 follows the barrier and reads the next tile's step-0
+  // fragments from the other buffer.
   for (int kt = kb; kt < ke; ++kt) {
     const int buf = (kt - kb) & 1;
     const uint8_t* ab = smem + buf * C::STAGE;
-    const uint8_t* wb = ab + C::A_BYTES;
     uint8_t* nb = smem + (buf ^ 1) * C::STAGE;
     const int knext = min((kt + 2) * BK, last);  // past the end: re-read the last tile (unused)
-    u32x4 fa[2][MT], fw[2][NT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) fa[0][i] = *reinterpret_cast<const u32x4*>(ab + swz(a_off[i], lane >> 5));
-#pragma unroll
-    for (int t = 0; t < NT; ++t) fw[0][t] = *reinterpret_cast<const u32x4*>(wb + swz(w_off[t], lane >> 5));
-    __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
+      const int cur = ks & 1, nx = cur ^ 1;
+      if (ks == BK / 16 - 1) {
+        // tile t+1 complete in the other buffer; every read of this buffer has been issued
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint8_t* rbase = (ks == BK / 16 - 1) ? nb : ab;
+      const int rks = (ks == BK / 16 - 1) ? 0 : ks + 1;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[i][t] = mfma32x32x16(fa[cur][i], fw[cur][t], acc[i][t]);
-      if (ks + 1 < BK / 16) {
-        const int ch = 2 * (ks + 1) + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) fa[cur ^ 1][i] = *reinterpret_cast<const u32x4*>(ab + swz(a_off[i], ch));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) fw[cur ^ 1][t] = *reinterpret_cast<const u32x4*>(wb + swz(w_off[t], ch));
-#pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-          if (q < MT + NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      for (int q = 0; q < MT * NT; ++q) {
+        acc[q / NT][q % NT] = mfma32x32x16(fa[cur][q / NT], fw[cur][q % NT], acc[q / NT][q % NT]);
+        if (q < MT + NT) rd1(rbase, nx, rks, q);
+        if (ks < BK / 16 - 1 && q < PER && ks * PER + q < NCH) {
+          const int i = ks * PER + q;
+          *reinterpret_cast<u32x4*>(nb + dst(i)) = rg[i];
+          rg[i] = *gsrc(i, knext);
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(nb + dst_off[i]) = rg[i];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) rg[i] = *reinterpret_cast<const u32x4*>(src[i] + knext);
-#pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-          if (q < NCH) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);          // LDS write
-          else if (q < 2 * NCH) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
   }
+  // the next call (stream-K) or the epilogue reuses the LDS
+  __syncthreads();
 }
 
 // Rows of the 32 x 32 block a lane holds: 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32.
 HL_DEV int block_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
 // RoPE + KV append for 8 pairs of one staged row: `srow` points at the fp32 row of one head.
+// Only decode tokens (`decode`) get the low half of q: decode attention alone reads it.
 template <int HD>
-HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot, const float* srow,
-                           int c) {
+HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot, bool decode,
+                           const float* srow, int c) {
   constexpr int half = HD / 2;
   const int Hq = ep.n_q_heads, Hkv = ep.n_kv_heads;
   float a[8], b[8];
@@ -208,7 +216,7 @@ HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot,
     const size_t o = ((size_t)gm * Hq + gh) * HD + 8 * c;
     *reinterpret_cast<u32x4*>(ep.q_rot + o) = pack8(a);
     *reinterpret_cast<u32x4*>(ep.q_rot + o + half) = pack8(b);
-    if (ep.q_lo) {  // what bf16 dropped, so decode attention can use q to ~16 bits
+    if (ep.q_lo && decode) {  // what bf16 dropped, so decode attention can use q to ~16 bits
       float la[8], lb[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -237,18 +245,18 @@ HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot,
 
 // SK: stream-K run of (tile, k-step) iterations; otherwise exactly one tile per workgroup (kept a
 // separate instantiation so the one-tile kernels carry no loop state in registers).
-template <int EPI, int BM, int BN, int WAVES_M, int HD, bool SK>
+template <int EPI, int BM, int BN, int HD, bool SK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
     const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, hl_bf16* __restrict__ C, int M,
     int N, int K, GemmEpi ep, Sched sc) {
-  using CF = Cfg<BM, BN, WAVES_M>;
+  using CF = Cfg<BM, BN>;
   constexpr int MT = CF::MT, NT = CF::NT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float rs_sh[BM];
   __shared__ int pos_sh[BM];
   __shared__ int blk_sh[BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int wm = wave >> 1, wn = wave & 1;
   const int lc = lane & 31;
   const int half_n = N >> 1;
   const int tiles = sc.mtiles * sc.ntiles;
@@ -264,14 +272,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
     it_end = min(it + sc.ipw, tiles * sc.nk);
   }
   int seg = 0;
-  while (it < it_end) {
+  do {
     const int tile = it / sc.nk;
     const int kb = SK ? it % sc.nk : 0;
     const int ke = SK ? min(sc.nk, kb + (it_end - it)) : sc.nk;
     const int mt = tile % sc.mtiles, nt = tile / sc.mtiles;
     const int m0 = mt * BM;
     f32x16 acc[MT][NT];
-    mainloop<EPI, BM, BN, WAVES_M>(A, W, M, N, K, mt, nt, kb, ke, smem, acc);
+    mainloop<EPI, BM, BN>(A, W, M, N, K, mt, nt, kb, ke, smem, acc);
     it += ke - kb;
     if (SK && (kb != 0 || ke != sc.nk)) {
       // a piece of a split tile: raw fp32 partial for the fix-up kernel (slot 0 = the first
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
         const int gm = m0 + r;
         if (gm >= M) continue;
         rope_store_row<HD>(ep, gm, nt * heads + hi, blk_sh[r], pos_sh[r] & (HL_BLOCK_SIZE - 1),
-                           st + r * BN + hi * HD, c);
+                           (pos_sh[r] & hl::kDecodeBit) != 0, st + r * BN + hi * HD, c);
       }
     } else {
       const hl_bf16* R = ep.residual;
@@ -351,9 +359,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
           }
         }
     }
-    if constexpr (!SK) break;
-    __syncthreads();  // rs_sh / LDS reuse by the next segment
-  }
+    if constexpr (SK) __syncthreads();  // rs_sh / LDS reuse by the next segment
+  } while (SK && it < it_end);
 }
 
 // Stream-K fix-up: for each split tile, sum its pieces and apply the plain or residual epilogue
@@ -390,13 +397,13 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
   *reinterpret_cast<u32x2*>(C + o) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
 }
 
-template <int EPI, int BM, int BN, int WAVES_M, int HD = 0>
+template <int EPI, int BM, int BN, int HD = 0>
 hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
                         const GemmEpi& epi, float* part, size_t part_bytes, hipStream_t st) {
-  using CF = Cfg<BM, BN, WAVES_M>;
+  using CF = Cfg<BM, BN>;
   constexpr bool kCanSplit = (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL);
-  auto kern = gemm_bf16_nt_kernel<EPI, BM, BN, WAVES_M, HD, false>;
-  auto kern_sk = gemm_bf16_nt_kernel<EPI, BM, BN, WAVES_M, HD, kCanSplit>;
+  auto kern = gemm_bf16_nt_kernel<EPI, BM, BN, HD, false>;
+  auto kern_sk = gemm_bf16_nt_kernel<EPI, BM, BN, HD, kCanSplit>;
   const int lds = (EPI == kEpiRopeAppend) ? max(CF::MAIN_LDS, BM * BN * 4) : CF::MAIN_LDS;
   static bool attr = false;
   if (!attr) {
@@ -450,19 +457,19 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
   float* part = static_cast<float*>(ws);
   switch (epi.kind) {
     case HL_EPI_NONE:
-      if (n % 256 == 0) return launch_tiles<HL_EPI_NONE, 128, 256, 2>(a, w, c, m, n, k, epi, part, ws_bytes, st);
-      return launch_tiles<HL_EPI_NONE, 128, 128, 4>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      if (n % 256 == 0) return launch_tiles<HL_EPI_NONE, 128, 256>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      return launch_tiles<HL_EPI_NONE, 128, 128>(a, w, c, m, n, k, epi, part, ws_bytes, st);
     case HL_EPI_RESIDUAL:
-      if (n % 256 == 0) return launch_tiles<HL_EPI_RESIDUAL, 128, 256, 2>(a, w, c, m, n, k, epi, part, ws_bytes, st);
-      return launch_tiles<HL_EPI_RESIDUAL, 128, 128, 4>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      if (n % 256 == 0) return launch_tiles<HL_EPI_RESIDUAL, 128, 256>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      return launch_tiles<HL_EPI_RESIDUAL, 128, 128>(a, w, c, m, n, k, epi, part, ws_bytes, st);
     case HL_EPI_SWIGLU:
-      if (n % 256 == 0 && m > 512) return launch_tiles<HL_EPI_SWIGLU, 256, 256, 4>(a, w, c, m, n, k, epi, nullptr, 0, st);
-      if (n % 256 == 0) return launch_tiles<HL_EPI_SWIGLU, 128, 256, 2>(a, w, c, m, n, k, epi, nullptr, 0, st);
-      return launch_tiles<HL_EPI_SWIGLU, 128, 128, 4>(a, w, c, m, n, k, epi, nullptr, 0, st);
+      if (n % 256 == 0 && m > 512) return launch_tiles<HL_EPI_SWIGLU, 256, 256>(a, w, c, m, n, k, epi, nullptr, 0, st);
+      if (n % 256 == 0) return launch_tiles<HL_EPI_SWIGLU, 128, 256>(a, w, c, m, n, k, epi, nullptr, 0, st);
+      return launch_tiles<HL_EPI_SWIGLU, 128, 128>(a, w, c, m, n, k, epi, nullptr, 0, st);
     default:
       return epi.head_dim == 128
-                 ? launch_tiles<kEpiRopeAppend, 128, 256, 2, 128>(a, w, c, m, n, k, epi, nullptr, 0, st)
-                 : launch_tiles<kEpiRopeAppend, 128, 256, 2, 64>(a, w, c, m, n, k, epi, nullptr, 0, st);
+                 ? launch_tiles<kEpiRopeAppend, 128, 256, 128>(a, w, c, m, n, k, epi, nullptr, 0, st)
+                 : launch_tiles<kEpiRopeAppend, 128, 256, 64>(a, w, c, m, n, k, epi, nullptr, 0, st);
   }
 }
 

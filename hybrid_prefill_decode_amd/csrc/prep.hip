@@ -35,7 +35,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int half = D >> 1;
     if (threadIdx.x == 0) {
       const int blk = table[(size_t)lo * max_blocks + p / HL_BLOCK_SIZE];
-      tok_pos[row] = p;
+      const bool decode = q_start[lo + 1] - q_start[lo] == 1;
+      tok_pos[row] = p | (decode ? hl::kDecodeBit : 0);
       tok_blk[row] = (blk >= 0 && (long long)blk < num_blocks) ? blk : -1;
     }
     for (int j = threadIdx.x; j < half; j += kThreads) {

@@ -59,7 +59,8 @@ enum {
   HL_ERR_NULL = -1,      /* a required pointer is NULL */
   HL_ERR_SHAPE = -2,     /* unsupported layer dimensions (see hl_layer_cfg) */
   HL_ERR_DESC = -3,      /* bad batch descriptor: q_len < 1, q_start not starting at 0 or not
-                            increasing, q_start[S] != num_tokens, num_cached < 0 */
+                            increasing, q_start[S] != num_tokens, num_cached < 0, or
+                            num_tokens * max(hidden, d_ff, Hq * head_dim) >= 2^32 */
   HL_ERR_BLOCK = -4,     /* a sequence needs more than max_blocks_per_seq pages, or a used
                             block id lies outside [0, num_blocks) */
   HL_ERR_ALIGN = -5,     /* a device pointer is not 16-byte aligned */
@@ -71,8 +72,11 @@ enum {
 typedef uint16_t hl_bf16; /* raw bfloat16 bits */
 
 /* Layer dimensions. Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0 and
- * n_q_heads / n_kv_heads <= 16; hidden % 64 == 0; d_ff % 64 == 0; n_q_heads * head_dim % 64 == 0;
- * block_size == HL_BLOCK_SIZE. softmax_scale == 0 means 1 / sqrt(head_dim). */
+ * n_q_heads / n_kv_heads <= 16; hidden % 128 == 0; d_ff % 64 == 0; n_q_heads * head_dim % 64 == 0;
+ * (n_q_heads + 2 n_kv_heads) * head_dim % 256 == 0; every weight matrix and every
+ * max(hidden, d_ff, n_q_heads * head_dim)-wide row block below 2^32 elements; block_size ==
+ * HL_BLOCK_SIZE; rms_eps >= 0, rope_theta > 0, softmax_scale >= 0. softmax_scale == 0 means
+ * 1 / sqrt(head_dim). Anything else is HL_ERR_SHAPE. */
 typedef struct {
   int32_t hidden;
   int32_t n_q_heads;
@@ -181,7 +185,8 @@ int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_
  *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + s * A W^T
  *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
  *                   c [m, f] = silu(s * A W_gate^T) * (s * A W_up^T)
- * Requirements: k % 64 == 0, n % 128 == 0, m >= 0. `workspace` (device, may be NULL): when it
+ * Requirements: k % 64 == 0, n % 128 == 0, m >= 0, m * k and n * k at most 2^32 - 1 (operands
+ * are addressed with 32-bit element offsets; HL_ERR_ARG otherwise). `workspace` (device, may be NULL): when it
  * holds hl_gemm_workspace_bytes() bytes, shapes with fewer output tiles than compute units run a
  * stream-K schedule (partial tiles in the workspace, summed by a fix-up pass); without it they run
  * one tile per workgroup. Results agree to fp32 summation order either way. */
