@@ -54,6 +54,37 @@ def algorithmic_counts(spec):
     }
 
 
+def pct(v):
+    """median, p10 and p90 of a sorted list of milliseconds"""
+    if not v:
+        return None
+    q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4),
+            "n": len(v)}
+
+
+def gpu_clocks():
+    """Current SCLK / MCLK as rocm-smi reports them (a child process; None if unavailable)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi")
+    if not exe:
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=20)
+    except Exception:
+        return None
+    out = {}
+    for line in r.stdout.splitlines():
+        low = line.lower()
+        for key in ("sclk", "mclk"):
+            if key in low and "mhz" in low and key not in out:
+                tok = [t for t in line.replace("(", " ").replace(")", " ").split() if t.lower().endswith("mhz")]
+                if tok:
+                    out[key] = tok[0]
+    return out or None
+
+
 def kernel_source_hash(names):
     h = hashlib.sha256()
     for n in names:
@@ -81,10 +112,13 @@ def read_traffic(profile_txt, src_hash):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg2", help="cfg1..cfg5, cfg4_prefill_only, cfg4_decode_only")
     ap.add_argument("--phase-reps", type=int, default=20)
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="steps timed one at a time after overwriting 1 GiB (evicts the 256 MB "
+                         "last-level cache), reported next to the warm steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-phase", default=None,
@@ -150,15 +184,34 @@ def main():
         torch.cuda.synchronize()
     else:
         args.steps = 0
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # K timed steps back to back; an event after every step gives the per-step distribution
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / max(args.steps, 1)
+    ms_step = evs[0].elapsed_time(evs[-1]) / max(args.steps, 1)
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    clocks = gpu_clocks() if args.only_phase is None else None
+
+    # cold steps: the last-level cache holds nothing of the previous step
+    cold = []
+    if args.only_phase is None and args.cold_reps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_reps):
+            scratch.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del scratch
+        cold.sort()
 
     # ---- per-phase timing through the phase entry points (same kernels as the step)
     qd = s.n_q_heads * s.head_dim
@@ -182,6 +235,10 @@ def main():
     if has_dec:
         phases.append(("decode_attention",
                        lambda: B.decode_attention(cfg, batch, q_rot, kp, vp, attn, ws, stream)))
+    if has_pre and has_dec:
+        # both paths in the one fused launch the step uses (compare with the two phases above)
+        phases.append(("hybrid_attention",
+                       lambda: B.attention(cfg, batch, q_rot, kp, vp, attn, ws, stream)))
     phases += [
         ("gemm_o", lambda: B.gemm_bf16_nt(attn, w["w_o"], h2, x, B.HL_EPI_RESIDUAL,
                                           workspace=gws, stream=stream)),
@@ -234,6 +291,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": pct(per_step),
+        "cold_step_ms": pct(cold) if cold else None,
+        "gpu_clocks_after_timed_steps": clocks,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -290,7 +350,7 @@ def cpu_baseline(spec, x, w, table, dev, budget_s):
         OL.layer_step(spec.shape, xh, wh, spec.seqs, cached, table)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 5:
+        if el >= budget_s or reps >= 50:
             break
     return {"value": round(reps * spec.num_tokens / el, 2), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",

@@ -30,9 +30,11 @@ CFLAGS = [
 ]
 
 
-# Per-source extra flags. The prefill attention kernel takes maxima over raw matrix-core scores;
-# masked scores are -inf, never NaN, so fmax needs no NaN canonicalisation of its inputs.
-EXTRA_FLAGS = {"attention_prefill.hip": ["-fno-honor-nans"]}
+# Per-source extra flags. The prefill attention code takes maxima over raw matrix-core scores;
+# masked scores are -inf (selected, never computed from garbage), so fmax needs no NaN
+# canonicalisation of its inputs. The fused kernel contains the same code.
+EXTRA_FLAGS = {"attention_prefill.hip": ["-fno-honor-nans"],
+               "attention_hybrid.hip": ["-fno-honor-nans"]}
 
 
 def sources():

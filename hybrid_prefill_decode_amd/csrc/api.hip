@@ -26,8 +26,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 struct HostPlan {
   int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
+  bool fused = false;  // prefill and decode attention in one launch
   // workspace byte offsets
-  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
+  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_counters = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
          o_blk = 0, o_cs = 0, o_qlo = 0, o_qrot = 0, o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0,
          o_gemm = 0, total = 0;
   size_t gemm_bytes = 0;
@@ -161,10 +162,42 @@ int pick_split(const hl_batch_desc* b) {
   return (int)best_sp;
 }
 
+// Pages per decode work unit when prefill and decode run in the fused launch: its workers claim
+// units dynamically, so units only need to be small enough that every worker gets several (the
+// queue then balances the two paths), and large enough to amortise a unit's fixed cost.
+int pick_split_fused(const hl_batch_desc* b) {
+  int64_t total = 0, max_pages = 0;
+  for (int s = 0; s < b->num_seqs; ++s)
+    if (b->h_q_start[s + 1] - b->h_q_start[s] == 1) {
+      const int64_t p = ((int64_t)b->h_num_cached[s] + HL_BLOCK_SIZE) / HL_BLOCK_SIZE;
+      total += p;
+      max_pages = std::max(max_pages, p);
+    }
+  const int64_t workers = 2 * (int64_t)device_cus();
+  int64_t sp = (total * b->cfg->n_kv_heads + 4 * workers - 1) / (4 * workers);
+  sp = std::min<int64_t>(std::max<int64_t>(sp, 32), 256);
+  sp = std::max<int64_t>(sp, (max_pages + hl::kMaxUnitsPerSeq - 1) / hl::kMaxUnitsPerSeq);
+  return (int)sp;
+}
+
 void make_plan(const hl_batch_desc* b, HostPlan* p) {
   const hl_layer_cfg& c = *b->cfg;
   *p = HostPlan{};
-  p->split_pages = pick_split(b);
+  // Fused attention pays when the prefill work is comparable to the decode work (it then hides
+  // behind the decode streams) or when the decode work is so large that unit granularity does not
+  // matter; a small prefill next to a moderate decode runs best as two tuned launches. The
+  // estimates use sustained rates of the two kernels on this part (prefill ~0.7 PFLOP/s, decode
+  // ~5 TB/s); only their ratio matters.
+  double pre_flops = 0.0, dec_bytes = 0.0;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const double n = b->h_q_start[s + 1] - b->h_q_start[s], kv = b->h_num_cached[s] + n;
+    if (n == 1) dec_bytes += kv * c.n_kv_heads * c.head_dim * 4.0;
+    else pre_flops += 4.0 * c.head_dim * c.n_q_heads * (n * b->h_num_cached[s] + n * (n + 1) / 2);
+  }
+  const double pre_us = pre_flops / 0.7e9, dec_us = dec_bytes / 5.0e6;  // flop/us, byte/us
+  p->fused = pre_flops > 0 && dec_bytes > 0 &&
+             (pre_us >= 0.5 * dec_us || (dec_us >= 1000.0 && pre_us >= 0.02 * dec_us));
+  p->split_pages = p->fused ? pick_split_fused(b) : pick_split(b);
   for (int s = 0; s < b->num_seqs; ++s) {
     const int qlen = b->h_q_start[s + 1] - b->h_q_start[s];
     if (qlen == 1) {
@@ -184,6 +217,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
     off += align_up(bytes);
     return o;
   };
+  p->o_counters = take(sizeof(int32_t) * hl::kPlanCounters);
   p->o_dec_units = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_units);
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
   p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);
@@ -210,6 +244,7 @@ hl::Plan device_plan(const HostPlan& hp, void* ws) {
   p.dec_seqs = reinterpret_cast<int32_t*>(base + hp.o_dec_seqs);
   p.pre_tiles = reinterpret_cast<int32_t*>(base + hp.o_pre_tiles);
   p.dec_part = reinterpret_cast<float*>(base + hp.o_part);
+  p.counters = reinterpret_cast<int32_t*>(base + hp.o_counters);
   p.n_dec_units = hp.n_dec_units;
   p.n_dec_seqs = hp.n_dec_seqs;
   p.n_pre_tiles = hp.n_pre_tiles;
@@ -307,6 +342,13 @@ int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q
   int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, hp.split_pages,
                                   hl::kPrefillQTile, dp, st));
   if (rc) return rc;
+  if (do_prefill && do_decode && hp.fused) {
+    // both paths in one fused launch: prefill and decode overlap on every compute unit
+    return hip_rc(hl::launch_hybrid_attention(*b->cfg, b->q_start, b->num_cached, q_rot, q_lo,
+                                              kv->k, kv->v, kv->num_blocks, bt->table,
+                                              bt->max_blocks_per_seq, dp, device_cus(), attn_out,
+                                              st));
+  }
   if (do_prefill) {
     rc = hip_rc(hl::launch_prefill_attention(*b->cfg, b->q_start, b->num_cached, q_rot, kv->k,
                                              kv->v, kv->num_blocks, bt->table,

@@ -21,40 +21,11 @@
 // tiles hit in that XCD's L2. Softmax runs in fp32 in the exp2 domain. Keys past a query's
 // position are masked by select and V rows past the sequence end are zeroed before they reach LDS,
 // so unused cache slots never reach the result.
-#include <type_traits>
-
-#include "common.h"
+#include "attn_prefill_core.h"
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kKeys = 64;  // keys per step = 4 pages
-
-template <int D>
-struct PrefillSmem {
-  static constexpr int kKBytes = kKeys * D * 2;     // K tile [64][D]
-  static constexpr int kVBytes = 4 * D * 32;        // V^T tile [4 pages][D][16]
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kTotal = 2 * kStage;
-  static constexpr int kChunks = kKBytes / 16;      // 16-byte chunks of K (same count for V)
-  static constexpr int kPer = kChunks / kThreads;   // per thread: 4 (D = 128) or 2 (D = 64)
-  static constexpr int kChunksPerPage = kChunks / 4;
-};
-
-// K tile rows of D*2 bytes; the 16-byte chunk c of row r is XOR-swizzled so that the 16 lanes of
-// one read group (rows r..r+15, same chunk) hit distinct banks.
-template <int D>
-HL_DEV int k_off(int r, int c) {
-  if (D == 128) return r * 256 + ((c ^ (r & 15)) << 4);
-  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-// V^T tile: dim row d of page pg holds its 16 tokens in quad order (0, 2, 1, 3), so that the
-// 16 bytes the P V product needs in lane half h (tokens 4h..4h+3 and 8+4h..8+4h+3) are contiguous;
-// the two 16-byte halves of rows d and d + 8 are swapped so 16 consecutive rows hit distinct banks.
-template <int D>
-HL_DEV int v_off(int pg, int d, int half) {
-  return pg * D * 32 + d * 32 + ((half ^ ((d >> 3) & 1)) << 4);
-}
+using hl::prefill::PrefillArgs;
 
 // Bijection from dispatch order to work order that keeps consecutive work items on one XCD.
 HL_DEV int xcd_item(int bid, int nblk) {
@@ -63,231 +34,22 @@ HL_DEV int xcd_item(int bid, int nblk) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// One workgroup per work item; the items of one (tile, KV head) group are consecutive in work
+// order and so share an XCD (their K/V tiles hit in its L2).
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_attn_kernel(
-    const int32_t* __restrict__ q_start, const int32_t* __restrict__ num_cached,
-    const hl_bf16* __restrict__ q_rot, const hl_bf16* __restrict__ kpool,
-    const hl_bf16* __restrict__ vpool, long long num_blocks, const int32_t* __restrict__ table,
-    int max_blocks, const int32_t* __restrict__ tiles, int Hq, int Hkv, float scale_log2,
-    hl_bf16* __restrict__ attn_out) {
-  using SM = PrefillSmem<D>;
+__global__ __launch_bounds__(hl::prefill::kThreads, 2) void prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // work item -> (query tile, KV head, head within the group); the heads of one KV head are
-  // consecutive items and so share an XCD
-  const int g = Hq / Hkv;
   const int item = xcd_item(blockIdx.x, gridDim.x);
-  const int tile = item / Hq, hrem = item % Hq;
-  const int h = hrem;  // items are ordered (tile, kv head, head in group) = (tile, h)
-  const int s = tiles[2 * tile], r0 = tiles[2 * tile + 1];
-  const int qs = q_start[s], n = q_start[s + 1] - qs, c = num_cached[s];
-  const int kvh = h / g;
-  const int kv_len = c + n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl32 = lane >> 5;
-  const int tile_rows = min(128, n - r0);
-  const int key_end = c + r0 + tile_rows;  // exclusive key bound of the whole tile
-  const int nkt = (key_end + kKeys - 1) / kKeys;
-  const int wr0 = r0 + 32 * wave;
-  const int my_row = wr0 + (lane & 31);
-  const bool row_ok = my_row < n;
-  const int qpos = row_ok ? c + my_row : -1;
-  const int32_t* trow = table + (size_t)s * max_blocks;
-  const size_t page_elems = (size_t)HL_BLOCK_SIZE * D;
-
-  // Q^T operand: slot j of lane-half hl32 at k-step ks holds d = 16 ks + 8 hl32 + j
-  u32x4 qf[D / 16];
-  {
-    const hl_bf16* qp = q_rot + ((size_t)(qs + (row_ok ? my_row : 0)) * Hq + h) * D + 8 * hl32;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-  }
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-  float m_run = -1e30f, l_run = 0.f;
-
-  // Per-thread slice of a key tile: 16-byte chunk q = tid + kThreads * i lies in page
-  // pg = q / kChunksPerPage at element offset w * 8, w = q % kChunksPerPage. Consecutive i step
-  // the page by kThreads / kChunksPerPage and every LDS destination by 4096 bytes.
-  constexpr int kPagesPerI = kThreads / SM::kChunksPerPage;
-  const int pg0 = tid / SM::kChunksPerPage, w = tid % SM::kChunksPerPage;
-  // K: page pg, token row w / (D / 8), chunk w % (D / 8)
-  const int k_dst = k_off<D>(pg0 * 16 + w / (D / 8), w % (D / 8));
-  // V^T: dim row w / 2 of page pg, token quads 2 (w & 1) and 2 (w & 1) + 1, which sit at
-  // quad positions (w & 1) and 2 + (w & 1) (8-byte pieces)
-  const int v_dst0 = v_off<D>(pg0, w >> 1, 0) + 8 * (w & 1);
-  const int v_dst1 = v_off<D>(pg0, w >> 1, 1) + 8 * (w & 1);
-  static_assert(kPagesPerI * 16 * D * 2 == 4096 && kPagesPerI * D * 32 == 4096, "tile slice");
-  // byte addresses: page base + this thread's chunk; a block adds blk * block_bytes
-  const uint32_t block_bytes = (uint32_t)(Hkv * page_elems * 2);
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kpool) + (size_t)kvh * page_elems * 2 + 16 * w;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vpool) + (size_t)kvh * page_elems * 2 + 16 * w;
-  const uint32_t nb = (uint32_t)min(num_blocks, (long long)INT32_MAX);
-
-  u32x4 rk[SM::kPer], rv[SM::kPer];
-  int blk[SM::kPer];
-  const int npages = (kv_len + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
-  // Three-stage software pipeline over key tiles: step kt first stores tile kt + 1 to LDS, then
-  // issues the K/V loads of tile kt + 2 and the block-table reads of tile kt + 3, each from data
-  // that arrived during the previous step, so no step waits on a load it issued itself. Loads
-  // are unconditional: a page past the sequence repeats the last page, whose surplus rows are
-  // masked (K by the score mask, V by zeroing in sstore); invalid table entries read block 0.
-  auto tload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < SM::kPer; ++i)
-      blk[i] = trow[min(4 * kt + pg0 + kPagesPerI * i, npages - 1)];
-  };
-  auto gload = [&]() {
-#pragma unroll
-    for (int i = 0; i < SM::kPer; ++i) {
-      const uint32_t b = ((uint32_t)blk[i] < nb) ? (uint32_t)blk[i] : 0u;
-      const size_t off = (size_t)b * block_bytes;
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + off);
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + off);
-    }
-  };
-  // ZERO: V rows past the sequence end are zeroed when stored (their weight is 0, the slot may
-  // hold anything, and 0 * NaN would poison the product); only the last tile has such rows
-  auto sstore = [&](int buf, int kt, auto zero) {
-    uint8_t* kb = smem + buf * SM::kStage;
-    uint8_t* vb = kb + SM::kKBytes;
-#pragma unroll
-    for (int i = 0; i < SM::kPer; ++i) {
-      u32x4 vv = rv[i];
-      if constexpr (decltype(zero)::value) {
-        const int tok0 = (4 * kt + pg0 + kPagesPerI * i) * HL_BLOCK_SIZE + 8 * (w & 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo_ok = (tok0 + 2 * e < kv_len) ? 0x0000ffffu : 0u;
-          const uint32_t hi_ok = (tok0 + 2 * e + 1 < kv_len) ? 0xffff0000u : 0u;
-          vv[e] &= (lo_ok | hi_ok);
-        }
-      }
-      *reinterpret_cast<u32x4*>(kb + k_dst + 4096 * i) = rk[i];
-      *reinterpret_cast<u32x2*>(vb + v_dst0 + 4096 * i) = u32x2{vv[0], vv[1]};
-      *reinterpret_cast<u32x2*>(vb + v_dst1 + 4096 * i) = u32x2{vv[2], vv[3]};
-    }
-  };
-  const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
-
-  // One key tile. MASKED: keys past a query's position are masked and the stored tile's V rows
-  // past the sequence end are zeroed; both are needed only on the last few tiles of a query tile.
-  auto step = [&](int kt, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int buf = kt & 1;
-    const uint8_t* kb = smem + buf * SM::kStage;
-    const uint8_t* vb = kb + SM::kKBytes;
-    // the next tile into the other buffer (last read one step ago, before the barrier), then
-    // the loads of the two tiles after it (past the end they repeat the last tile, unused)
-    sstore(buf ^ 1, min(kt + 1, nkt - 1), masked);
-    gload();
-    tload(min(kt + 3, nkt - 1));
-    // S^T for the two 32-key halves of the tile; half hb holds keys
-    // 32 hb + 8 (i / 4) + 4 hl32 + (i & 3) of query lane & 31
-    f32x16 st[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 ka =
-            *reinterpret_cast<const u32x4*>(kb + k_off<D>(32 * hb + (lane & 31), 2 * ks + hl32));
-        st[hb] = mfma32x32x16(ka, qf[ks], st[hb]);
-      }
-    if constexpr (kMasked) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt * kKeys + 32 * hb + 8 * (i >> 2) + 4 * hl32 + (i & 3);
-          st[hb][i] = (key <= qpos) ? st[hb][i] : -INFINITY;
-        }
-    }
-    // Softmax in the exp2 domain with the scale folded in: the max is taken on raw scores and
-    // p = 2^(s * scale_log2 - m) costs one FMA and one exp2.
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(st[hb][i], st[hb][i + 1]));
-    // loads first, stores between the score MFMAs, K fragment reads running ahead of them
-    __builtin_amdgcn_sched_group_barrier(0x020, 3 * SM::kPer, 0);  // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             // LDS read
-#pragma unroll
-    for (int q = 0; q < D / 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (q < D / 8 - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      if (q < 3 * SM::kPer) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-    }
-    tmax = wave_max_xor(tmax, 32) * scale_log2;
-    // Lazy rescaling: the reference m_run moves only when a tile max exceeds it by more than 8,
-    // so every p stays <= 2^8 (far inside fp32 / bf16 range) and most tiles skip the rescale of
-    // o and l; o / l does not depend on the reference. The branch is taken wave-wide (a lane
-    // that did not need it rescales by its own alpha <= 1, which is equally valid).
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + 8.f)) {
-      const float m_new = fmaxf(tmax, m_run);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
-    }
-    // Page by page: the weights of page t (P^T operand: half t / 2, regs 8 (t % 2) .. +7), their
-    // sum (taken from the same bf16 weights that multiply V, by a packed dot product with
-    // (1, 1)), then the page's D / 32 products, so the exponentials of page t + 1 overlap the
-    // matrix cores working on page t.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(st[t >> 1][8 * (t & 1) + 2 * e], scale_log2, -m_run));
-        const float p1 = fast_exp2(fmaf(st[t >> 1][8 * (t & 1) + 2 * e + 1], scale_log2, -m_run));
-        pb[e] = pack_bf2(p0, p1);
-        l_run = dot2_bf16(pb[e], ones, l_run);
-      }
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(vb + v_off<D>(t, 32 * mt + (lane & 31), hl32));
-        o[mt] = mfma32x32x16(va, pb, o[mt]);
-      }
-    }
-    __syncthreads();
-  };
-
-  tload(0);
-  gload();
-  tload(min(1, nkt - 1));
-  sstore(0, 0, std::true_type{});
-  gload();
-  tload(min(2, nkt - 1));
-  __syncthreads();
-  // Tiles wholly at or below the tile's first query position need neither the mask nor V
-  // zeroing; the step before the first tile that needs them already stores it, so runs masked.
-  const int kt_m = (c + r0 + 1) / kKeys;
-  const int kt_a = max(0, min(kt_m - 1, nkt));
-  for (int kt = 0; kt < kt_a; ++kt) step(kt, std::false_type{});
-  for (int kt = kt_a; kt < nkt; ++kt) step(kt, std::true_type{});
-
-  if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
-  hl_bf16* op = attn_out + ((size_t)(qs + my_row) * Hq + h) * D;
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * mt + 8 * g4 + 4 * hl32;
-      const u32x2 v = {pack_bf2(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv),
-                       pack_bf2(o[mt][4 * g4 + 2] * inv, o[mt][4 * g4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(op + d0) = v;
-    }
+  hl::prefill::prefill_item<D>(a, item / a.Hq, item % a.Hq, smem);
 }
 
 }  // namespace
 
 namespace hl {
+
+using prefill::PrefillArgs;
+using prefill::PrefillSmem;
+using prefill::kThreads;
 
 hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
                                     const int32_t* num_cached, const hl_bf16* q_rot,
@@ -298,6 +60,9 @@ hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_st
   const float scale = cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(plan.n_pre_tiles * cfg.n_q_heads), block(kThreads);
+  const PrefillArgs args{q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
+                         max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
+                         attn_out};
   if (cfg.head_dim == 128) {
     static bool attr = false;
     if (!attr) {
@@ -306,15 +71,9 @@ hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_st
       (void)hipGetLastError();
       attr = true;
     }
-    hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, block, PrefillSmem<128>::kTotal, st,
-                       q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
-                       max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       attn_out);
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, block, PrefillSmem<128>::kTotal, st, args);
   } else {
-    hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, block, PrefillSmem<64>::kTotal, st,
-                       q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
-                       max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       attn_out);
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, block, PrefillSmem<64>::kTotal, st, args);
   }
   return hipGetLastError();
 }

@@ -56,6 +56,8 @@ struct Plan {
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
   int32_t* pre_tiles;      // [n_pre_tiles][2]: (seq, first query row within the sequence)
   float* dec_part;         // [n_dec_units][Hkv][group][head_dim + 2] partial (o, m, l)
+  int32_t* counters;       // [kPlanCounters] work-queue counters of the fused attention kernel,
+                           // zeroed by the plan kernel
   int32_t n_dec_units, n_dec_seqs, n_pre_tiles;
   int32_t split_pages;     // pages per decode work unit
   int32_t max_pre_kv;      // longest key range of any prefill tile (host-side estimate)
@@ -99,6 +101,7 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
                        hipStream_t st);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
                        int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
+constexpr int kPlanCounters = 16;
 constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
 hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
                           int32_t cols, float eps, hipStream_t st);
@@ -121,6 +124,17 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
                                    const hl_bf16* kpool, const hl_bf16* vpool,
                                    int64_t num_blocks, const int32_t* table, int32_t max_blocks,
                                    const Plan& plan, hl_bf16* attn_out, hipStream_t st);
+
+hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, const Plan& plan,
+                               hl_bf16* attn_out, hipStream_t st);
+// Prefill and decode attention of one batch in a single launch (plus the decode merge); `cus`
+// is the device's compute-unit count.
+hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
+                                   const int32_t* num_cached, const hl_bf16* q_rot,
+                                   const hl_bf16* q_lo, const hl_bf16* kpool,
+                                   const hl_bf16* vpool, int64_t num_blocks, const int32_t* table,
+                                   int32_t max_blocks, const Plan& plan, int32_t cus,
+                                   hl_bf16* attn_out, hipStream_t st);
 
 constexpr int kPrefillQTile = 128;  // query rows per prefill work tile
 

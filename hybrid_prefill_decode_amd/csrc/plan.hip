@@ -36,8 +36,10 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
                                                         int num_seqs, int split_pages, int q_tile,
                                                         int32_t* __restrict__ dec_units,
                                                         int32_t* __restrict__ dec_seqs,
-                                                        int32_t* __restrict__ pre_tiles) {
+                                                        int32_t* __restrict__ pre_tiles,
+                                                        int32_t* __restrict__ counters) {
   __shared__ int buf[kThreads];
+  if (threadIdx.x < hl::kPlanCounters) counters[threadIdx.x] = 0;
   int base_u = 0, base_d = 0, base_t = 0;
   for (int s0 = 0; s0 < num_seqs; s0 += kThreads) {
     const int s = s0 + threadIdx.x;
@@ -84,7 +86,8 @@ hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_
                        int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st) {
   if (num_seqs <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, st, q_start, num_cached, num_seqs,
-                     split_pages, q_tile, plan.dec_units, plan.dec_seqs, plan.pre_tiles);
+                     split_pages, q_tile, plan.dec_units, plan.dec_seqs, plan.pre_tiles,
+                     plan.counters);
   return hipGetLastError();
 }
 }  // namespace hl

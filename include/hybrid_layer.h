@@ -211,9 +211,16 @@ int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q
 
 /* Attention of every sequence of the batch over its cached keys plus its new ones (the new K/V
  * must already be in the cache, as hl_rope_kv_append leaves them). q_rot [T, Hq d] device;
- * writes attn_out [T, Hq d]. Uses the batch workspace. hl_attention runs both paths;
- * hl_prefill_attention only rows of sequences with q_len > 1, hl_decode_attention only rows of
- * sequences with q_len == 1 (other rows are left untouched). */
+ * writes attn_out [T, Hq d]. Uses the batch workspace. hl_prefill_attention computes only rows of
+ * sequences with q_len > 1, hl_decode_attention only rows of sequences with q_len == 1 (other
+ * rows are left untouched). hl_attention computes both: when the batch holds both kinds it runs
+ * them in ONE fused launch whose persistent workers share every compute unit between the
+ * compute-bound prefill items and the bandwidth-bound decode units (the two attention paths of a
+ * hybrid step are independent and overlap: "ConfluxServe" summary, "Why can linear layers be
+ * batched but attention cannot?"; a fused prefill-decode kernel is what the overlap needs,
+ * "Chunked prefill (stall-free batching), explained", "Simulated numbers: choosing the budget").
+ * Its rows are bit-identical to those of the two separate entry points. hybrid_layer_step uses
+ * the same path. */
 int hl_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
                  const hl_block_table* block_table, hl_bf16* attn_out);
 int hl_prefill_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,

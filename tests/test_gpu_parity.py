@@ -167,6 +167,10 @@ ATTN_CASES = {
                                           (31, 33), (1000, 1), (511, 1)]),
     "g16_d128": (workloads.LayerShape(2048, 16, 1, 128, 512), [(100, 77), (600, 1), (17, 1)]),
     "g5_d128": (workloads.LayerShape(1280, 10, 2, 128, 512), [(40, 300), (2047, 1), (2048, 1)]),
+    # fused launch with far more decode units than prefill items, and the other way round
+    "many_decodes": (workloads.SHAPES["tiny"], [(7, 200)] + [(17 * i % 1500, 1) for i in range(300)]),
+    "many_prefill": (workloads.LayerShape(1280, 10, 2, 128, 512),
+                     [(64 * i, 257 + 31 * i) for i in range(6)] + [(900, 1), (3, 1)]),
 }
 
 
@@ -191,7 +195,7 @@ def test_attention_paths_vs_oracle(case):
         assert_close(got[pre], ref[pre], "prefill attention rows")
     if dec.size:
         assert_close(got[dec], ref[dec], "decode attention rows")
-    # each path alone writes only its own rows
+    # each path alone writes only its own rows, bit-identical to the fused launch of both
     out2 = torch.full_like(q, float("nan"))
     B.decode_attention(cfg, b, q, kp, vp, out2, ws)
     torch.cuda.synchronize()
@@ -200,6 +204,14 @@ def test_attention_paths_vs_oracle(case):
         assert np.isnan(g2[pre]).all()
     if dec.size:
         assert np.array_equal(g2[dec], got[dec])
+    out3 = torch.full_like(q, float("nan"))
+    B.prefill_attention(cfg, b, q, kp, vp, out3, ws)
+    torch.cuda.synchronize()
+    g3 = f64(out3)
+    if dec.size:
+        assert np.isnan(g3[dec]).all()
+    if pre.size:
+        assert np.array_equal(g3[pre], got[pre])
 
 
 def test_rope_kv_append_vs_oracle():
