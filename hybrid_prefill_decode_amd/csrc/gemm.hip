@@ -34,6 +34,9 @@ using hl::GemmEpi;
 using hl::kEpiRopeAppend;
 
 constexpr int BK = 64, kThreads = 256;
+// stream-K: one workgroup per compute unit, each with up to two fp32 pieces of a 256 x 256 tile
+constexpr int kStreamKGrid = 256;
+constexpr size_t kStreamKWorkspace = (size_t)kStreamKGrid * 2 * 256 * 256 * 4;
 
 // 128-byte LDS rows (64 bf16 of K); 16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 7)
 HL_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
@@ -50,6 +53,7 @@ HL_DEV float silu(float g) { return g / (1.f + __expf(-g)); }
 struct Sched {
   int mtiles, ntiles, nk;  // tiles in M and N; k-steps per tile
   int ipw;                 // stream-K: k-steps per workgroup (0: one tile per workgroup)
+  int phase_runs;          // stream-K: run = dispatch index (else XCD-contiguous runs)
   float* part;             // stream-K: [grid][2][BM * BN] fp32 pieces
 };
 
@@ -261,14 +265,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
   const int half_n = N >> 1;
   const int tiles = sc.mtiles * sc.ntiles;
 
-  // work: one tile, or a stream-K run of (tile, k-step) iterations
+  // work: one tile, or a stream-K run of (tile, k-step) iterations. Runs are normally
+  // XCD-contiguous (the runs of one XCD cover adjacent tiles, the M tiles of one or two N columns,
+  // whose operands its L2 can hold for short K); with phase_runs, run r goes to XCD r mod 8, which
+  // puts runs that start at the same k-step on the same M tile of successive N columns together
+  // (they read the same A slices at the same time; for long K nothing else would be reused).
+  const int run = (SK && sc.phase_runs) ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
   int it = 0, it_end = 0;
   if constexpr (!SK) {
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    it = tile * sc.nk;
+    it = run * sc.nk;
     it_end = it + sc.nk;
   } else {
-    it = blockIdx.x * sc.ipw;
+    it = run * sc.ipw;
     it_end = min(it + sc.ipw, tiles * sc.nk);
   }
   int seg = 0;
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
     if (SK && (kb != 0 || ke != sc.nk)) {
       // a piece of a split tile: raw fp32 partial for the fix-up kernel (slot 0 = the first
       // segment of this workgroup's run, slot 1 = its last)
-      float* pdst = sc.part + ((size_t)blockIdx.x * 2 + (seg == 0 ? 0 : 1)) * BM * BN;
+      float* pdst = sc.part + ((size_t)run * 2 + (seg == 0 ? 0 : 1)) * BM * BN;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -399,7 +407,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
 
 template <int EPI, int BM, int BN, int HD = 0>
 hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
-                        const GemmEpi& epi, float* part, size_t part_bytes, hipStream_t st) {
+                        const GemmEpi& epi, float* part, bool streamk, hipStream_t st) {
   using CF = Cfg<BM, BN>;
   constexpr bool kCanSplit = (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL);
   auto kern = gemm_bf16_nt_kernel<EPI, BM, BN, HD, false>;
@@ -419,17 +427,22 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
   sc.ntiles = n / BN;
   sc.nk = k / BK;
   sc.ipw = 0;
+  sc.phase_runs = 0;
   sc.part = part;
   const int tiles = sc.mtiles * sc.ntiles;
   int grid = tiles;
-  // stream-K when the tiles leave compute units idle and the workspace can hold the pieces
-  const int cus = 256;
-  const bool streamk = kCanSplit && tiles < cus &&
-                       part && part_bytes >= (size_t)cus * 2 * BM * BN * 4 && sc.nk >= 4;
+  streamk = streamk && kCanSplit && part;
   if (streamk) {
     const int total = tiles * sc.nk;
-    sc.ipw = (total + cus - 1) / cus;
+    sc.ipw = (total + kStreamKGrid - 1) / kStreamKGrid;
     grid = (total + sc.ipw - 1) / sc.ipw;
+    // runs r and r + period start at the same k-step, `adv` tiles apart; dispatch order puts
+    // them on one XCD when the period is a multiple of 8, and on one M tile when adv is a
+    // multiple of the M tile count (tiles are numbered M-fastest)
+    int g = sc.ipw, h = sc.nk;
+    while (h) { const int t = g % h; g = h; h = t; }
+    const long period = sc.nk / g, adv = (long)sc.ipw * period / sc.nk;
+    sc.phase_runs = (k >= 8192 && period % 8 == 0 && adv % sc.mtiles == 0) ? 1 : 0;
   }
   if (streamk)
     hipLaunchKernelGGL(kern_sk, dim3(grid), dim3(kThreads), lds, st, a, w, c, m, n, k, epi, sc);
@@ -442,14 +455,41 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
   return hipGetLastError();
 }
 
+// Schedule of a plain / residual GEMM. Measured on the layer shapes: stream-K over 128 x 256 tiles
+// is the best or close to it everywhere (it fills every CU, and its pieces are small), except for
+// the long-K down projections, where 256 x 256 tiles (1.5x less LDS and L2 traffic per flop) win
+// once each workgroup's run is long enough to hide the larger pieces. Without a workspace, or when
+// the 128 x 256 tiles fill whole rounds: one tile per workgroup.
+struct PlainChoice {
+  bool wide;     // 256 x 256 tiles (else 128 x 256)
+  bool streamk;
+};
+PlainChoice choose_plain(int m, int n, int k, bool has_ws) {
+  const int nk = k / BK;
+  if (!has_ws || nk < 4) return PlainChoice{false, false};
+  const long narrow_tiles = (long)((m + 127) / 128) * (n / 256);
+  const long wide_tiles = (long)((m + 255) / 256) * (n / 256);
+  const long narrow_run = (narrow_tiles * nk + kStreamKGrid - 1) / kStreamKGrid;
+  const long wide_run = (wide_tiles * nk + kStreamKGrid - 1) / kStreamKGrid;
+  if (m > 128 && narrow_run >= 384 && wide_run >= 200) return PlainChoice{true, true};
+  return PlainChoice{false, narrow_tiles % kStreamKGrid != 0};
+}
+
+template <int EPI>
+hipError_t launch_plain(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
+                        const GemmEpi& epi, float* part, size_t ws_bytes, hipStream_t st) {
+  if (n % 256 != 0) return launch_tiles<EPI, 128, 128>(a, w, c, m, n, k, epi, nullptr, false, st);
+  const PlainChoice ch = choose_plain(m, n, k, part && ws_bytes >= kStreamKWorkspace);
+  if (ch.wide) return launch_tiles<EPI, 256, 256>(a, w, c, m, n, k, epi, part, ch.streamk, st);
+  return launch_tiles<EPI, 128, 256>(a, w, c, m, n, k, epi, part, ch.streamk, st);
+}
+
 }  // namespace
 
 namespace hl {
 
-// Stream-K pieces of the narrow GEMMs: 256 workgroups x 2 pieces x a 128 x 256 fp32 tile.
-size_t gemm_workspace_bytes(int32_t, int32_t, int32_t, int32_t) {
-  return (size_t)256 * 2 * 128 * 256 * 4;
-}
+// Stream-K pieces: up to kStreamKGrid workgroups x 2 pieces x a 256 x 256 fp32 tile.
+size_t gemm_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return kStreamKWorkspace; }
 
 hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,
                        int32_t k, const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -457,19 +497,17 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
   float* part = static_cast<float*>(ws);
   switch (epi.kind) {
     case HL_EPI_NONE:
-      if (n % 256 == 0) return launch_tiles<HL_EPI_NONE, 128, 256>(a, w, c, m, n, k, epi, part, ws_bytes, st);
-      return launch_tiles<HL_EPI_NONE, 128, 128>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      return launch_plain<HL_EPI_NONE>(a, w, c, m, n, k, epi, part, ws_bytes, st);
     case HL_EPI_RESIDUAL:
-      if (n % 256 == 0) return launch_tiles<HL_EPI_RESIDUAL, 128, 256>(a, w, c, m, n, k, epi, part, ws_bytes, st);
-      return launch_tiles<HL_EPI_RESIDUAL, 128, 128>(a, w, c, m, n, k, epi, part, ws_bytes, st);
+      return launch_plain<HL_EPI_RESIDUAL>(a, w, c, m, n, k, epi, part, ws_bytes, st);
     case HL_EPI_SWIGLU:
-      if (n % 256 == 0 && m > 512) return launch_tiles<HL_EPI_SWIGLU, 256, 256>(a, w, c, m, n, k, epi, nullptr, 0, st);
-      if (n % 256 == 0) return launch_tiles<HL_EPI_SWIGLU, 128, 256>(a, w, c, m, n, k, epi, nullptr, 0, st);
-      return launch_tiles<HL_EPI_SWIGLU, 128, 128>(a, w, c, m, n, k, epi, nullptr, 0, st);
+      if (n % 256 == 0 && m > 512) return launch_tiles<HL_EPI_SWIGLU, 256, 256>(a, w, c, m, n, k, epi, nullptr, false, st);
+      if (n % 256 == 0) return launch_tiles<HL_EPI_SWIGLU, 128, 256>(a, w, c, m, n, k, epi, nullptr, false, st);
+      return launch_tiles<HL_EPI_SWIGLU, 128, 128>(a, w, c, m, n, k, epi, nullptr, false, st);
     default:
       return epi.head_dim == 128
-                 ? launch_tiles<kEpiRopeAppend, 128, 256, 128>(a, w, c, m, n, k, epi, nullptr, 0, st)
-                 : launch_tiles<kEpiRopeAppend, 128, 256, 64>(a, w, c, m, n, k, epi, nullptr, 0, st);
+                 ? launch_tiles<kEpiRopeAppend, 128, 256, 128>(a, w, c, m, n, k, epi, nullptr, false, st)
+                 : launch_tiles<kEpiRopeAppend, 128, 256, 64>(a, w, c, m, n, k, epi, nullptr, false, st);
   }
 }
 

@@ -65,6 +65,59 @@ def test_gemm_vs_oracle(m, n, k, epi, scaled):
     assert_close(f64(c), ref, "gemm")
 
 
+@pytest.mark.parametrize("m,n,k", [(1040, 1024, 512), (300, 512, 1024), (1, 256, 256)])
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL])
+def test_gemm_streamk_vs_oracle(m, n, k, epi):
+    """With a workspace the plain / residual GEMM may split tiles over workgroups (stream-K):
+    fp32 pieces summed by the fix-up kernel. Small K runs make every tile a multi-piece one."""
+    say(f"gemm stream-K m={m} n={n} k={k} epi={epi}")
+    a = _randn((m, k), 21 + m)
+    w = _randn((n, k), 22 + n, 0.05)
+    res = _randn((m, n), 23 + k)
+    ws = torch.empty(B.gemm_workspace_bytes(m, n, k, epi), dtype=torch.uint8, device=DEV)
+    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt(a, w, c, res if epi == B.HL_EPI_RESIDUAL else None, epi, workspace=ws)
+    torch.cuda.synchronize()
+    ref = OL.linear(f64(a), f64(w))
+    if epi == B.HL_EPI_RESIDUAL:
+        ref = ref + f64(res)
+    assert_close(f64(c), ref, "gemm stream-K")
+
+
+def _edge_sample(size, tile, count, seed):
+    """Indices that include both edges of every tile plus the ragged end, and random fill."""
+    idx = {0, size - 1}
+    for t in range(0, size, tile):
+        idx.update({t, min(t + tile - 1, size - 1)})
+    rng = np.random.default_rng(seed)
+    idx.update(rng.integers(0, size, count).tolist())
+    return torch.tensor(sorted(idx), dtype=torch.long)
+
+
+# The O and down projections of the layer shapes with the layer's workspace: these are the shapes
+# whose schedules differ (128 x 256 or 256 x 256 stream-K, XCD-contiguous or phase-aligned runs).
+# The oracle computes a sampled block of outputs: rows at every M tile edge plus random rows,
+# columns at every N tile edge plus random columns.
+@pytest.mark.parametrize("m,n,k", [(1040, 4096, 4096), (1040, 4096, 12288), (2144, 5120, 17408),
+                                   (4160, 4096, 12288), (1024, 8192, 28672)])
+def test_gemm_layer_shapes_sampled(m, n, k):
+    say(f"gemm layer shape m={m} n={n} k={k} residual, workspace")
+    a = _randn((m, k), 31 + m)
+    w = _randn((n, k), 32 + n, 0.02)
+    res = _randn((m, n), 33 + k)
+    ws = torch.empty(B.gemm_workspace_bytes(m, n, k, B.HL_EPI_RESIDUAL), dtype=torch.uint8,
+                     device=DEV)
+    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt(a, w, c, res, B.HL_EPI_RESIDUAL, workspace=ws)
+    torch.cuda.synchronize()
+    rows, cols = _edge_sample(m, 128, 48, m), _edge_sample(n, 256, 48, n)
+    A, W = f64(a[rows.to(DEV)]), f64(w[cols.to(DEV)])
+    ref = OL.linear(A, W) + f64(res[rows.to(DEV)][:, cols.to(DEV)])
+    got = f64(c[rows.to(DEV)][:, cols.to(DEV)])
+    assert_close(got, ref, "gemm layer shape (sampled)")
+    assert not torch.isnan(c).any().item(), "unwritten outputs"
+
+
 @pytest.mark.parametrize("rows,cols", [(1, 256), (68, 256), (5, 8192), (3, 20480)])
 def test_rmsnorm_vs_oracle(rows, cols):
     say(f"rmsnorm rows={rows} cols={cols}")
