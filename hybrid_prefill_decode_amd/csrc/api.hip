@@ -217,7 +217,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
     off += align_up(bytes);
     return o;
   };
-  p->o_counters = take(sizeof(int32_t) * hl::kPlanCounters);
+  p->o_counters = take(sizeof(int32_t) * hl::kPlanCounters * hl::kCounterStride);
   p->o_dec_units = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_units);
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
   p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);

@@ -10,13 +10,19 @@
 // Persistent workers, two per compute unit. Workers 0..P-1 start on prefill items, the rest on
 // decode units; workgroups are dealt to the compute units one each before any gets a second, so
 // every unit holds one worker of each kind: the split of the units between the paths happens
-// inside each unit, where the matrix cores and the memory pipeline are both kept busy. Work is
-// claimed from device counters that the step's plan kernel zeroes: a prefill item comes from the
-// queue of the worker's XCD (the query heads of one KV head are consecutive items, so their K/V
-// tiles hit in that XCD's L2), then from the other XCDs' queues; a decode unit from the single
-// decode queue. A worker that drains its own kind helps with the other; every worker exits once all
-// queues are empty. Each item runs the same code as in the separate kernels, so the results are
-// bit-identical to theirs.
+// inside each unit, where the matrix cores and the memory pipeline are both kept busy.
+//
+// Queues. The items of each kind are dealt to 8 queues in contiguous runs, one per XCD (the query
+// heads of one KV head are consecutive prefill items, so their K/V tiles hit in that XCD's L2). A
+// worker's first item needs no claim: the l-th worker of a kind on XCD x takes the l-th item of
+// that kind's queue x. Further items are claimed from per-queue device counters (zeroed by the
+// step's plan kernel, each on its own 256-byte line) that number the claims past those first
+// items: a worker drains its own queue, then the other XCDs' queues of its kind, then helps with
+// the other kind, and exits once every queue is empty. A queue is read before it is incremented,
+// so drained queues cost no atomic. (One shared decode counter serialised every claim at one
+// memory location: with a few hundred workers that cost tens of microseconds per launch.)
+// Each item runs the same code as in the separate kernels, so the results are bit-identical to
+// theirs.
 #include "attn_decode_core.h"
 #include "attn_prefill_core.h"
 
@@ -41,58 +47,72 @@ constexpr int kHybridLds = PrefillSmem<D>::kTotal > (int)sizeof(DecodeLds<D>)
                                ? PrefillSmem<D>::kTotal
                                : (int)sizeof(DecodeLds<D>);
 
-// counters[0..7]: prefill queue of each XCD; counters[8]: decode queue.
-//
-// Queue sequence of a worker: a prefill worker visits its XCD's prefill queue, the other seven,
-// then the decode queue (stage 8); a decode worker visits the decode queue (stage 0), then the
-// eight prefill queues from its own XCD on. A claim is one atomic increment of the current stage's
-// counter by thread 0, broadcast through LDS; everything else about the queues is computed by all
-// threads alike, so control flow stays uniform across the workgroup (the only one-thread branches
-// are the atomic and the LDS write).
+// Queues 0..7: prefill items of XCD 0..7; queues 8..15: decode units of XCD 0..7 (decode units
+// are numbered after the prefill items). Everything about the queues is computed by all threads
+// alike, so control flow stays uniform across the workgroup; a claim is a peek and an atomic
+// increment by thread 0, broadcast through LDS (the only one-thread branch).
 struct Queues {
   int32_t* counters;
-  int n_pre, n_dec, xcd;
+  int n_pre, n_dec;  // items of each kind
+  int wp, w;         // prefill workers are blocks [0, wp), decode workers [wp, w)
+  int xcd;           // this worker's XCD (blocks go to the 8 XCDs round-robin)
   bool pre_worker;
-  HL_DEV bool is_dec(int stage) const { return pre_worker ? stage == 8 : stage == 0; }
-  HL_DEV int32_t* counter(int stage) const {
-    return is_dec(stage) ? &counters[8] : &counters[(xcd + (pre_worker ? stage : stage - 1)) & 7];
+  HL_DEV int begin(int q) const {
+    return q < 8 ? queue_begin(q, n_pre) : n_pre + queue_begin(q - 8, n_dec);
   }
-  // [begin, end) of the stage's items in claim numbering (prefill items first, then decode)
-  HL_DEV void range(int stage, int& beg, int& end) const {
-    if (is_dec(stage)) {
-      beg = n_pre;
-      end = n_pre + n_dec;
-    } else {
-      const int x = (xcd + (pre_worker ? stage : stage - 1)) & 7;
-      beg = queue_begin(x, n_pre);
-      end = queue_begin(x + 1, n_pre);
-    }
+  HL_DEV int end(int q) const {
+    return q < 8 ? queue_begin(q + 1, n_pre) : n_pre + queue_begin(q - 7, n_dec);
   }
-  // the claimed item for ticket i of `stage`, or -1 if that queue is drained
-  HL_DEV int resolve(int stage, int i) const {
-    int beg, end;
-    range(stage, beg, end);
-    return beg + i < end ? beg + i : -1;
+  // first block of queue q's kind on its XCD, and how many blocks of that kind it holds
+  HL_DEV int first_block(int q) const {
+    const int lo = q < 8 ? 0 : wp;
+    return lo + (((q & 7) - lo) % 8 + 8) % 8;
+  }
+  HL_DEV int workers_on(int q) const {
+    const int hi = q < 8 ? wp : w, f = first_block(q);
+    return f < hi ? (hi - f + 7) / 8 : 0;
+  }
+  // items of queue q taken without a claim (one per worker of its kind on its XCD)
+  HL_DEV int statics(int q) const { return min(workers_on(q), end(q) - begin(q)); }
+  HL_DEV int32_t* counter(int q) const { return counters + q * hl::kCounterStride; }
+  // queue of stage s (0..15): the worker's own kind from its own XCD on, then the other kind
+  HL_DEV int queue_at(int s) const {
+    const int own = pre_worker ? 0 : 8;
+    return s < 8 ? own + ((xcd + s) & 7) : (8 - own) + ((xcd + s - 8) & 7);
+  }
+  // this worker's first item (no claim), or -1
+  HL_DEV int first_item(int block) const {
+    const int q = (pre_worker ? 0 : 8) + xcd;
+    const int l = (block - first_block(q)) / 8;
+    return l < statics(q) ? begin(q) + l : -1;
+  }
+  // item of claim ticket t of queue q, or -1 if the queue is drained
+  HL_DEV int resolve(int q, int t) const {
+    const int i = begin(q) + statics(q) + t;
+    return (t >= 0 && i < end(q)) ? i : -1;
   }
 };
 
-// one ticket of `stage` for the whole workgroup (called by every thread)
-HL_DEV int wg_ticket(const Queues& qs, int stage, int* s_tick) {
-  if (threadIdx.x == 0) *s_tick = atomicAdd(qs.counter(stage), 1);
+// a claim from queue q for the whole workgroup (called by every thread): -1 if it is drained
+HL_DEV int wg_claim_queue(const Queues& qs, int q, int* s_tick) {
+  if (qs.begin(q) + qs.statics(q) >= qs.end(q)) return -1;  // nothing beyond the first items
+  if (threadIdx.x == 0) {
+    const int seen = __hip_atomic_load(qs.counter(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_tick = (qs.begin(q) + qs.statics(q) + seen < qs.end(q)) ? atomicAdd(qs.counter(q), 1) : -1;
+  }
   __syncthreads();
-  const int t = *s_tick;
+  // every lane reads the same value; readfirstlane tells the compiler so, which keeps the item
+  // index, and the loops it bounds, in scalar registers
+  const int t = __builtin_amdgcn_readfirstlane(*s_tick);
   __syncthreads();  // s_tick may be rewritten by the next claim
-  return t;
+  return qs.resolve(q, t);
 }
 
-// waiting claim from `stage` on (every thread; stage uniform); advances stage past drained queues;
-// -1 when all are drained
+// waiting claim from stage `stage` on (every thread; stage uniform); advances stage past drained
+// queues; -1 when all are drained
 HL_DEV int wg_claim(const Queues& qs, int& stage, int* s_tick) {
-  for (; stage < 9; ++stage) {
-    int beg, end;
-    qs.range(stage, beg, end);
-    if (beg >= end) continue;
-    const int c = qs.resolve(stage, wg_ticket(qs, stage, s_tick));
+  for (; stage < 16; ++stage) {
+    const int c = wg_claim_queue(qs, qs.queue_at(stage), s_tick);
     if (c >= 0) return c;
   }
   return -1;
@@ -104,17 +124,19 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
     int n_dec_items, int n_pre_workers) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_tick;
-  const Queues qs{counters, n_pre_items, n_dec_items, (int)(blockIdx.x & 7),
-                  (int)blockIdx.x < n_pre_workers};
+  const Queues qs{counters, n_pre_items, n_dec_items, n_pre_workers, (int)gridDim.x,
+                  (int)(blockIdx.x & 7), (int)blockIdx.x < n_pre_workers};
   int stage = 0;
-  int cur = wg_claim(qs, stage, &s_tick);
+  int cur = qs.first_item(blockIdx.x);
+  if (cur < 0) cur = wg_claim(qs, stage, &s_tick);
   while (cur >= 0) {
     // Decode units are short: thread 0 takes the next decode ticket now and publishes it after
     // the unit. Prefill items are long and few, so their next claim waits for the item's end
     // (a ticket taken early would reserve an item that an idle worker could have run).
-    const bool ahead = stage < 9 && qs.is_dec(stage);
+    const int q = qs.queue_at(stage);
+    const bool ahead = q >= 8;
     int t = 0;
-    if (threadIdx.x == 0 && ahead) t = atomicAdd(qs.counter(stage), 1);
+    if (threadIdx.x == 0 && ahead) t = atomicAdd(qs.counter(q), 1);
     if (cur < n_pre_items) {
       hl::prefill::prefill_item<D>(pa, cur / pa.Hq, cur % pa.Hq, smem);
     } else {
@@ -126,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
     if (ahead) {
       if (threadIdx.x == 0) s_tick = t;
       __syncthreads();  // also: the item's LDS reads are done before the next item writes
-      next = qs.resolve(stage, s_tick);
+      next = qs.resolve(q, __builtin_amdgcn_readfirstlane(s_tick));
       __syncthreads();
       if (next < 0) {
         ++stage;

@@ -56,8 +56,8 @@ struct Plan {
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
   int32_t* pre_tiles;      // [n_pre_tiles][2]: (seq, first query row within the sequence)
   float* dec_part;         // [n_dec_units][Hkv][group][head_dim + 2] partial (o, m, l)
-  int32_t* counters;       // [kPlanCounters] work-queue counters of the fused attention kernel,
-                           // zeroed by the plan kernel
+  int32_t* counters;       // [kPlanCounters][kCounterStride] work-queue counters of the fused
+                           // attention kernel (one per 256-byte line), zeroed by the plan kernel
   int32_t n_dec_units, n_dec_seqs, n_pre_tiles;
   int32_t split_pages;     // pages per decode work unit
   int32_t max_pre_kv;      // longest key range of any prefill tile (host-side estimate)
@@ -102,6 +102,7 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
                        int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
 constexpr int kPlanCounters = 16;
+constexpr int kCounterStride = 64;  // int32 slots per counter: each on its own 256-byte line
 constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
 hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,
                           int32_t cols, float eps, hipStream_t st);

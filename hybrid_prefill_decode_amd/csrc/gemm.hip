@@ -329,25 +329,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
           }
         }
     } else if constexpr (EPI == kEpiRopeAppend) {
-      // stage the scaled fp32 tile in LDS, then rotate / route whole 8-element runs
+      // stage the scaled fp32 tile in LDS, then rotate / route whole 8-element runs; a 256-row
+      // tile is staged one wave row (128 rows) at a time so the stage fits in the main-loop LDS
+      constexpr int NPASS = BM > 128 ? 2 : 1, PROWS = BM / NPASS;
       float* st = reinterpret_cast<float*>(smem);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * CF::WM + i * 32 + block_row(lane, r);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            st[row * BN + wn * CF::WN + t * 32 + lc] = acc[i][t][r] * rs_sh[row];
-        }
-      __syncthreads();
       constexpr int heads = BN / HD, chunks = HD / 16;
-      for (int e = tid; e < BM * heads * chunks; e += kThreads) {
-        const int c = e % chunks, rest = e / chunks, hi = rest % heads, r = rest / heads;
-        const int gm = m0 + r;
-        if (gm >= M) continue;
-        rope_store_row<HD>(ep, gm, nt * heads + hi, blk_sh[r], pos_sh[r] & (HL_BLOCK_SIZE - 1),
-                           (pos_sh[r] & hl::kDecodeBit) != 0, st + r * BN + hi * HD, c);
+#pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
+        if (NPASS == 1 || wm == pass) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = wm * CF::WM + i * 32 + block_row(lane, r);
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+                st[(row - pass * PROWS) * BN + wn * CF::WN + t * 32 + lc] = acc[i][t][r] * rs_sh[row];
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < PROWS * heads * chunks; e += kThreads) {
+          const int c = e % chunks, rest = e / chunks, hi = rest % heads, rr = rest / heads;
+          const int r = pass * PROWS + rr, gm = m0 + r;
+          if (gm >= M) continue;
+          rope_store_row<HD>(ep, gm, nt * heads + hi, blk_sh[r], pos_sh[r] & (HL_BLOCK_SIZE - 1),
+                             (pos_sh[r] & hl::kDecodeBit) != 0, st + rr * BN + hi * HD, c);
+        }
+        if (NPASS > 1) __syncthreads();
       }
     } else {
       const hl_bf16* R = ep.residual;
@@ -412,7 +420,7 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
   constexpr bool kCanSplit = (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL);
   auto kern = gemm_bf16_nt_kernel<EPI, BM, BN, HD, false>;
   auto kern_sk = gemm_bf16_nt_kernel<EPI, BM, BN, HD, kCanSplit>;
-  const int lds = (EPI == kEpiRopeAppend) ? max(CF::MAIN_LDS, BM * BN * 4) : CF::MAIN_LDS;
+  const int lds = (EPI == kEpiRopeAppend) ? max(CF::MAIN_LDS, min(BM, 128) * BN * 4) : CF::MAIN_LDS;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -475,6 +483,15 @@ PlainChoice choose_plain(int m, int n, int k, bool has_ws) {
   return PlainChoice{false, narrow_tiles % kStreamKGrid != 0};
 }
 
+// One tile per workgroup (SwiGLU and RoPE epilogues): 256 x 256 tiles when their rounds, at 1.5x
+// the time of a 128 x 256 round (the measured ratio of k-step times), finish first.
+bool wide_one_tile(int m, int n) {
+  if (n % 256 != 0 || m <= 128) return false;
+  const long rn = ((long)((m + 127) / 128) * (n / 256) + kStreamKGrid - 1) / kStreamKGrid;
+  const long rw = ((long)((m + 255) / 256) * (n / 256) + kStreamKGrid - 1) / kStreamKGrid;
+  return 3 * rw < 2 * rn;
+}
+
 template <int EPI>
 hipError_t launch_plain(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
                         const GemmEpi& epi, float* part, size_t ws_bytes, hipStream_t st) {
@@ -501,10 +518,14 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
     case HL_EPI_RESIDUAL:
       return launch_plain<HL_EPI_RESIDUAL>(a, w, c, m, n, k, epi, part, ws_bytes, st);
     case HL_EPI_SWIGLU:
-      if (n % 256 == 0 && m > 512) return launch_tiles<HL_EPI_SWIGLU, 256, 256>(a, w, c, m, n, k, epi, nullptr, false, st);
+      if (wide_one_tile(m, n)) return launch_tiles<HL_EPI_SWIGLU, 256, 256>(a, w, c, m, n, k, epi, nullptr, false, st);
       if (n % 256 == 0) return launch_tiles<HL_EPI_SWIGLU, 128, 256>(a, w, c, m, n, k, epi, nullptr, false, st);
       return launch_tiles<HL_EPI_SWIGLU, 128, 128>(a, w, c, m, n, k, epi, nullptr, false, st);
     default:
+      if (wide_one_tile(m, n))
+        return epi.head_dim == 128
+                   ? launch_tiles<kEpiRopeAppend, 256, 256, 128>(a, w, c, m, n, k, epi, nullptr, false, st)
+                   : launch_tiles<kEpiRopeAppend, 256, 256, 64>(a, w, c, m, n, k, epi, nullptr, false, st);
       return epi.head_dim == 128
                  ? launch_tiles<kEpiRopeAppend, 128, 256, 128>(a, w, c, m, n, k, epi, nullptr, false, st)
                  : launch_tiles<kEpiRopeAppend, 128, 256, 64>(a, w, c, m, n, k, epi, nullptr, false, st);

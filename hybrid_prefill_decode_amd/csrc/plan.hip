@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ pre_tiles,
                                                         int32_t* __restrict__ counters) {
   __shared__ int buf[kThreads];
-  if (threadIdx.x < hl::kPlanCounters) counters[threadIdx.x] = 0;
+  if (threadIdx.x < hl::kPlanCounters) counters[threadIdx.x * hl::kCounterStride] = 0;
   int base_u = 0, base_d = 0, base_t = 0;
   for (int s0 = 0; s0 < num_seqs; s0 += kThreads) {
     const int s = s0 + threadIdx.x;

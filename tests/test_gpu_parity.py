@@ -149,6 +149,12 @@ def test_rms_scale_vs_oracle(rows, cols):
 QKV_CASES = {
     "cfg1": (workloads.SHAPES["tiny"], None),
     "d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 130), (70000, 1), (33, 1), (15, 17)]),
+    # ~6000 rows: 256 x 256 tiles take fewer rounds than 128 x 256 ones, so the RoPE epilogue
+    # stages each tile in two 128-row passes
+    "wide_d128": (workloads.LayerShape(1024, 8, 2, 128, 512),
+                  [(0, 2900), (777, 3000), (5000, 1), (33, 1), (15, 130)]),
+    "wide_d64": (workloads.LayerShape(1024, 16, 4, 64, 512),
+                 [(3, 3100), (0, 2800), (4095, 1), (16, 1), (250, 100)]),
 }
 
 
