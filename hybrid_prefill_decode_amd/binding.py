@@ -78,12 +78,16 @@ _SIGS = {
                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p],
                         ctypes.c_int),
+    "hl_gemm_bf16_nt_tiled": ([ctypes.c_void_p] * 5 + [ctypes.c_int32] * 7 +
+                              [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "hl_rms_scale": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p], ctypes.c_int),
     "hl_qkv_rope_append": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(Weights), ctypes.c_void_p,
                             ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_gemm_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_gemm_tile_choice": ([ctypes.c_int32] * 6 + [ctypes.POINTER(ctypes.c_int32)] * 3,
+                            ctypes.c_int),
     "hl_rope_kv_append": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
@@ -227,11 +231,38 @@ def gemm_bf16_nt(a, w, c, residual=None, epilogue: int = HL_EPI_NONE, workspace=
            "hl_gemm_bf16_nt")
 
 
+def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: bool = False, residual=None,
+                       epilogue: int = HL_EPI_NONE, workspace=None, stream=None,
+                       row_scale=None) -> None:
+    m, k = a.shape
+    n = w.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hl_gemm_bf16_nt_tiled(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), _ptr(row_scale),
+                                       m, n, k, epilogue, tile_m, tile_n, int(bool(stream_k)),
+                                       _ptr(workspace), wsb, _stream_ptr(stream)),
+           "hl_gemm_bf16_nt_tiled")
+
+
+GEMM_TILES = ((256, 256), (224, 256), (192, 256), (160, 256), (128, 256), (256, 128), (224, 128),
+              (160, 128), (128, 128))
+
+
 def gemm_workspace_bytes(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE) -> int:
     v = ctypes.c_size_t(0)
     _check(lib().hl_gemm_workspace_bytes(m, n, k, epilogue, ctypes.byref(v)),
            "hl_gemm_workspace_bytes")
     return int(v.value)
+
+
+def gemm_tile_choice(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE,
+                     with_workspace: bool = True, qkv_head_dim: int = 0):
+    """(tile_m, tile_n, stream_k) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's QKV
+    projection) uses for this shape; host-only."""
+    tm, tn, sk = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().hl_gemm_tile_choice(m, n, k, epilogue, int(bool(with_workspace)), qkv_head_dim,
+                                     ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sk)),
+           "hl_gemm_tile_choice")
+    return tm.value, tn.value, bool(sk.value)
 
 
 def rms_scale(x, gain, xg, row_scale, eps: float, stream=None) -> None:

@@ -46,11 +46,11 @@ int check_cfg(const hl_layer_cfg* c) {
   if (c->block_size != HL_BLOCK_SIZE) return HL_ERR_SHAPE;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || !(c->softmax_scale >= 0.f))
     return HL_ERR_SHAPE;
-  // the GEMMs address their operands with 32-bit element offsets
+  // the GEMMs address each operand with 32-bit byte offsets: below 2^31 elements
   const int64_t qkv_cols = (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
   const int64_t widest = std::max<int64_t>({qkv_cols, 2 * (int64_t)c->d_ff, c->hidden});
   if (widest * std::max<int64_t>({(int64_t)c->hidden, (int64_t)c->d_ff,
-                                  (int64_t)c->n_q_heads * c->head_dim}) > (int64_t)UINT32_MAX)
+                                  (int64_t)c->n_q_heads * c->head_dim}) > (int64_t)INT32_MAX)
     return HL_ERR_SHAPE;
   return HL_OK;
 }
@@ -71,11 +71,11 @@ int check_batch(const hl_batch_desc* b) {
     if ((int64_t)b->h_num_cached[s] + qlen > (int64_t)1 << 30) return HL_ERR_DESC;
   }
   if (b->h_q_start[b->num_seqs] != b->num_tokens) return HL_ERR_DESC;
-  // token rows of every GEMM operand stay within 32-bit element offsets
+  // token rows of every GEMM operand stay within 32-bit byte offsets
   const hl_layer_cfg* c = b->cfg;
   const int64_t row = std::max<int64_t>({(int64_t)c->hidden, (int64_t)c->d_ff,
                                          (int64_t)c->n_q_heads * c->head_dim});
-  if ((int64_t)b->num_tokens * row > (int64_t)UINT32_MAX) return HL_ERR_DESC;
+  if ((int64_t)b->num_tokens * row > (int64_t)INT32_MAX) return HL_ERR_DESC;
   return HL_OK;
 }
 
@@ -412,6 +412,21 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
   return HL_OK;
 }
 
+int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t with_workspace,
+                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k) {
+  if (!tile_m || !tile_n || !stream_k) return HL_ERR_NULL;
+  if (epilogue != HL_EPI_NONE && epilogue != HL_EPI_RESIDUAL && epilogue != HL_EPI_SWIGLU)
+    return HL_ERR_ARG;
+  if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
+  if (qkv_head_dim != 0 && qkv_head_dim != 64 && qkv_head_dim != 128) return HL_ERR_ARG;
+  const bool split = !qkv_head_dim && epilogue != HL_EPI_SWIGLU && with_workspace;
+  const hl::TileChoice tc = hl::choose_tiles(m, n, k, split, qkv_head_dim ? qkv_head_dim : 1);
+  *tile_m = tc.bm;
+  *tile_n = tc.bn;
+  *stream_k = tc.sk ? 1 : 0;
+  return HL_OK;
+}
+
 int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_scale,
                  int32_t rows, int32_t cols, float eps, void* stream) {
   if (!x || !gain || !xg || !row_scale) return HL_ERR_NULL;
@@ -421,19 +436,43 @@ int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_
                                 static_cast<hipStream_t>(stream)));
 }
 
-int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
-                    const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int check_gemm_args(const hl_bf16* a, const hl_bf16* w, const hl_bf16* c,
+                    const hl_bf16* residual, int32_t m, int32_t n, int32_t k, int32_t epilogue) {
   if (!a || !w || !c) return HL_ERR_NULL;
   if (epilogue != HL_EPI_NONE && epilogue != HL_EPI_RESIDUAL && epilogue != HL_EPI_SWIGLU)
     return HL_ERR_ARG;
   if (epilogue == HL_EPI_RESIDUAL && !residual) return HL_ERR_NULL;
   if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
-  if ((int64_t)m * k > (int64_t)UINT32_MAX || (int64_t)n * k > (int64_t)UINT32_MAX) return HL_ERR_ARG;
+  if ((int64_t)m * k > (int64_t)INT32_MAX || (int64_t)n * k > (int64_t)INT32_MAX) return HL_ERR_ARG;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c) || (residual && !aligned16(residual)))
     return HL_ERR_ALIGN;
+  return HL_OK;
+}
+
+int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
+                    const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_gemm_args(a, w, c, residual, m, n, k, epilogue);
+  if (rc) return rc;
   return hip_rc(hl::launch_gemm(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),
                                 workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
+                          const hl_bf16* residual, const float* row_scale, int32_t m, int32_t n,
+                          int32_t k, int32_t epilogue, int32_t tile_m, int32_t tile_n,
+                          int32_t stream_k, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const int rc = check_gemm_args(a, w, c, residual, m, n, k, epilogue);
+  if (rc) return rc;
+  if (!hl::gemm_tile_supported(tile_m, tile_n) || n % tile_n) return HL_ERR_ARG;
+  if (stream_k && (epilogue == HL_EPI_SWIGLU || !workspace ||
+                   workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
+    return HL_ERR_ARG;
+  if (m == 0) return HL_OK;
+  return hip_rc(hl::launch_gemm_tiles(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),
+                                      hl::TileChoice{tile_m, tile_n, stream_k != 0}, workspace,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,

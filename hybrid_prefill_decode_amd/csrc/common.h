@@ -109,6 +109,17 @@ hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_
 hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,
                        int32_t k, const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epi);
+struct TileChoice {
+  int bm, bn;
+  bool sk;  // stream-K (plain and residual epilogues with a workspace only)
+};
+// Tile shape and schedule of a GEMM launch (gemm.hip); col_align: N-tile widths a multiple of it.
+TileChoice choose_tiles(int m, int n, int k, bool split_ok, int col_align);
+bool gemm_tile_supported(int bm, int bn);
+// plain / residual / SwiGLU GEMM with a given tile shape (stream-K needs the workspace)
+hipError_t launch_gemm_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,
+                             int32_t k, const GemmEpi& epi, const TileChoice& tc, void* ws,
+                             hipStream_t st);
 hipError_t launch_rope_append(const hl_layer_cfg& cfg, int32_t num_seqs, int32_t num_tokens,
                               const int32_t* q_start, const int32_t* num_cached,
                               const hl_bf16* qkv, hl_bf16* q_rot, hl_bf16* kpool,

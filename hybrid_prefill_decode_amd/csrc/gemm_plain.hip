@@ -1,0 +1,12 @@
+// Token-batched GEMM kernels with the plain (no epilogue) epilogue, one instantiation per tile shape
+// (the kernels themselves are in gemm_core.h).
+#include "gemm_core.h"
+
+namespace hl {
+
+hipError_t launch_gemm_plain(const TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
+                             int m, int n, int k, const GemmEpi& epi, float* part, hipStream_t st) {
+  return launch_choice<HL_EPI_NONE>(tc, a, w, c, m, n, k, epi, part, st);
+}
+
+}  // namespace hl

@@ -1,0 +1,13 @@
+// Token-batched GEMM kernels with the residual epilogue, one instantiation per tile shape
+// (the kernels themselves are in gemm_core.h).
+#include "gemm_core.h"
+
+namespace hl {
+
+hipError_t launch_gemm_residual(const TileChoice& tc, const hl_bf16* a, const hl_bf16* w,
+                                hl_bf16* c, int m, int n, int k, const GemmEpi& epi, float* part,
+                                hipStream_t st) {
+  return launch_choice<HL_EPI_RESIDUAL>(tc, a, w, c, m, n, k, epi, part, st);
+}
+
+}  // namespace hl

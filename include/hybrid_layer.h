@@ -60,7 +60,7 @@ enum {
   HL_ERR_SHAPE = -2,     /* unsupported layer dimensions (see hl_layer_cfg) */
   HL_ERR_DESC = -3,      /* bad batch descriptor: q_len < 1, q_start not starting at 0 or not
                             increasing, q_start[S] != num_tokens, num_cached < 0, or
-                            num_tokens * max(hidden, d_ff, Hq * head_dim) >= 2^32 */
+                            num_tokens * max(hidden, d_ff, Hq * head_dim) >= 2^31 */
   HL_ERR_BLOCK = -4,     /* a sequence needs more than max_blocks_per_seq pages, or a used
                             block id lies outside [0, num_blocks) */
   HL_ERR_ALIGN = -5,     /* a device pointer is not 16-byte aligned */
@@ -74,7 +74,7 @@ typedef uint16_t hl_bf16; /* raw bfloat16 bits */
 /* Layer dimensions. Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0 and
  * n_q_heads / n_kv_heads <= 16; hidden % 128 == 0; d_ff % 64 == 0; n_q_heads * head_dim % 64 == 0;
  * (n_q_heads + 2 n_kv_heads) * head_dim % 256 == 0; every weight matrix and every
- * max(hidden, d_ff, n_q_heads * head_dim)-wide row block below 2^32 elements; block_size ==
+ * max(hidden, d_ff, n_q_heads * head_dim)-wide row block below 2^31 elements; block_size ==
  * HL_BLOCK_SIZE; rms_eps >= 0, rope_theta > 0, softmax_scale >= 0. softmax_scale == 0 means
  * 1 / sqrt(head_dim). Anything else is HL_ERR_SHAPE. */
 typedef struct {
@@ -185,8 +185,8 @@ int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_
  *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + s * A W^T
  *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
  *                   c [m, f] = silu(s * A W_gate^T) * (s * A W_up^T)
- * Requirements: k % 64 == 0, n % 128 == 0, m >= 0, m * k and n * k at most 2^32 - 1 (operands
- * are addressed with 32-bit element offsets; HL_ERR_ARG otherwise). `workspace` (device, may be NULL): when it
+ * Requirements: k % 64 == 0, n % 128 == 0, m >= 0, m * k and n * k at most 2^31 - 1 (operands
+ * are addressed with 32-bit byte offsets; HL_ERR_ARG otherwise). `workspace` (device, may be NULL): when it
  * holds hl_gemm_workspace_bytes() bytes, shapes with fewer output tiles than compute units run a
  * stream-K schedule (partial tiles in the workspace, summed by a fix-up pass); without it they run
  * one tile per workgroup. Results agree to fp32 summation order either way. */
@@ -195,6 +195,29 @@ int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf1
                     const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
                     void* workspace, size_t workspace_bytes, void* stream);
 int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, size_t* bytes);
+
+/* hl_gemm_bf16_nt with the tile shape and schedule given by the caller instead of chosen (for
+ * tuning and tests). tile_m x tile_n must be one of 256x256, 224x256, 192x256, 160x256, 128x256,
+ * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0; stream_k != 0 runs a stream-K schedule
+ * (HL_EPI_NONE / HL_EPI_RESIDUAL only, and `workspace` must hold hl_gemm_workspace_bytes()).
+ * Results agree with hl_gemm_bf16_nt to fp32 summation order. Errors as hl_gemm_bf16_nt, and
+ * HL_ERR_ARG for an unsupported tile or schedule. */
+int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
+                          const hl_bf16* residual, const float* row_scale, int32_t m, int32_t n,
+                          int32_t k, int32_t epilogue, int32_t tile_m, int32_t tile_n,
+                          int32_t stream_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The tile shape (*tile_m x *tile_n outputs per workgroup) and schedule (*stream_k: 1 for a
+ * stream-K run with a fix-up pass, 0 for one tile per workgroup) that hl_gemm_bf16_nt uses for
+ * these arguments (with_workspace != 0: a stream-K workspace is passed). qkv_head_dim 64 or 128
+ * asks instead for the QKV projection of the layer step (RoPE + KV-append epilogue: one tile per
+ * workgroup, whole heads per tile); 0 otherwise. Host-only: no device work, no GPU needed. The
+ * choice minimises a cost model of the launch (rounds of tiles over the compute units, or the
+ * stream-K run length plus its fix-up traffic); the token count of a hybrid batch is arbitrary, so
+ * fixed tiles would hit the tile-quantisation cliff that the chunked-prefill page describes.
+ * Errors: HL_ERR_NULL, HL_ERR_ARG (the same size rules as hl_gemm_bf16_nt). */
+int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t with_workspace,
+                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k);
 
 /* First half of the layer up to attention, as the step runs it: RMSNorm of batch->x (gain
  * w->attn_norm), the QKV projection (w->w_qkv) and, in the same kernel's epilogue, the rotary

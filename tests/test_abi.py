@@ -6,6 +6,7 @@ on to launch a kernel on this GPU-less machine it would have come back as HL_ERR
 each expected code also shows that nothing was launched.
 """
 import ctypes
+import math
 import os
 import re
 
@@ -184,3 +185,47 @@ def test_gemm_and_rmsnorm_argument_checks():
     assert L.hl_rmsnorm(None, p, p, 4, 16, 1e-6, None) == B.HL_ERR_NULL
     assert L.hl_rms_scale(p, p, p, None, 4, 16, 1e-6, None) == B.HL_ERR_NULL
     assert L.hl_rms_scale(p, p, p, p, 4, 12, 1e-6, None) == B.HL_ERR_ARG
+
+
+def test_gemm_tiled_argument_checks():
+    t = torch.zeros(64 * 128, dtype=torch.bfloat16)
+    p = t.data_ptr()
+    g = B.lib().hl_gemm_bf16_nt_tiled
+    assert g(p, p, p, None, None, 8, 256, 64, 0, 96, 256, 0, None, 0, None) == B.HL_ERR_ARG  # tile
+    assert g(p, p, p, None, None, 8, 384, 64, 0, 128, 256, 0, None, 0, None) == B.HL_ERR_ARG  # n % tile_n
+    assert g(p, p, p, None, None, 8, 256, 64, 0, 128, 256, 1, None, 0, None) == B.HL_ERR_ARG  # no workspace
+    assert g(p, p, p, None, None, 8, 256, 64, 2, 128, 256, 1, p, 1 << 30, None) == B.HL_ERR_ARG  # SwiGLU split
+    assert g(p, p, p, None, None, 8, 256, 64, 0, 128, 256, 1, p, 1024, None) == B.HL_ERR_ARG  # small workspace
+    assert g(p, p, p, None, None, 8, 256, 60, 0, 128, 256, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
+    assert g(p, p, p, None, None, 0, 256, 64, 0, 128, 256, 0, None, 0, None) == B.HL_OK  # m == 0: nothing
+
+
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
+def test_gemm_tile_choice_is_valid(epi):
+    """The chooser returns a compiled tile shape that divides N, splits only plain / residual
+    GEMMs that have a workspace, and keeps whole heads per tile for the QKV projection."""
+    rng = np.random.default_rng(epi)
+    tiles = set(B.GEMM_TILES)
+    for _ in range(300):
+        m = int(rng.integers(0, 9000))
+        n = 128 * int(rng.integers(1, 400))
+        k = 64 * int(rng.integers(1, 500))
+        ws = bool(rng.integers(0, 2))
+        hd = int(rng.choice([0, 64, 128])) if epi == B.HL_EPI_NONE else 0
+        bm, bn, sk = B.gemm_tile_choice(m, n, k, epi, ws, hd)
+        assert (bm, bn) in tiles and n % bn == 0, (m, n, k, bm, bn)
+        if sk:
+            assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)
+        if hd:
+            assert bn % hd == 0
+    with pytest.raises(RuntimeError):
+        B.gemm_tile_choice(8, 100, 64, epi)
+
+
+def test_gemm_tile_choice_fits_the_batch():
+    """The tile-quantisation cliff: a 1040-token batch (1024-token chunk + 16 decodes) gets tiles
+    whose row count wastes less than a 256-row tile would (5 x 256 = 1280 rows for 1040)."""
+    for n, k, epi in [(4096, 4096, B.HL_EPI_RESIDUAL), (24576, 4096, B.HL_EPI_SWIGLU),
+                      (4096, 12288, B.HL_EPI_RESIDUAL)]:
+        bm, bn, sk = B.gemm_tile_choice(1040, n, k, epi)
+        assert sk or bm * math.ceil(1040 / bm) < 1280, (n, k, bm, bn, sk)

@@ -84,6 +84,43 @@ def test_gemm_streamk_vs_oracle(m, n, k, epi):
     assert_close(f64(c), ref, "gemm stream-K")
 
 
+@pytest.mark.parametrize("tile", B.GEMM_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("epi,stream_k", [(B.HL_EPI_NONE, False), (B.HL_EPI_RESIDUAL, False),
+                                          (B.HL_EPI_SWIGLU, False), (B.HL_EPI_NONE, True),
+                                          (B.HL_EPI_RESIDUAL, True)],
+                         ids=["plain", "residual", "swiglu", "plain-sk", "residual-sk"])
+def test_gemm_every_tile_shape(tile, epi, stream_k):
+    """Every compiled tile shape, one tile per workgroup and stream-K, through the explicit-tile
+    entry point. 300 rows leave a ragged last M tile for every BM; the stream-K shape (2100 x 8192
+    x 192: 3 k-steps per tile, runs of 4 or more) mixes tiles split across runs (fix-up) with tiles
+    whole inside one run (finished in the main kernel), and uses a row scale."""
+    bm, bn = tile
+    shapes = [(300, 512, 320)] + ([(2100, 8192, 192)] if stream_k else [])
+    for m, n, k in shapes:
+        say(f"gemm tile {bm}x{bn} stream_k={stream_k} epi={epi} m={m} n={n} k={k}")
+        a = _randn((m, k), 41 + m + bm)
+        w = _randn((n, k), 42 + n + bn, 0.05)
+        out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
+        res = _randn((m, out_n), 43 + k) if epi == B.HL_EPI_RESIDUAL else None
+        rs = (0.5 + torch.rand(m, generator=torch.Generator(device=DEV).manual_seed(m),
+                               device=DEV)) if stream_k else None
+        ws = torch.empty(B.gemm_workspace_bytes(m, n, k, epi), dtype=torch.uint8, device=DEV) \
+            if stream_k else None
+        c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.gemm_bf16_nt_tiled(a, w, c, bm, bn, stream_k, res, epi, workspace=ws, row_scale=rs)
+        torch.cuda.synchronize()
+        A, W = f64(a), f64(w)
+        if rs is not None:
+            A = A * f64(rs)[:, None]
+        if epi == B.HL_EPI_SWIGLU:
+            ref = OL.swiglu(A, W, n // 2)
+        else:
+            ref = OL.linear(A, W)
+            if epi == B.HL_EPI_RESIDUAL:
+                ref = ref + f64(res)
+        assert_close(f64(c), ref, f"gemm {bm}x{bn} sk={stream_k}")
+
+
 def _edge_sample(size, tile, count, seed):
     """Indices that include both edges of every tile plus the ragged end, and random fill."""
     idx = {0, size - 1}
@@ -156,6 +193,22 @@ QKV_CASES = {
     "wide_d64": (workloads.LayerShape(1024, 16, 4, 64, 512),
                  [(3, 3100), (0, 2800), (4095, 1), (16, 1), (250, 100)]),
 }
+# One case per RoPE-epilogue tile shape: the token count decides the tile the QKV projection gets
+# (checked against the library's own choice below), so each count below lands on another shape.
+_QKV_TILE_ROWS = {(160, 128): 2716, (224, 128): 3382, (256, 128): 4714, (160, 256): 5380,
+                  (192, 256): 6749, (224, 256): 8081, (256, 256): 9413, (128, 256): 10782}
+
+
+def _qkv_rows_case(total):
+    return [(0, total - 200), (777, 130), (5000, 1), (33, 1), (15, 66), (4096, 1), (64, 1)]
+
+
+for _t, _rows in _QKV_TILE_ROWS.items():
+    QKV_CASES[f"tile{_t[0]}x{_t[1]}_d128"] = (workloads.LayerShape(1024, 8, 2, 128, 512),
+                                             _qkv_rows_case(_rows))
+for _t in [(160, 128), (224, 256), (256, 128)]:
+    QKV_CASES[f"tile{_t[0]}x{_t[1]}_d64"] = (workloads.LayerShape(1024, 16, 4, 64, 512),
+                                            _qkv_rows_case(_QKV_TILE_ROWS[_t]))
 
 
 @pytest.mark.parametrize("case", sorted(QKV_CASES))
@@ -164,6 +217,12 @@ def test_qkv_rope_append_vs_oracle(case):
     spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 3)
     say(f"qkv+rope+append {case}: {spec.seqs}")
     s = spec.shape
+    if case.startswith("tile"):
+        want = tuple(int(v) for v in case[4:].split("_")[0].split("x"))
+        qkv_cols = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
+        got = B.gemm_tile_choice(spec.num_tokens, qkv_cols, s.hidden, B.HL_EPI_NONE, True,
+                                 s.head_dim)
+        assert got[:2] == want, (case, got)
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
