@@ -280,7 +280,7 @@ def main():
 
     gu_flops = cnt["gemm_flops"]["gate_up"]
     gu_tflops = gu_flops / (phase_us["gemm_gate_up"] * 1e-6) / 1e12
-    src_hash = kernel_source_hash(["gemm.hip", "common.h"])
+    src_hash = kernel_source_hash(["gemm.hip", "gemm_core.h", "gemm_swiglu.hip", "common.h"])
     traffic = read_traffic(f"gemm_gate_up_{name}_pmc.txt", src_hash)
 
     result = {
