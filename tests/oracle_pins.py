@@ -20,6 +20,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
+import oracle.kv_transfer as OKV
 import oracle.layer as OL
 import workloads
 
@@ -332,11 +333,87 @@ def check_block_permutation_addresses():
         assert len(set(map(tuple, a[:, 2:].tolist()))) == a.shape[0]
 
 
+# --------------------------------------------------------------------------- KV transfer
+
+def _code(b, h, s, d):
+    """An exact fp64 label of pool element (block, head, slot, dim)."""
+    return ((np.asarray(b) * 64.0 + h) * 16.0 + s) * 256.0 + d
+
+
+def _coded_pools(nblk, hkv, dim):
+    b, h, s, d = np.meshgrid(np.arange(nblk), np.arange(hkv), np.arange(16), np.arange(dim),
+                             indexing="ij")
+    k = _code(b, h, s, d)                       # K[b][h][s][d]
+    v = np.transpose(_code(b, h, s, d), (0, 1, 3, 2)).copy()  # V[b][h][d][s] holds code(b,h,s,d)
+    return k, v
+
+
+def check_kv_export_closed_form():
+    """Every exported element is the label of the slot the table names for its position."""
+    rng = np.random.default_rng(3)
+    nblk, hkv, dim, L = 23, 3, 8, 4
+    k, v = _coded_pools(nblk, hkv, dim)
+    table = rng.permutation(nblk)[:9]
+    for start, count, layer in [(0, 16, 0), (5, 100, 2), (37, 1, 3), (31, 2, 1), (0, 0, 0)]:
+        out = np.full((L, 2, count, hkv, dim), np.nan)
+        OKV.export_layer(k, v, table, start, count, layer, out)
+        p = start + np.arange(count)
+        want = _code(table[p // 16][:, None, None], np.arange(hkv)[None, :, None],
+                     (p % 16)[:, None, None], np.arange(dim)[None, None, :])
+        assert np.array_equal(out[layer, 0], want) and np.array_equal(out[layer, 1], want)
+        others = [l for l in range(L) if l != layer]
+        assert np.isnan(out[others]).all(), "export wrote outside its layer"
+
+
+def check_kv_import_closed_form():
+    """Import writes exactly the slots of the span, each from the element of its position, and
+    leaves every other slot alone."""
+    rng = np.random.default_rng(4)
+    nblk, hkv, dim, L = 17, 2, 8, 3
+    table = rng.permutation(nblk)[:7]
+    start, count, layer = 9, 90, 1
+    p = start + np.arange(count)
+    src = np.full((L, 2, count, hkv, dim), np.nan)
+    src[layer, 0] = (p[:, None, None] * 10.0 + np.arange(hkv)[None, :, None]) * 100.0 + np.arange(dim)
+    src[layer, 1] = -src[layer, 0]
+    k = np.full((nblk, hkv, 16, dim), 7.5)
+    v = np.full((nblk, hkv, dim, 16), 7.5)
+    OKV.import_layer(src, table, start, count, layer, k, v)
+    inv = {int(b): j for j, b in enumerate(table)}
+    for b in range(nblk):
+        for s in range(16):
+            pos = inv[b] * 16 + s if b in inv else -1
+            kk, vv = k[b, :, s, :], v[b, :, :, s]
+            if start <= pos < start + count:
+                want = (pos * 10.0 + np.arange(hkv)[:, None]) * 100.0 + np.arange(dim)[None, :]
+                assert np.array_equal(kk, want) and np.array_equal(vv, -want), (b, s)
+            else:
+                assert (kk == 7.5).all() and (vv == 7.5).all(), (b, s)
+
+
+def check_kv_round_trip_across_tables():
+    """Exporting, importing into another pool under another table and exporting again gives the
+    same transfer tensor (what a decode instance receives is what the prefill instance held)."""
+    rng = np.random.default_rng(5)
+    hkv, dim, L = 2, 16, 2
+    k1, v1 = rng.standard_normal((12, hkv, 16, dim)), rng.standard_normal((12, hkv, dim, 16))
+    t1, t2 = rng.permutation(12)[:8], rng.permutation(30)[:8]
+    start, count = 3, 120
+    a = np.zeros((L, 2, count, hkv, dim))
+    OKV.export_layer(k1, v1, t1, start, count, 1, a)
+    k2, v2 = np.zeros((30, hkv, 16, dim)), np.zeros((30, hkv, dim, 16))
+    OKV.import_layer(a, t2, start, count, 1, k2, v2)
+    b = np.zeros_like(a)
+    OKV.export_layer(k2, v2, t2, start, count, 1, b)
+    assert np.array_equal(a, b)
+
+
 ALL_CHECKS = [
     check_attention_bruteforce, check_attention_sdpa_library, check_attention_closed_forms,
     check_gqa_group_mapping, check_rope_hand_values, check_rope_complex_form_and_invariance,
     check_rmsnorm, check_silu_swiglu, check_slot_addresses, check_layer_vs_torch_library,
     check_batch_equals_alone, check_chunked_equals_one_shot,
     check_decode_equals_last_prefill_row, check_sampled_rows_match_full,
-    check_block_permutation_addresses,
+    check_block_permutation_addresses, check_kv_export_closed_form, check_kv_import_closed_form,
+    check_kv_round_trip_across_tables,
 ]

@@ -9,6 +9,7 @@ import textwrap
 
 import pytest
 
+import oracle.kv_transfer as OKV
 import oracle.layer as OL
 from tests import oracle_pins
 
@@ -35,15 +36,25 @@ MUTANTS = [
     ("kv_slot_addresses", "positions % block_size", "positions % (block_size + 1)"),
     ("layer_step", "pos = c + np.arange(n)", "pos = np.arange(n)"),
 ]
+# planted mistakes in the KV-transfer reference
+KV_MUTANTS = [
+    ("export_layer", "out[layer, 1, i] = vpool[b, :, :, s]", "out[layer, 1, i] = vpool[b, :, s, :]"),
+    ("export_layer", "p = start + i", "p = i"),
+    ("export_layer", "out[layer, 0, i] = kpool[b, :, s, :]", "out[0, 0, i] = kpool[b, :, s, :]"),
+    ("export_layer", "b, s = int(table_row[p // BLOCK]), p % BLOCK", "b, s = p // BLOCK, p % BLOCK"),
+    ("import_layer", "vpool[b, :, :, s] = src[layer, 1, i]", "vpool[b, :, :, s] = src[layer, 0, i]"),
+    ("import_layer", "p = start + i", "p = start + i + 1"),
+    ("import_layer", "b, s = int(table_row[p // BLOCK]), p % BLOCK", "b, s = int(table_row[p // BLOCK]), (p + 1) % BLOCK"),
+]
 
 
-def _mutant(fn_name, old, new):
-    src = textwrap.dedent(inspect.getsource(getattr(OL, fn_name)))
-    fn = getattr(OL, fn_name)
+def _mutant(fn_name, old, new, mod=OL):
+    src = textwrap.dedent(inspect.getsource(getattr(mod, fn_name)))
+    fn = getattr(mod, fn_name)
     if fn.__doc__:  # edit code, never the docstring
         src = src.replace(fn.__doc__, "", 1)
     assert old in src, f"mutation site not found in {fn_name}: {old!r}"
-    ns = dict(vars(OL))
+    ns = dict(vars(mod))
     exec(compile(src.replace(old, new, 1), f"<mutant {fn_name}>", "exec"), ns)
     return ns[fn_name]
 
@@ -56,5 +67,18 @@ def test_pins_catch_planted_mistake(monkeypatch, fn_name, old, new):
         try:
             check()
         except Exception:  # an assertion, or NaN/shape fallout of the mistake
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
+
+
+@pytest.mark.parametrize("fn_name,old,new", KV_MUTANTS,
+                         ids=[f"{m[0]}:{m[1][:24]}" for m in KV_MUTANTS])
+def test_pins_catch_planted_kv_transfer_mistake(monkeypatch, fn_name, old, new):
+    monkeypatch.setattr(OKV, fn_name, _mutant(fn_name, old, new, OKV))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception:
             caught.append(check.__name__)
     assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
