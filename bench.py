@@ -124,7 +124,8 @@ def main():
     ap.add_argument("--only-phase", default=None,
                     help="profiling aid: after set-up run only this phase --phase-reps times "
                          "(qkv_rope_append, prefill_attention, decode_attention, gemm_o, "
-                         "rms_scale_mlp, gemm_gate_up, gemm_down) and print its timing")
+                         "rms_scale_mlp, gemm_gate_up, gemm_down, kv_export, kv_import) and "
+                         "print its timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="profiling aid: run a plain elementwise copy (read N MiB, write N MiB) "
                          "--phase-reps times, to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -248,6 +249,20 @@ def main():
         ("gemm_down", lambda: B.gemm_bf16_nt(mlp, w["w_down"], out, h2, B.HL_EPI_RESIDUAL,
                                              workspace=gws, stream=stream)),
     ]
+    # KV hand-off of the longest request (not part of the step): its whole span of this layer
+    # out to the [L, 2, T, Hkv, d] transfer layout, and back in under another table and pool
+    sl = max(range(len(spec.seqs)), key=lambda i: spec.seqs[i][0] + spec.seqs[i][1])
+    span_len = spec.seqs[sl][0] + spec.seqs[sl][1]
+    npg = (span_len + 15) // 16
+    row_a = np.ascontiguousarray(table[sl][:npg], dtype=np.int32)
+    row_b = np.random.default_rng(7).permutation(npg).astype(np.int32)
+    ta, tb = torch.from_numpy(row_a).to(dev), torch.from_numpy(row_b).to(dev)
+    xfer = torch.empty(1, 2, span_len, s.n_kv_heads, s.head_dim, dtype=torch.bfloat16, device=dev)
+    kp2, vp2 = kvcache.alloc_pools(npg, s.n_kv_heads, s.head_dim, dev, fill=0.0)
+    phases += [
+        ("kv_export", lambda: B.kv_export(kp, vp, ta, row_a, 0, span_len, 0, xfer, stream)),
+        ("kv_import", lambda: B.kv_import(xfer, tb, row_b, 0, span_len, 0, kp2, vp2, stream)),
+    ]
     if args.only_phase is not None:
         phases = [p for p in phases if p[0] == args.only_phase]
         if not phases:
@@ -313,6 +328,12 @@ def main():
         "decode_attn_hbm_gbps": None if dec_gbps is None else round(dec_gbps, 1),
         "decode_attn_hbm_frac": None if dec_gbps is None else round(dec_gbps / PEAK_HBM_GBPS, 4),
         "prefill_attn_tflops": None if pre_tflops is None else round(pre_tflops, 1),
+        "kv_transfer": {
+            "tokens": span_len, "bytes_per_layer_slice": 2 * xfer.numel(),
+            "export_gbps": round(2 * 2 * xfer.numel() / (phase_us["kv_export"] * 1e-6) / 1e9, 1),
+            "import_gbps": round(2 * 2 * xfer.numel() / (phase_us["kv_import"] * 1e-6) / 1e9, 1),
+            "note": "one layer slice of the longest request; GB/s counts bytes read + written",
+        },
         "wall_s_timed": round(t_wall, 3),
         "cpu_baseline": None,
     }

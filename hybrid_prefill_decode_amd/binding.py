@@ -56,6 +56,14 @@ class BlockTable(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32)]
 
 
+class KvSpan(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("layer", ctypes.c_int32),
+                ("start", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("table", ctypes.c_void_p), ("h_table", _c_i32p), ("table_len", ctypes.c_int32),
+                ("stream", ctypes.c_void_p)]
+
+
 class HLError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -86,6 +94,10 @@ _SIGS = {
                             ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_gemm_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_kv_export": ([ctypes.POINTER(KvSpan), ctypes.POINTER(KvPages), ctypes.c_void_p],
+                     ctypes.c_int),
+    "hl_kv_import": ([ctypes.POINTER(KvSpan), ctypes.c_void_p, ctypes.POINTER(KvPages)],
+                     ctypes.c_int),
     "hl_gemm_tile_choice": ([ctypes.c_int32] * 6 + [ctypes.POINTER(ctypes.c_int32)] * 3,
                             ctypes.c_int),
     "hl_rope_kv_append": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
@@ -186,6 +198,35 @@ def _desc(cfg: LayerCfg, b: Batch, x=None, workspace=None, stream=None, taps=Non
 
 def _pages(k_pool, v_pool) -> KvPages:
     return KvPages(_ptr(k_pool), _ptr(v_pool), int(k_pool.shape[0]))
+
+
+def _span(table_row, h_table_row, n_kv_heads: int, head_dim: int, num_layers: int, layer: int,
+          start: int, count: int, stream) -> KvSpan:
+    h = np.ascontiguousarray(h_table_row, dtype=np.int32)
+    return KvSpan(n_kv_heads, head_dim, num_layers, layer, start, count, _ptr(table_row),
+                  h.ctypes.data_as(_c_i32p), int(h.shape[0]), _stream_ptr(stream)), h
+
+
+def kv_export(k_pool, v_pool, table_row, h_table_row, start: int, count: int, layer: int,
+              dst, stream=None) -> None:
+    """dst [L, 2, count, Hkv, d] (device bf16) <- the span's K/V of this layer's pools; only
+    dst[layer] is written. table_row: the request's block-table row (device int32), with its host
+    mirror h_table_row."""
+    L, two, T, hkv, d = dst.shape
+    assert two == 2 and T == count
+    sp, keep = _span(table_row, h_table_row, hkv, d, L, layer, start, count, stream)
+    kv = _pages(k_pool, v_pool)
+    _check(lib().hl_kv_export(ctypes.byref(sp), ctypes.byref(kv), _ptr(dst)), "hl_kv_export")
+
+
+def kv_import(src, table_row, h_table_row, start: int, count: int, layer: int, k_pool, v_pool,
+              stream=None) -> None:
+    """The span's slots of this layer's pools <- src[layer] ([L, 2, count, Hkv, d] device bf16)."""
+    L, two, T, hkv, d = src.shape
+    assert two == 2 and T == count
+    sp, keep = _span(table_row, h_table_row, hkv, d, L, layer, start, count, stream)
+    kv = _pages(k_pool, v_pool)
+    _check(lib().hl_kv_import(ctypes.byref(sp), _ptr(src), ctypes.byref(kv)), "hl_kv_import")
 
 
 def _table(b: Batch) -> BlockTable:

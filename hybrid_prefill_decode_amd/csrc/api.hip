@@ -475,6 +475,34 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                                       static_cast<hipStream_t>(stream)));
 }
 
+// Host checks of a KV span (nothing is launched on failure).
+int check_span(const hl_kv_span* s, const hl_kv_pages* kv, const void* buf) {
+  if (!s || !kv || !buf) return HL_ERR_NULL;
+  if (s->n_kv_heads <= 0 || (s->head_dim != 64 && s->head_dim != 128)) return HL_ERR_ARG;
+  if (s->num_layers <= 0 || s->layer < 0 || s->layer >= s->num_layers) return HL_ERR_ARG;
+  if (s->start < 0 || s->count < 0 || s->table_len < 0) return HL_ERR_ARG;
+  if ((int64_t)s->start + s->count > (int64_t)HL_BLOCK_SIZE * s->table_len) return HL_ERR_ARG;
+  if (s->count == 0) return HL_OK;
+  if (!s->table || !s->h_table || !kv->k || !kv->v) return HL_ERR_NULL;
+  if (!aligned16(kv->k) || !aligned16(kv->v) || !aligned16(buf)) return HL_ERR_ALIGN;
+  const int first = s->start / HL_BLOCK_SIZE, last = (s->start + s->count - 1) / HL_BLOCK_SIZE;
+  for (int j = first; j <= last; ++j)
+    if (s->h_table[j] < 0 || s->h_table[j] >= kv->num_blocks) return HL_ERR_BLOCK;
+  return HL_OK;
+}
+
+int hl_kv_export(const hl_kv_span* span, const hl_kv_pages* kv, hl_bf16* dst) {
+  const int rc = check_span(span, kv, dst);
+  if (rc || span->count == 0) return rc;
+  return hip_rc(hl::launch_kv_span(*span, *kv, dst, true));
+}
+
+int hl_kv_import(const hl_kv_span* span, const hl_bf16* src, hl_kv_pages* kv) {
+  const int rc = check_span(span, kv, src);
+  if (rc || span->count == 0) return rc;
+  return hip_rc(hl::launch_kv_span(*span, *kv, const_cast<hl_bf16*>(src), false));
+}
+
 int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,
                       hl_kv_pages* kv, const hl_block_table* bt) {
   HostPlan hp;

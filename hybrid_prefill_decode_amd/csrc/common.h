@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "hybrid_layer.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -149,5 +151,8 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
                                    hl_bf16* attn_out, hipStream_t st);
 
 constexpr int kPrefillQTile = 128;  // query rows per prefill work tile
+
+// One request's K/V span to (exporting) or from the [L][2][T][Hkv][d] transfer layout.
+hipError_t launch_kv_span(const hl_kv_span& s, const hl_kv_pages& kv, hl_bf16* buf, bool exporting);
 
 }  // namespace hl

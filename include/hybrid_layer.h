@@ -165,6 +165,42 @@ const char* hl_strerror(int code);
 /* HL_VERSION of the library. */
 int hl_version(void);
 
+/* ---- KV transfer between instances ------------------------------------------------------ */
+
+/* One request's token span [start, start + count) of one layer, for the KV hand-off between a
+ * prefill instance and a decode instance. The transfer tensor of a request is
+ * [num_layers][2][count][n_kv_heads][head_dim] bf16 (layer, K then V, token, KV head, dim), the
+ * shape "7.8 Disaggregated Prefill/Decode & Chunked Prefill" gives for the KV cache a prefill
+ * worker transmits ("Lifecycle of a Request", step 3); it moves one layer slice at a time, each as
+ * soon as that layer has written its rows ("Layer-Wise Pipelining"). `table` is the request's
+ * block-table row (device) with its host mirror `h_table` (validation only), `table_len` entries.
+ * head_dim in {64, 128}; 0 <= layer < num_layers; start >= 0, count >= 0, start + count <=
+ * 16 * table_len. */
+typedef struct {
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t num_layers;
+  int32_t layer;
+  int32_t start;
+  int32_t count;
+  const int32_t* table;   /* device [table_len] */
+  const int32_t* h_table; /* host   [table_len] */
+  int32_t table_len;
+  void* stream;           /* hipStream_t; NULL = the null stream */
+} hl_kv_span;
+
+/* Export: dst[layer][0][i] = K of position start + i, dst[layer][1][i] = V of it, for every KV
+ * head (dst is the whole [num_layers][2][count][n_kv_heads][head_dim] buffer, device; only the
+ * layer's slice is written). Bit-exact copy; the pool is only read. Errors: HL_ERR_NULL,
+ * HL_ERR_ARG (span fields), HL_ERR_BLOCK (a page of the span outside [0, num_blocks)),
+ * HL_ERR_ALIGN (pointers not 16-byte aligned), HL_ERR_HIP. Asynchronous on span->stream. */
+int hl_kv_export(const hl_kv_span* span, const hl_kv_pages* kv, hl_bf16* dst);
+
+/* Import: the inverse scatter of src's layer slice into the slots of positions start .. start +
+ * count - 1 under this span's table (which may differ from the exporter's). Every other byte of
+ * both pools keeps its value. Errors as hl_kv_export. */
+int hl_kv_import(const hl_kv_span* span, const hl_bf16* src, hl_kv_pages* kv);
+
 /* ---- the phases the step is composed of (same conventions; used by tests and benchmarks) --- */
 
 /* y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain, rows x cols, all device bf16.

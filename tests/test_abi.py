@@ -229,3 +229,30 @@ def test_gemm_tile_choice_fits_the_batch():
                       (4096, 12288, B.HL_EPI_RESIDUAL)]:
         bm, bn, sk = B.gemm_tile_choice(1040, n, k, epi)
         assert sk or bm * math.ceil(1040 / bm) < 1280, (n, k, bm, bn, sk)
+
+
+def test_kv_span_argument_checks():
+    t = torch.zeros(4096, dtype=torch.bfloat16)
+    p = t.data_ptr()
+    row = np.array([3, 1, 7], dtype=np.int32)
+    pages = B.KvPages(p, p, 8)
+
+    def span(hkv=2, d=128, L=2, layer=1, start=0, count=20, table=row):
+        return B.KvSpan(hkv, d, L, layer, start, count, p, table.ctypes.data_as(B._c_i32p),
+                        int(table.shape[0]), None)
+    L = B.lib()
+    e = lambda s, buf=p: L.hl_kv_export(ctypes.byref(s), ctypes.byref(pages), buf)
+    i = lambda s, buf=p: L.hl_kv_import(ctypes.byref(s), buf, ctypes.byref(pages))
+    for f in (e, i):
+        assert f(span(d=96)) == B.HL_ERR_ARG
+        assert f(span(hkv=0)) == B.HL_ERR_ARG
+        assert f(span(layer=2)) == B.HL_ERR_ARG
+        assert f(span(start=40, count=9)) == B.HL_ERR_ARG        # past 16 * table_len
+        assert f(span(start=-1)) == B.HL_ERR_ARG
+        assert f(span(table=np.array([3, 9, 7], dtype=np.int32), start=10, count=20)) == B.HL_ERR_BLOCK
+        assert f(span(table=np.array([3, -1, 7], dtype=np.int32), start=10, count=20)) == B.HL_ERR_BLOCK
+        assert f(span(), p + 8) == B.HL_ERR_ALIGN
+        assert f(span(), None) == B.HL_ERR_NULL
+        assert f(span(count=0)) == B.HL_OK                       # empty span: nothing launched
+        # a span whose pages are all valid is accepted up to the launch (which fails here: no GPU)
+        assert f(span(table=np.array([3, 9, 7], dtype=np.int32), start=0, count=16)) == B.HL_ERR_HIP
