@@ -21,6 +21,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle.kv_transfer as OKV
+import oracle.model as OM
 import oracle.layer as OL
 import workloads
 
@@ -408,6 +409,68 @@ def check_kv_round_trip_across_tables():
     assert np.array_equal(a, b)
 
 
+# --------------------------------------------------------------------------- model step
+
+def _tiny_model(layers, zero_residual_branches):
+    shape = workloads.SHAPES["tiny"]
+    spec = workloads.custom_spec(shape, [(5, 9), (0, 1), (17, 1), (0, 4)], 11)
+    table, _ = workloads.block_table(spec)
+    t = workloads.model_tensors(spec, 64)
+    Ws, caches = [], []
+    for l in range(layers):
+        ls = workloads.layer_spec(spec, l)
+        w = {k: v.double().numpy() for k, v in workloads.weights(ls).items()}
+        if zero_residual_branches:
+            w["w_o"][:] = 0.0
+            w["w_down"][:] = 0.0
+        Ws.append(w)
+        caches.append([tuple(a.double().numpy() for a in workloads.cached_kv(ls, si))
+                       for si in range(spec.num_seqs)])
+    return shape, spec, table, t, Ws, caches
+
+
+def check_model_head_library_and_identity_stack():
+    """With the attention and MLP outputs projected to zero, every layer is the identity on the
+    residual stream, so a stack of any depth gives the logits of the embedded tokens themselves;
+    those are checked against torch's rms_norm and linear on the last row of each sequence."""
+    for layers in (0, 2):
+        shape, spec, table, t, Ws, caches = _tiny_model(layers, True)
+        emb, head = t["embed"].double().numpy(), t["lm_head"].double().numpy()
+        gain = t["final_norm"].double().numpy()
+        r = OM.model_step(shape, t["tokens"], emb, Ws, gain, head, spec.seqs, caches, table)
+        last = np.cumsum([n for _, n in spec.seqs]) - 1
+        xt = torch.from_numpy(emb[t["tokens"][last]])
+        want = F.linear(F.rms_norm(xt, (shape.hidden,), torch.from_numpy(gain), shape.rms_eps),
+                        torch.from_numpy(head)).numpy()
+        assert _rel(r["logits"], want) < TOL
+        assert np.array_equal(r["hidden"], emb[t["tokens"]])
+
+
+def check_model_stack_is_layer_by_layer():
+    """A two-layer stack equals the first layer's output fed to the second (rows of each request
+    see only that request), and its logits rows follow the sequences' last rows."""
+    shape, spec, table, t, Ws, caches = _tiny_model(2, False)
+    emb, head = t["embed"].double().numpy(), t["lm_head"].double().numpy()
+    gain = t["final_norm"].double().numpy()
+    r = OM.model_step(shape, t["tokens"], emb, Ws, gain, head, spec.seqs, caches, table)
+    x = emb[t["tokens"]]
+    row = 0
+    for s, (c, n) in enumerate(spec.seqs):
+        h = x[row:row + n]
+        for l in range(2):
+            h = OL.sequence_step(shape, h, Ws[l], c, *caches[l][s])["out"]
+        assert _rel(r["hidden"][row:row + n], h) < TOL
+        want = F.linear(F.rms_norm(torch.from_numpy(h[-1:]), (shape.hidden,),
+                                   torch.from_numpy(gain), shape.rms_eps), torch.from_numpy(head))
+        assert _rel(r["logits"][s:s + 1], want.numpy()) < TOL
+        row += n
+
+
+def check_greedy_hand_values():
+    assert list(OM.greedy(np.array([[1.0, 3.0, 3.0, 2.0], [-5.0, -7.0, -5.0, -6.0]]))) == [1, 0]
+    assert list(OM.last_rows([(0, 3), (9, 1), (2, 5)])) == [2, 3, 8]
+
+
 ALL_CHECKS = [
     check_attention_bruteforce, check_attention_sdpa_library, check_attention_closed_forms,
     check_gqa_group_mapping, check_rope_hand_values, check_rope_complex_form_and_invariance,
@@ -415,5 +478,6 @@ ALL_CHECKS = [
     check_batch_equals_alone, check_chunked_equals_one_shot,
     check_decode_equals_last_prefill_row, check_sampled_rows_match_full,
     check_block_permutation_addresses, check_kv_export_closed_form, check_kv_import_closed_form,
-    check_kv_round_trip_across_tables,
+    check_kv_round_trip_across_tables, check_model_head_library_and_identity_stack,
+    check_model_stack_is_layer_by_layer, check_greedy_hand_values,
 ]

@@ -10,6 +10,7 @@ import textwrap
 import pytest
 
 import oracle.kv_transfer as OKV
+import oracle.model as OM
 import oracle.layer as OL
 from tests import oracle_pins
 
@@ -46,6 +47,15 @@ KV_MUTANTS = [
     ("import_layer", "p = start + i", "p = start + i + 1"),
     ("import_layer", "b, s = int(table_row[p // BLOCK]), p % BLOCK", "b, s = int(table_row[p // BLOCK]), (p + 1) % BLOCK"),
 ]
+# planted mistakes in the model-step reference
+MODEL_MUTANTS = [
+    ("last_rows", "np.cumsum([n for _, n in seqs]) - 1", "np.cumsum([n for _, n in seqs]) - 2"),
+    ("lm_logits", "OL.linear(OL.rmsnorm(h, final_norm, eps), lm_head)", "OL.linear(h, lm_head)"),
+    ("greedy", "np.argmax(logits, axis=-1)", "np.argmax(logits[:, ::-1], axis=-1)"),
+    ("model_step", "x = OL.layer_step(shape, x, w, seqs, caches[l], block_table)[\"out\"]",
+     "x = OL.layer_step(shape, x, w, seqs, caches[0], block_table)[\"out\"]"),
+    ("model_step", "for l, w in enumerate(layers):", "for l, w in enumerate(layers[:1]):"),
+]
 
 
 def _mutant(fn_name, old, new, mod=OL):
@@ -75,6 +85,19 @@ def test_pins_catch_planted_mistake(monkeypatch, fn_name, old, new):
                          ids=[f"{m[0]}:{m[1][:24]}" for m in KV_MUTANTS])
 def test_pins_catch_planted_kv_transfer_mistake(monkeypatch, fn_name, old, new):
     monkeypatch.setattr(OKV, fn_name, _mutant(fn_name, old, new, OKV))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception:
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
+
+
+@pytest.mark.parametrize("fn_name,old,new", MODEL_MUTANTS,
+                         ids=[f"{m[0]}:{m[1][:24]}" for m in MODEL_MUTANTS])
+def test_pins_catch_planted_model_mistake(monkeypatch, fn_name, old, new):
+    monkeypatch.setattr(OM, fn_name, _mutant(fn_name, old, new, OM))
     caught = []
     for check in oracle_pins.ALL_CHECKS:
         try:

@@ -232,3 +232,29 @@ def describe(spec: BatchSpec) -> dict:
         "decodes": len(dec), "decode_ctx_mean": (float(np.mean(dec)) if dec else 0.0),
         "block_size": s.block_size,
     }
+
+
+# ---------------------------------------------------------------------- layer stacks (model step)
+
+def layer_spec(spec: BatchSpec, layer: int) -> BatchSpec:
+    """The same batch for layer `layer` of a stack: its own seed for that layer's weights and
+    cached K/V (the contexts, the block table and the tokens stay those of `spec`)."""
+    return BatchSpec(f"{spec.name}/L{layer}", spec.shape, list(spec.seqs),
+                     spec.seed * 1000 + 1 + layer, spec.pool_slack)
+
+
+def model_tensors(spec: BatchSpec, vocab: int, device="cpu") -> Dict[str, "object"]:
+    """Token ids [T] (uniform in [0, vocab)), embedding [vocab, hidden] ~ N(0, 1) (so embedded
+    activations are N(0, 1) like the layer workloads), LM head [vocab, hidden] ~ N(0, 0.02^2),
+    final norm gain 1."""
+    import torch
+    s = spec.shape
+    ss = np.random.SeedSequence([spec.seed, vocab, 77])
+    rng = np.random.default_rng(ss.spawn(1)[0])
+    tokens = rng.integers(0, vocab, spec.num_tokens).astype(np.int32)
+    return {
+        "tokens": tokens,
+        "embed": _randn_bf16((vocab, s.hidden), 1.0, _torch_seed(ss, 1), device),
+        "lm_head": _randn_bf16((vocab, s.hidden), 0.02, _torch_seed(ss, 2), device),
+        "final_norm": torch.ones(s.hidden, dtype=torch.bfloat16, device=device),
+    }
