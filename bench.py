@@ -114,7 +114,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2", help="cfg1..cfg5, cfg4_prefill_only, cfg4_decode_only")
+    ap.add_argument("--workload", default="cfg2",
+                    help="cfg1..cfg5, cfgN_prefill_only / cfgN_decode_only (the batch split), or "
+                         "p1_16dec_8k (16 decodes at 8K context, Qwen3-14B-shaped)")
+    ap.add_argument("--model-layers", type=int, default=0,
+                    help="time a whole model iteration instead of one layer: embedding, this many "
+                         "layers of the workload's shape (own weights and KV pools each), final "
+                         "norm + LM head on each sequence's last row, greedy (hl_model_step)")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="vocabulary of --model-layers (default: 151936 for the Qwen3 shapes, "
+                         "128256 for the 70B shape)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --model-layers: capture the iteration in a HIP graph and time replays")
     ap.add_argument("--phase-reps", type=int, default=20)
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="steps timed one at a time after overwriting 1 GiB (evicts the 256 MB "
@@ -156,10 +167,9 @@ def main():
                           "reps": args.phase_reps}), flush=True)
         return
     name = args.workload
-    if name.startswith("cfg4_"):
-        spec = workloads.make_spec(4, name[len("cfg4_"):])
-    else:
-        spec = workloads.make_spec(int(name[3:]))
+    spec = workloads.named_spec(name)
+    if args.model_layers > 0:
+        return model_bench(args, spec, dev)
     s = spec.shape
     T = spec.num_tokens
     table, pool = workloads.block_table(spec)
@@ -341,6 +351,77 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, x, w, table, dev, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def model_bench(args, spec, dev):
+    """Whole-model iteration (hl_model_step) on the workload's batch: tokens/s and ms per step."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from hybrid_prefill_decode_amd import binding as B
+    from hybrid_prefill_decode_amd import kvcache
+
+    s = spec.shape
+    L = args.model_layers
+    vocab = args.vocab or (128256 if s.hidden == 8192 else 151936)
+    table, pool = workloads.block_table(spec)
+    cfg = B.layer_cfg(s)
+    batch = B.Batch(spec.q_start, spec.num_cached, table, dev)
+    # every layer has its own weights; the cached K/V of layer 0 is copied into every layer's
+    # own pools (distinct memory, same values: the values do not change the work)
+    kp0, vp0 = kvcache.alloc_pools(pool, s.n_kv_heads, s.head_dim, dev, fill=0.0)
+    for si, (c, _) in enumerate(spec.seqs):
+        if c:
+            k, v = workloads.cached_kv(spec, si, dev)
+            kvcache.write_positions(kp0, vp0, table[si], range(c), k, v)
+    layers, pools = [], []
+    for l in range(L):
+        layers.append(workloads.weights(workloads.layer_spec(spec, l), dev))
+        pools.append((kp0.clone(), vp0.clone()) if l else (kp0, vp0))
+    t = workloads.model_tensors(spec, vocab, dev)
+    model = B.ModelHandle(layers, pools, t["embed"], t["final_norm"], t["lm_head"])
+    tokens = torch.from_numpy(t["tokens"]).to(dev)
+    logits = torch.empty(spec.num_seqs, vocab, dtype=torch.bfloat16, device=dev)
+    nxt = torch.empty(spec.num_seqs, dtype=torch.int32, device=dev)
+    ws = B.alloc_model_workspace(cfg, batch, model, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(st=None):
+        B.model_step(cfg, batch, model, tokens, t["tokens"], logits, nxt, ws,
+                     stream=st if st is not None else stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            step(gs)
+        run = g.replay
+        run()
+        torch.cuda.synchronize()
+    steps = max(args.steps // 5, 5)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        run()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    T = spec.num_tokens
+    print(json.dumps({
+        "metric": "model iteration tokens/s (embedding + layers + LM head + greedy)",
+        "value": round(T / (ms / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+        "ms_per_step": round(ms, 3), "step_ms": pct(per), "steps": steps, "warmup": args.warmup,
+        "layers": L, "vocab": vocab, "graph": bool(args.graph), "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights of the workload's layer shape)",
+        "config": {"workload": workloads.describe(spec), "parallelism": "none (1 GPU)"},
+    }), flush=True)
 
 
 def cpu_baseline(spec, x, w, table, dev, budget_s):

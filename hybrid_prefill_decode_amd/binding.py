@@ -64,6 +64,12 @@ class KvSpan(ctypes.Structure):
                 ("stream", ctypes.c_void_p)]
 
 
+class Model(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("embed", ctypes.c_void_p), ("layers", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+
+
 class HLError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -94,6 +100,11 @@ _SIGS = {
                             ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_gemm_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_model_workspace_bytes": ([ctypes.POINTER(Model), ctypes.POINTER(BatchDesc),
+                                  ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_model_step": ([ctypes.POINTER(Model), ctypes.POINTER(BatchDesc), ctypes.c_void_p, _c_i32p,
+                       ctypes.POINTER(BlockTable), ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p], ctypes.c_int),
     "hl_kv_export": ([ctypes.POINTER(KvSpan), ctypes.POINTER(KvPages), ctypes.c_void_p],
                      ctypes.c_int),
     "hl_kv_import": ([ctypes.POINTER(KvSpan), ctypes.c_void_p, ctypes.POINTER(KvPages)],
@@ -227,6 +238,43 @@ def kv_import(src, table_row, h_table_row, start: int, count: int, layer: int, k
     sp, keep = _span(table_row, h_table_row, hkv, d, L, layer, start, count, stream)
     kv = _pages(k_pool, v_pool)
     _check(lib().hl_kv_import(ctypes.byref(sp), _ptr(src), ctypes.byref(kv)), "hl_kv_import")
+
+
+class ModelHandle:
+    """Host-side description of a layer stack (keeps the ctypes arrays alive)."""
+
+    def __init__(self, layers, kv_pools, embed, final_norm, lm_head):
+        n = len(layers)
+        self.weights = (Weights * n)(*[_weights(w) for w in layers])
+        self.pages = (KvPages * n)(*[_pages(k, v) for k, v in kv_pools])
+        self.c = Model(n, int(embed.shape[0]), _ptr(embed), ctypes.cast(self.weights, ctypes.c_void_p),
+                       ctypes.cast(self.pages, ctypes.c_void_p), _ptr(final_norm), _ptr(lm_head))
+
+
+def model_workspace_bytes(cfg: LayerCfg, b: Batch, model: ModelHandle) -> int:
+    d = _desc(cfg, b, None, None, None)
+    v = ctypes.c_size_t(0)
+    _check(lib().hl_model_workspace_bytes(ctypes.byref(model.c), ctypes.byref(d), ctypes.byref(v)),
+           "hl_model_workspace_bytes")
+    return int(v.value)
+
+
+def alloc_model_workspace(cfg: LayerCfg, b: Batch, model: ModelHandle, device="cuda"):
+    import torch
+    n = max(model_workspace_bytes(cfg, b, model), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def model_step(cfg: LayerCfg, b: Batch, model: ModelHandle, tokens, h_tokens, logits,
+               next_tokens, workspace, hidden_out=None, stream=None) -> None:
+    """tokens: device int32 [T] with host mirror h_tokens (numpy int32); logits: device bf16
+    [num_seqs, vocab]; next_tokens: device int32 [num_seqs]."""
+    d = _desc(cfg, b, None, workspace, stream)
+    ht = np.ascontiguousarray(h_tokens, dtype=np.int32)
+    t = _table(b)
+    _check(lib().hl_model_step(ctypes.byref(model.c), ctypes.byref(d), _ptr(tokens),
+                               ht.ctypes.data_as(_c_i32p), ctypes.byref(t), _ptr(hidden_out),
+                               _ptr(logits), _ptr(next_tokens)), "hl_model_step")
 
 
 def _table(b: Batch) -> BlockTable:

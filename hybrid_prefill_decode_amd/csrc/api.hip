@@ -363,6 +363,61 @@ int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q
   return rc;
 }
 
+int check_weights(const hl_weights* w) {
+  if (!w) return HL_ERR_NULL;
+  if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
+    return HL_ERR_NULL;
+  for (const void* p : {(const void*)w->attn_norm, (const void*)w->w_qkv, (const void*)w->w_o,
+                        (const void*)w->mlp_norm, (const void*)w->w_gate_up,
+                        (const void*)w->w_down})
+    if (!aligned16(p)) return HL_ERR_ALIGN;
+  return HL_OK;
+}
+
+// The layer on a validated batch and plan.
+int run_layer(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
+              const hl_block_table* bt, const HostPlan& hp, hl_bf16* out) {
+  const hl_layer_cfg& c = *batch->cfg;
+  const int T = batch->num_tokens;
+  const int qd = c.n_q_heads * c.head_dim;
+  hipStream_t st = static_cast<hipStream_t>(batch->stream);
+  const Buffers B = buffers(batch, hp);
+  int rc;
+  if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B))) return rc;
+  if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true))) return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
+                                   plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), B.gemm_ws,
+                                   B.gemm_bytes, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_prep(B.h2, w->mlp_norm, B.h1, B.rs, T, c.hidden, c.rms_eps,
+                                   nullptr, st))))
+    return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, T, 2 * c.d_ff, c.hidden,
+                                   plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), nullptr, 0, st))))
+    return rc;
+  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
+                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
+                                B.gemm_bytes, st));
+}
+
+// Model workspace: the step's workspace, then two [T, H] residual-stream buffers, the last row of
+// each sequence and its gain-scaled copy ([S, H] each), and the final norm's row factors [S].
+struct ModelLayout {
+  size_t o_x0, o_x1, o_rows, o_rows_g, o_rs, total;
+};
+ModelLayout model_layout(const hl_batch_desc* b, size_t step_bytes) {
+  auto up = [](size_t v) { return (v + kAlign - 1) / kAlign * kAlign; };
+  const size_t T = b->num_tokens, S = b->num_seqs, H = b->cfg->hidden;
+  ModelLayout m;
+  m.o_x0 = up(step_bytes);
+  m.o_x1 = m.o_x0 + up(T * H * 2);
+  m.o_rows = m.o_x1 + up(T * H * 2);
+  m.o_rows_g = m.o_rows + up(S * H * 2);
+  m.o_rs = m.o_rows_g + up(S * H * 2);
+  m.total = m.o_rs + up(S * 4);
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -564,37 +619,86 @@ int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pag
   int rc = prepare(batch, kv, bt, &hp);
   if (rc) return rc;
   if (batch->num_seqs == 0) return HL_OK;
-  if (!w || !out || !batch->x) return HL_ERR_NULL;
-  if (!aligned16(batch->x)) return HL_ERR_ALIGN;
-  if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
-    return HL_ERR_NULL;
-  for (const void* p : {(const void*)w->attn_norm, (const void*)w->w_qkv, (const void*)w->w_o,
-                        (const void*)w->mlp_norm, (const void*)w->w_gate_up,
-                        (const void*)w->w_down, (const void*)out})
-    if (!aligned16(p)) return HL_ERR_ALIGN;
+  if (!out || !batch->x) return HL_ERR_NULL;
+  if (!aligned16(batch->x) || !aligned16(out)) return HL_ERR_ALIGN;
+  if ((rc = check_weights(w))) return rc;
   if ((const void*)out == (const void*)batch->x) return HL_ERR_ARG;
+  return run_layer(batch, w, kv, bt, hp, out);
+}
+
+int hl_model_workspace_bytes(const hl_model* m, const hl_batch_desc* batch, size_t* bytes) {
+  if (!m || !batch || !bytes) return HL_ERR_NULL;
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  HostPlan hp;
+  if (batch->num_seqs > 0) make_plan(batch, &hp);
+  *bytes = model_layout(batch, batch->num_seqs > 0 ? hp.total : 0).total;
+  return HL_OK;
+}
+
+int hl_model_step(const hl_model* m, const hl_batch_desc* batch, const int32_t* tokens,
+                  const int32_t* h_tokens, const hl_block_table* bt, hl_bf16* hidden_out,
+                  hl_bf16* logits, int32_t* next_tokens) {
+  if (!m || !batch) return HL_ERR_NULL;
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  if (batch->num_seqs == 0) return HL_OK;
+  if (m->num_layers < 1 || m->vocab <= 0 || m->vocab % 128) return HL_ERR_ARG;
+  if ((int64_t)m->vocab * batch->cfg->hidden > (int64_t)INT32_MAX) return HL_ERR_ARG;
+  if (!m->embed || !m->final_norm || !m->lm_head || !m->layers || !m->kv) return HL_ERR_NULL;
+  if (!tokens || !h_tokens || !logits || !next_tokens) return HL_ERR_NULL;
+  for (const void* p : {(const void*)m->embed, (const void*)m->final_norm,
+                        (const void*)m->lm_head, (const void*)logits, (const void*)tokens,
+                        (const void*)next_tokens})
+    if (!aligned16(p)) return HL_ERR_ALIGN;
+  if (hidden_out && !aligned16(hidden_out)) return HL_ERR_ALIGN;
+  for (int t = 0; t < batch->num_tokens; ++t)
+    if (h_tokens[t] < 0 || h_tokens[t] >= m->vocab) return HL_ERR_ARG;
+  for (int l = 0; l < m->num_layers; ++l) {
+    if ((rc = check_weights(&m->layers[l]))) return rc;
+    if (!m->kv[l].k || !m->kv[l].v) return HL_ERR_NULL;
+    if (m->kv[l].num_blocks != m->kv[0].num_blocks) return HL_ERR_ARG;
+  }
+  // plan once for every layer (same batch, same table, pools of one size); the step's own
+  // workspace sits first in the model workspace
+  HostPlan hp;
+  hl_batch_desc inner = *batch;
+  if (!batch->workspace) return HL_ERR_WORKSPACE;
+  make_plan(batch, &hp);
+  const ModelLayout ml = model_layout(batch, hp.total);
+  if (batch->workspace_bytes < ml.total) return HL_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(batch->workspace);
+  inner.workspace_bytes = hp.total;
+  inner.x = reinterpret_cast<hl_bf16*>(base + ml.o_x0);
+  inner.tap_q_rot = inner.tap_attn_out = inner.tap_h2 = nullptr;  // per-layer tensors: not kept
+  if ((rc = prepare(&inner, &m->kv[0], bt, &hp))) return rc;
 
   const hl_layer_cfg& c = *batch->cfg;
-  const int T = batch->num_tokens;
-  const int qd = c.n_q_heads * c.head_dim;
+  const int T = batch->num_tokens, S = batch->num_seqs, H = c.hidden;
   hipStream_t st = static_cast<hipStream_t>(batch->stream);
-  const Buffers B = buffers(batch, hp);
-
-  if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B))) return rc;
-  if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true))) return rc;
-  if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
-                                   plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), B.gemm_ws,
-                                   B.gemm_bytes, st))))
+  hl_bf16* xa = reinterpret_cast<hl_bf16*>(base + ml.o_x0);
+  hl_bf16* xb = reinterpret_cast<hl_bf16*>(base + ml.o_x1);
+  if ((rc = hip_rc(hl::launch_embed(tokens, m->embed, xa, T, H, m->vocab, st)))) return rc;
+  for (int l = 0; l < m->num_layers; ++l) {
+    hl_bf16* dst = (l == m->num_layers - 1 && hidden_out) ? hidden_out : xb;
+    inner.x = xa;
+    if ((rc = run_layer(&inner, &m->layers[l], &m->kv[l], bt, hp, dst))) return rc;
+    xb = xa;
+    xa = dst;
+  }
+  // logits of the last row of every sequence: final RMSNorm as a row factor into the LM head
+  hl_bf16* rows = reinterpret_cast<hl_bf16*>(base + ml.o_rows);
+  hl_bf16* rows_g = reinterpret_cast<hl_bf16*>(base + ml.o_rows_g);
+  float* rrs = reinterpret_cast<float*>(base + ml.o_rs);
+  const Buffers B = buffers(&inner, hp);
+  if ((rc = hip_rc(hl::launch_last_rows(batch->q_start, xa, rows, S, H, st)))) return rc;
+  if ((rc = hip_rc(hl::launch_prep(rows, m->final_norm, rows_g, rrs, S, H, c.rms_eps, nullptr, st))))
     return rc;
-  if ((rc = hip_rc(hl::launch_prep(B.h2, w->mlp_norm, B.h1, B.rs, T, c.hidden, c.rms_eps,
-                                   nullptr, st))))
+  if ((rc = hip_rc(hl::launch_gemm(rows_g, m->lm_head, logits, S, m->vocab, H,
+                                   plain_epi(HL_EPI_NONE, nullptr, rrs), B.gemm_ws, B.gemm_bytes,
+                                   st))))
     return rc;
-  if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, T, 2 * c.d_ff, c.hidden,
-                                   plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), nullptr, 0, st))))
-    return rc;
-  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
-                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
-                                B.gemm_bytes, st));
+  return hip_rc(hl::launch_argmax(logits, S, m->vocab, next_tokens, st));
 }
 
 }  // extern "C"

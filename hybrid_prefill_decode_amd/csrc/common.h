@@ -152,6 +152,13 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
 
 constexpr int kPrefillQTile = 128;  // query rows per prefill work tile
 
+// Model-level kernels (model.hip).
+hipError_t launch_embed(const int32_t* tokens, const hl_bf16* table, hl_bf16* x, int T, int H,
+                        int vocab, hipStream_t st);
+hipError_t launch_last_rows(const int32_t* q_start, const hl_bf16* x, hl_bf16* rows, int S, int H,
+                            hipStream_t st);
+hipError_t launch_argmax(const hl_bf16* logits, int S, int V, int32_t* out, hipStream_t st);
+
 // One request's K/V span to (exporting) or from the [L][2][T][Hkv][d] transfer layout.
 hipError_t launch_kv_span(const hl_kv_span& s, const hl_kv_pages& kv, hl_bf16* buf, bool exporting);
 

@@ -165,6 +165,43 @@ const char* hl_strerror(int code);
 /* HL_VERSION of the library. */
 int hl_version(void);
 
+/* ---- a model step: embedding, the layer stack, LM head, greedy token --------------------- */
+
+/* A decoder stack of num_layers layers of one hl_layer_cfg shape. Every layer has its own
+ * weights and its own KV pools; all pools have the same num_blocks and share one block table
+ * (a sequence's logical page j is block table[s][j] in every layer). */
+typedef struct {
+  int32_t num_layers;
+  int32_t vocab;              /* multiple of 128 */
+  const hl_bf16* embed;       /* device [vocab, hidden] */
+  const hl_weights* layers;   /* host array [num_layers] */
+  hl_kv_pages* kv;            /* host array [num_layers] */
+  const hl_bf16* final_norm;  /* device [hidden] */
+  const hl_bf16* lm_head;     /* device [vocab, hidden] */
+} hl_model;
+
+/* Workspace of hl_model_step for this batch (the layer step's own, plus the residual stream and
+ * the per-sequence last rows), from the host mirrors only. */
+int hl_model_workspace_bytes(const hl_model* model, const hl_batch_desc* batch, size_t* bytes);
+
+/* One iteration over the hybrid batch, every layer in turn: x = embed[tokens]; for each layer,
+ * x = hybrid_layer_step(x) (each appending the batch's K/V rows to its own pools); then for the
+ * last new token of each sequence s, logits[s] = RMSNorm(x[row], final_norm) lm_head^T (bf16,
+ * [num_seqs, vocab]) and next_tokens[s] = the first index of its largest logit (greedy). A request
+ * whose last prompt chunk completes takes its first token from this same pass ("Chunked prefill
+ * (stall-free batching), explained", "How it works, step by step"); chapter 7.8's prefill listing
+ * takes the logits of the last position only and their argmax. For a chunk that does not end
+ * its prompt, next_tokens[s] is computed but has no meaning. tokens: device [num_tokens] with host
+ * mirror h_tokens (ids checked against vocab); batch->x is ignored; batch->workspace must hold
+ * hl_model_workspace_bytes() bytes. hidden_out (optional, device [num_tokens, hidden]) receives x
+ * after the last layer (before the final norm). No host synchronisation and no allocation: the
+ * call can be captured in a HIP graph (replays repeat the same batch). Errors as
+ * hybrid_layer_step; HL_ERR_ARG for num_layers < 1, vocab % 128, an id outside [0, vocab) or
+ * pools of different sizes. */
+int hl_model_step(const hl_model* model, const hl_batch_desc* batch, const int32_t* tokens,
+                  const int32_t* h_tokens, const hl_block_table* block_table, hl_bf16* hidden_out,
+                  hl_bf16* logits, int32_t* next_tokens);
+
 /* ---- KV transfer between instances ------------------------------------------------------ */
 
 /* One request's token span [start, start + count) of one layer, for the KV hand-off between a

@@ -1,0 +1,108 @@
+"""GPU parity of hl_model_step (embedding, a stack of hybrid layers, final norm + LM head on the
+last row of each sequence, greedy) against the fp64 oracle, and the same call captured in a HIP
+graph and replayed.
+
+Tolerance: the layer tests hold each layer to max|gpu - ref| <= 1e-2 * max|ref|, and the stack
+stores the residual stream in bf16 between layers, so the errors of successive layers add: the
+hidden rows after L layers are held to L * 1e-2 (in practice each layer contributes about 3e-3),
+the logits to 1e-2. The greedy pick is an integer decided by floating point, so both sides
+take it on the same numbers: the GPU's bf16 logits, whose first-largest index must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.model as OM
+import workloads
+from hybrid_prefill_decode_amd import binding as B
+from tests._gpu import assert_close, make_pools, say
+from tests._util import f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class ModelCase:
+    def __init__(self, spec, layers, vocab):
+        self.spec, s = spec, spec.shape
+        self.table, self.pool = workloads.block_table(spec)
+        self.cfg = B.layer_cfg(s)
+        self.batch = B.Batch(spec.q_start, spec.num_cached, self.table, DEV)
+        self.t = workloads.model_tensors(spec, vocab, DEV)
+        self.lspecs = [workloads.layer_spec(spec, l) for l in range(layers)]
+        self.ws_layers = [workloads.weights(ls, DEV) for ls in self.lspecs]
+        self.pools = [make_pools(ls, self.table, self.pool, DEV) for ls in self.lspecs]
+        self.model = B.ModelHandle(self.ws_layers, self.pools, self.t["embed"],
+                                   self.t["final_norm"], self.t["lm_head"])
+        self.tokens = torch.from_numpy(self.t["tokens"]).to(DEV)
+        T, S = spec.num_tokens, spec.num_seqs
+        self.hidden = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=DEV)
+        self.logits = torch.empty(S, vocab, dtype=torch.bfloat16, device=DEV)
+        self.next = torch.empty(S, dtype=torch.int32, device=DEV)
+        self.ws = B.alloc_model_workspace(self.cfg, self.batch, self.model, DEV)
+
+    def step(self, stream=None):
+        B.model_step(self.cfg, self.batch, self.model, self.tokens, self.t["tokens"], self.logits,
+                     self.next, self.ws, hidden_out=self.hidden, stream=stream)
+
+    def oracle(self):
+        caches = [[tuple(f64(a) for a in workloads.cached_kv(ls, si, DEV))
+                   for si in range(self.spec.num_seqs)] for ls in self.lspecs]
+        layers = [{k: f64(v) for k, v in w.items()} for w in self.ws_layers]
+        return OM.model_step(self.spec.shape, self.t["tokens"], f64(self.t["embed"]), layers,
+                             f64(self.t["final_norm"]), f64(self.t["lm_head"]), self.spec.seqs,
+                             caches, self.table)
+
+
+CASES = {
+    # config 1's batch (a 64-token chunk at prefix 64 + 4 decodes) through 3 layers
+    "tiny_L3": (lambda: workloads.make_spec(1), 3, 512),
+    # a ragged batch on a d = 128, GQA 4 shape: chunks, decodes at page edges, one fresh prompt
+    "d128_L2": (lambda: workloads.custom_spec(workloads.LayerShape(1024, 8, 2, 128, 1024),
+                                              [(0, 150), (31, 1), (256, 1), (100, 33), (15, 1)],
+                                              5), 2, 1024),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_model_step_vs_oracle(case):
+    mk, layers, vocab = CASES[case]
+    mc = ModelCase(mk(), layers, vocab)
+    say(f"model step {case}: {mc.spec.seqs}, {layers} layers, vocab {vocab}")
+    mc.step()
+    torch.cuda.synchronize()
+    ref = mc.oracle()
+    assert_close(f64(mc.hidden), ref["hidden"], "hidden after the last layer", tol=1e-2 * layers)
+    assert_close(f64(mc.logits), ref["logits"], "logits")
+    got = mc.next.cpu().numpy()
+    want = OM.greedy(mc.logits.float().cpu().numpy())
+    assert np.array_equal(got, want), (got, want)
+
+
+def test_model_step_graph_replays():
+    """The whole iteration captured once and replayed: each replay, with unrelated eager work and
+    synchronisations between replays, gives the eager result bit for bit (the K/V appends are
+    idempotent, so a replay repeats the same batch exactly)."""
+    mk, layers, vocab = CASES["tiny_L3"]
+    mc = ModelCase(mk(), layers, vocab)
+    mc.step()  # eager: also the first-call set-up, which must not happen under capture
+    torch.cuda.synchronize()
+    want = [mc.hidden.clone(), mc.logits.clone(), mc.next.clone()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mc.step(stream=s)
+    junk = torch.zeros(1 << 20, device=DEV)
+    for rep in range(4):
+        mc.hidden.fill_(0)
+        mc.logits.fill_(0)
+        mc.next.fill_(-1)
+        junk.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip([mc.hidden, mc.logits, mc.next], want):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep
+    say("graph replays bit-identical to the eager step")

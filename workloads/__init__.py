@@ -95,8 +95,8 @@ def _seq_streams(seed: int) -> List[np.random.SeedSequence]:
 
 
 def make_spec(cfg: int, variant: str = "mixed") -> BatchSpec:
-    """Build the batch of workload `cfg` (1..5). `variant` is "mixed", or for 4 also
-    "prefill_only" / "decode_only" (same data as the mixed batch, split)."""
+    """Build the batch of workload `cfg` (1..5). `variant` is "mixed", "prefill_only" or
+    "decode_only" (the same data as the mixed batch, split; workload 4 names the split runs)."""
     seed = 1000 + cfg
     ctx_rng = np.random.Generator(np.random.PCG64(_seq_streams(seed)[0]))
     if cfg == 1:
@@ -127,13 +127,21 @@ def make_spec(cfg: int, variant: str = "mixed") -> BatchSpec:
     spec = BatchSpec(f"cfg{cfg}", shape, seqs, seed, slack)
     if variant == "mixed":
         return spec
-    if cfg != 4:
-        raise ValueError("prefill_only / decode_only exist for workload 4")
     if variant == "prefill_only":
-        return BatchSpec("cfg4_prefill_only", shape, seqs[:1], seed, slack)
+        return BatchSpec(f"cfg{cfg}_prefill_only", shape, seqs[:1], seed, slack)
     if variant == "decode_only":
-        return BatchSpec("cfg4_decode_only", shape, seqs[1:], seed, slack)
+        return BatchSpec(f"cfg{cfg}_decode_only", shape, seqs[1:], seed, slack)
     raise ValueError(variant)
+
+
+def named_spec(name: str) -> BatchSpec:
+    """cfgN, cfgN_prefill_only, cfgN_decode_only, or "p1_16dec_8k": the decode-only scenario the
+    ConfluxServe page times on a full model (16 decodes at 8K context, Qwen3-14B-shaped)."""
+    if name == "p1_16dec_8k":
+        return BatchSpec(name, SHAPES["qwen3_14b"], [(8192, 1)] * 16, 1100, 1.25)
+    if "_" in name:
+        return make_spec(int(name[3:name.index("_")]), name[name.index("_") + 1:])
+    return make_spec(int(name[3:]))
 
 
 def custom_spec(shape: LayerShape, seqs: Sequence[Tuple[int, int]], seed: int,
