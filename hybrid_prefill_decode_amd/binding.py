@@ -345,13 +345,14 @@ def gemm_workspace_bytes(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE) ->
 
 def gemm_tile_choice(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE,
                      with_workspace: bool = True, qkv_head_dim: int = 0):
-    """(tile_m, tile_n, stream_k) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's QKV
-    projection) uses for this shape; host-only."""
+    """(tile_m, tile_n, schedule) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's QKV
+    projection) uses for this shape; schedule 0 = one tile per workgroup, 1 = stream-K, 2 = the
+    split-K path of up to 64 token rows. Host-only."""
     tm, tn, sk = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(lib().hl_gemm_tile_choice(m, n, k, epilogue, int(bool(with_workspace)), qkv_head_dim,
                                      ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sk)),
            "hl_gemm_tile_choice")
-    return tm.value, tn.value, bool(sk.value)
+    return tm.value, tn.value, int(sk.value)
 
 
 def rms_scale(x, gain, xg, row_scale, eps: float, stream=None) -> None:

@@ -331,7 +331,7 @@ int run_qkv(const hl_batch_desc* b, const hl_weights* w, hl_bf16* q_rot, const h
   e.rope_cs = B.cs;
   const int qkv_cols = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   return hip_rc(hl::launch_gemm(B.h1, w->w_qkv, nullptr, b->num_tokens, qkv_cols, c.hidden, e,
-                                nullptr, 0, st));
+                                B.gemm_ws, B.gemm_bytes, st));
 }
 
 int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q_lo,
@@ -393,7 +393,8 @@ int run_layer(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
                                    nullptr, st))))
     return rc;
   if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, T, 2 * c.d_ff, c.hidden,
-                                   plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), nullptr, 0, st))))
+                                   plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), B.gemm_ws,
+                                   B.gemm_bytes, st))))
     return rc;
   return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
                                 plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
@@ -474,6 +475,12 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
     return HL_ERR_ARG;
   if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
   if (qkv_head_dim != 0 && qkv_head_dim != 64 && qkv_head_dim != 128) return HL_ERR_ARG;
+  if (with_workspace && hl::use_skinny(m, n, k, hl::gemm_workspace_bytes(m, n, k, epilogue))) {
+    *tile_m = 16 * ((m + 15) / 16);
+    *tile_n = 64;
+    *stream_k = 2;
+    return HL_OK;
+  }
   const bool split = !qkv_head_dim && epilogue != HL_EPI_SWIGLU && with_workspace;
   const hl::TileChoice tc = hl::choose_tiles(m, n, k, split, qkv_head_dim ? qkv_head_dim : 1);
   *tile_m = tc.bm;

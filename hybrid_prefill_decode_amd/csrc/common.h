@@ -118,6 +118,12 @@ struct TileChoice {
 // Tile shape and schedule of a GEMM launch (gemm.hip); col_align: N-tile widths a multiple of it.
 TileChoice choose_tiles(int m, int n, int k, bool split_ok, int col_align);
 bool gemm_tile_supported(int bm, int bn);
+// few-token path (gemm_skinny.hip): split-K weight streaming with fp32 partials in the workspace
+constexpr int kSkinnyMaxM = 64;
+size_t skinny_workspace_bytes(int m, int n, int k);
+bool use_skinny(int m, int n, int k, size_t ws_bytes);  // the path launch_gemm takes
+hipError_t launch_gemm_skinny(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
+                              const GemmEpi& epi, float* part, hipStream_t st);
 // plain / residual / SwiGLU GEMM with a given tile shape (stream-K needs the workspace)
 hipError_t launch_gemm_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m, int32_t n,
                              int32_t k, const GemmEpi& epi, const TileChoice& tc, void* ws,

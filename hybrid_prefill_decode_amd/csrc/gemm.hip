@@ -78,6 +78,10 @@ TileChoice choose_tiles(int m, int n, int k, bool split_ok, int col_align) {
   return best;
 }
 
+bool use_skinny(int m, int n, int k, size_t ws_bytes) {
+  return m > 0 && m <= kSkinnyMaxM && n % 64 == 0 && ws_bytes >= skinny_workspace_bytes(m, n, k);
+}
+
 bool gemm_tile_supported(int bm, int bn) {
   for (const TileCost& t : kTiles)
     if (t.bm == bm && t.bn == bn) return true;
@@ -102,6 +106,9 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
                        int32_t k, const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   float* part = (ws && ws_bytes >= kStreamKWorkspace) ? static_cast<float*>(ws) : nullptr;
+  // few tokens: stream the weights with every compute unit (split K), when the partials fit
+  if (ws && use_skinny(m, n, k, ws_bytes))
+    return launch_gemm_skinny(a, w, c, m, n, k, epi, static_cast<float*>(ws), st);
   switch (epi.kind) {
     case HL_EPI_NONE:
       return launch_gemm_plain(choose_tiles(m, n, k, part != nullptr, 1), a, w, c, m, n, k, epi,

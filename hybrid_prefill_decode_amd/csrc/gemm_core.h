@@ -373,16 +373,29 @@ HL_DEV int block_row(int lane, int r) { return (lane >> 4) * 4 + r; }
 // RoPE + KV append for 8 pairs of one staged row: `srow` points at the fp32 row of one head.
 // Only decode tokens (`decode`) get the low half of q: decode attention alone reads it.
 template <int HD>
+HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot, bool decode,
+                            float (&a)[8], float (&b)[8], int c);
+
+template <int HD>
 HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot, bool decode,
                            const float* srow, int c) {
   constexpr int half = HD / 2;
-  const int Hq = ep.n_q_heads, Hkv = ep.n_kv_heads;
   float a[8], b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     a[e] = srow[8 * c + e];
     b[e] = srow[half + 8 * c + e];
   }
+  rope_store_vals<HD>(ep, gm, gh, blk, slot, decode, a, b, c);
+}
+
+// The same for values already in registers: a = elements 8c .. 8c+7 of the head, b = the
+// elements d/2 apart from them (their rotation partners).
+template <int HD>
+HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot, bool decode,
+                            float (&a)[8], float (&b)[8], int c) {
+  constexpr int half = HD / 2;
+  const int Hq = ep.n_q_heads, Hkv = ep.n_kv_heads;
   if (gh < Hq + Hkv) {
     const float2* cs = ep.rope_cs + (size_t)gm * half + 8 * c;
 #pragma unroll

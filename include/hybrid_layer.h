@@ -259,10 +259,11 @@ int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_
  *   HL_EPI_SWIGLU   W holds 2f rows (f = n / 2 gate rows, then f up rows);
  *                   c [m, f] = silu(s * A W_gate^T) * (s * A W_up^T)
  * Requirements: k % 64 == 0, n % 128 == 0, m >= 0, m * k and n * k at most 2^31 - 1 (operands
- * are addressed with 32-bit byte offsets; HL_ERR_ARG otherwise). `workspace` (device, may be NULL): when it
- * holds hl_gemm_workspace_bytes() bytes, shapes with fewer output tiles than compute units run a
- * stream-K schedule (partial tiles in the workspace, summed by a fix-up pass); without it they run
- * one tile per workgroup. Results agree to fp32 summation order either way. */
+ * are addressed with 32-bit byte offsets; HL_ERR_ARG otherwise). `workspace` (device, may be
+ * NULL): when it holds hl_gemm_workspace_bytes() bytes, up to 64 token rows take a split-K
+ * weight-streaming path (fp32 partials in the workspace, summed in a fixed order by the epilogue
+ * pass), and larger shapes may run a stream-K schedule (partial tiles summed by a fix-up pass);
+ * without it every shape runs one tile per workgroup. Results agree to fp32 summation order. */
 enum { HL_EPI_NONE = 0, HL_EPI_RESIDUAL = 1, HL_EPI_SWIGLU = 2 };
 int hl_gemm_bf16_nt(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, const hl_bf16* residual,
                     const float* row_scale, int32_t m, int32_t n, int32_t k, int32_t epilogue,
@@ -281,7 +282,9 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                           int32_t stream_k, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The tile shape (*tile_m x *tile_n outputs per workgroup) and schedule (*stream_k: 1 for a
- * stream-K run with a fix-up pass, 0 for one tile per workgroup) that hl_gemm_bf16_nt uses for
+ * stream-K run with a fix-up pass, 0 for one tile per workgroup, 2 for the split-K path of up to
+ * 64 token rows, whose workgroups each cover 64 columns of all rows over a K range) that
+ * hl_gemm_bf16_nt uses for
  * these arguments (with_workspace != 0: a stream-K workspace is passed). qkv_head_dim 64 or 128
  * asks instead for the QKV projection of the layer step (RoPE + KV-append epilogue: one tile per
  * workgroup, whole heads per tile); 0 otherwise. Host-only: no device work, no GPU needed. The

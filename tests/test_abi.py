@@ -213,6 +213,9 @@ def test_gemm_tile_choice_is_valid(epi):
         ws = bool(rng.integers(0, 2))
         hd = int(rng.choice([0, 64, 128])) if epi == B.HL_EPI_NONE else 0
         bm, bn, sk = B.gemm_tile_choice(m, n, k, epi, ws, hd)
+        if sk == 2:  # split-K path of few token rows
+            assert ws and 0 < m <= 64 and bn == 64 and bm == 16 * ((m + 15) // 16), (m, n, k)
+            continue
         assert (bm, bn) in tiles and n % bn == 0, (m, n, k, bm, bn)
         if sk:
             assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)

@@ -121,6 +121,33 @@ def test_gemm_every_tile_shape(tile, epi, stream_k):
         assert_close(f64(c), ref, f"gemm {bm}x{bn} sk={stream_k}")
 
 
+@pytest.mark.parametrize("m", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("n,k", [(384, 320), (1024, 4096)])
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
+def test_gemm_few_tokens_vs_oracle(m, n, k, epi):
+    """Up to 64 token rows with a workspace: the split-K weight-streaming path (fp32 partials per
+    K chunk, summed in chunk order by the epilogue pass), with a row scale."""
+    assert B.gemm_tile_choice(m, n, k, epi, True)[2] == 2
+    say(f"gemm few tokens m={m} n={n} k={k} epi={epi}")
+    a = _randn((m, k), 51 + m)
+    w = _randn((n, k), 52 + n, 0.05)
+    out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
+    res = _randn((m, out_n), 53 + k) if epi == B.HL_EPI_RESIDUAL else None
+    rs = 0.5 + torch.rand(m, generator=torch.Generator(device=DEV).manual_seed(m), device=DEV)
+    ws = torch.empty(B.gemm_workspace_bytes(m, n, k, epi), dtype=torch.uint8, device=DEV)
+    c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt(a, w, c, res, epi, workspace=ws, row_scale=rs)
+    torch.cuda.synchronize()
+    A, W = f64(a) * f64(rs)[:, None], f64(w)
+    if epi == B.HL_EPI_SWIGLU:
+        ref = OL.swiglu(A, W, n // 2)
+    else:
+        ref = OL.linear(A, W)
+        if epi == B.HL_EPI_RESIDUAL:
+            ref = ref + f64(res)
+    assert_close(f64(c), ref, "gemm few tokens")
+
+
 def _edge_sample(size, tile, count, seed):
     """Indices that include both edges of every tile plus the ragged end, and random fill."""
     idx = {0, size - 1}
@@ -192,6 +219,9 @@ QKV_CASES = {
                   [(0, 2900), (777, 3000), (5000, 1), (33, 1), (15, 130)]),
     "wide_d64": (workloads.LayerShape(1024, 16, 4, 64, 512),
                  [(3, 3100), (0, 2800), (4095, 1), (16, 1), (250, 100)]),
+    # at most 64 tokens: the split-K weight-streaming path and its RoPE / KV-append epilogue pass
+    "few_d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 9), (70000, 1), (33, 1), (15, 17)]),
+    "few_d64": (workloads.LayerShape(1024, 16, 4, 64, 512), [(0, 1), (4095, 1), (16, 30), (255, 1)]),
 }
 # One case per RoPE-epilogue tile shape: the token count decides the tile the QKV projection gets
 # (checked against the library's own choice below), so each count below lands on another shape.
