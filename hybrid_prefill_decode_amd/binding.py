@@ -70,6 +70,19 @@ class Model(ctypes.Structure):
                 ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
 
 
+class SchedParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("budget", "max_seqs", "num_blocks",
+                                             "max_blocks_per_seq", "adaptive", "min_chunk",
+                                             "base_chunk", "max_chunk", "pressure_threshold")]
+
+
+class SchedBatch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("q_start", _c_i32p), ("num_cached", _c_i32p), ("request_ids", _c_i32p),
+                ("table", _c_i32p), ("decode_tokens", _c_i32p), ("emits", _c_i32p),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
 class HLError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -105,6 +118,13 @@ _SIGS = {
     "hl_model_step": ([ctypes.POINTER(Model), ctypes.POINTER(BatchDesc), ctypes.c_void_p, _c_i32p,
                        ctypes.POINTER(BlockTable), ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_void_p], ctypes.c_int),
+    "hl_sched_create": ([ctypes.POINTER(SchedParams)], ctypes.c_void_p),
+    "hl_sched_destroy": ([ctypes.c_void_p], None),
+    "hl_sched_submit": ([ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                         _c_i32p], ctypes.c_int),
+    "hl_sched_next": ([ctypes.c_void_p, ctypes.POINTER(SchedBatch)], ctypes.c_int),
+    "hl_sched_complete": ([ctypes.c_void_p, _c_i32p, _c_i32p, _c_i32p], ctypes.c_int),
+    "hl_sched_counts": ([ctypes.c_void_p, _c_i32p, _c_i32p, _c_i32p, _c_i32p], ctypes.c_int),
     "hl_kv_export": ([ctypes.POINTER(KvSpan), ctypes.POINTER(KvPages), ctypes.c_void_p],
                      ctypes.c_int),
     "hl_kv_import": ([ctypes.POINTER(KvSpan), ctypes.c_void_p, ctypes.POINTER(KvPages)],
@@ -275,6 +295,59 @@ def model_step(cfg: LayerCfg, b: Batch, model: ModelHandle, tokens, h_tokens, lo
     _check(lib().hl_model_step(ctypes.byref(model.c), ctypes.byref(d), _ptr(tokens),
                                ht.ctypes.data_as(_c_i32p), ctypes.byref(t), _ptr(hidden_out),
                                _ptr(logits), _ptr(next_tokens)), "hl_model_step")
+
+
+class Scheduler:
+    """The native token-budget scheduler (hl_sched_*): host-side batch formation."""
+
+    def __init__(self, budget=0, max_seqs=1, num_blocks=1, max_blocks_per_seq=1, adaptive=False,
+                 min_chunk=128, base_chunk=512, max_chunk=4096, pressure_threshold=16):
+        p = SchedParams(budget, max_seqs, num_blocks, max_blocks_per_seq, int(bool(adaptive)),
+                        min_chunk, base_chunk, max_chunk, pressure_threshold)
+        self.h = lib().hl_sched_create(ctypes.byref(p))
+        if not self.h:
+            raise HLError(HL_ERR_ARG, "hl_sched_create")
+        self.max_blocks = max_blocks_per_seq
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib().hl_sched_destroy(self.h)
+            self.h = None
+
+    def submit(self, rid: int, prompt_len: int, max_new: int) -> int:
+        h = ctypes.c_int32(0)
+        _check(lib().hl_sched_submit(self.h, rid, prompt_len, max_new, ctypes.byref(h)),
+               "hl_sched_submit")
+        return h.value
+
+    def next(self):
+        """dict of numpy arrays: q_start, num_cached, request_ids, table [S, max_blocks],
+        decode_tokens, emits (copies)."""
+        b = SchedBatch()
+        _check(lib().hl_sched_next(self.h, ctypes.byref(b)), "hl_sched_next")
+        S = b.num_seqs
+
+        def arr(p, n):
+            return np.ctypeslib.as_array(p, shape=(n,)).copy() if n else np.zeros(0, np.int32)
+        return {"num_tokens": b.num_tokens, "q_start": arr(b.q_start, S + 1) if S else
+                np.zeros(1, np.int32), "num_cached": arr(b.num_cached, S),
+                "request_ids": arr(b.request_ids, S),
+                "table": arr(b.table, S * b.max_blocks_per_seq).reshape(S, b.max_blocks_per_seq),
+                "decode_tokens": arr(b.decode_tokens, S), "emits": arr(b.emits, S)}
+
+    def complete(self, next_tokens):
+        nt = np.ascontiguousarray(next_tokens, dtype=np.int32)
+        fin = np.zeros(max(len(nt), 1), dtype=np.int32)
+        nf = ctypes.c_int32(0)
+        _check(lib().hl_sched_complete(self.h, nt.ctypes.data_as(_c_i32p),
+                                       fin.ctypes.data_as(_c_i32p), ctypes.byref(nf)),
+               "hl_sched_complete")
+        return fin[:nf.value].tolist()
+
+    def counts(self):
+        v = [ctypes.c_int32(0) for _ in range(4)]
+        _check(lib().hl_sched_counts(self.h, *[ctypes.byref(x) for x in v]), "hl_sched_counts")
+        return tuple(x.value for x in v)  # waiting, prefilling, decoding, free blocks
 
 
 def _table(b: Batch) -> BlockTable:

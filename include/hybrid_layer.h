@@ -202,6 +202,64 @@ int hl_model_step(const hl_model* model, const hl_batch_desc* batch, const int32
                   const int32_t* h_tokens, const hl_block_table* block_table, hl_bf16* hidden_out,
                   hl_bf16* logits, int32_t* next_tokens);
 
+/* ---- token-budget scheduler (host) ------------------------------------------------------- */
+
+/* The iteration-level scheduler of chunked prefill that produces the hybrid batches: each
+ * iteration fills a token budget with one token per running decode, then the next chunk of the
+ * prompt being prefilled, then waiting requests in arrival order while budget, sequence slots and
+ * KV blocks remain ("Chunked prefill (stall-free batching), explained", "How it works, step by
+ * step"). With adaptive != 0 the prefill share follows chapter 7.8's dynamic chunk sizing:
+ * max_chunk while no request decodes, min_chunk once pressure_threshold or more do, linear from
+ * base_chunk to min_chunk in between (decode tokens come on top). A request is admitted only when
+ * blocks for its whole lifetime (prompt + outputs, 16 tokens per block) are free; they are taken
+ * from one free list of num_blocks ids (the pages of every layer's pool) and returned when it
+ * finishes, so nothing is ever preempted. Host memory only; not thread-safe. */
+typedef struct {
+  int32_t budget;               /* tokens per iteration (fixed policy) */
+  int32_t max_seqs;             /* sequences prefilling or decoding at once */
+  int32_t num_blocks;           /* KV blocks in the pool */
+  int32_t max_blocks_per_seq;   /* block-table row length */
+  int32_t adaptive;             /* 0: fixed budget; 1: dynamic chunk sizing */
+  int32_t min_chunk, base_chunk, max_chunk, pressure_threshold;  /* adaptive policy */
+} hl_sched_params;
+
+/* One iteration's batch, in the layout of hl_batch_desc / hl_block_table (host arrays owned by
+ * the scheduler, valid until the next hl_sched_next). Sequences are in priority order: decodes,
+ * then prompt chunks. decode_tokens[s] is the token a decode feeds (its last output), -1 for a
+ * prompt chunk (the caller supplies prompt tokens num_cached[s] .. num_cached[s] + q_len - 1);
+ * emits[s] = 1 if sequence s takes a new token from this iteration (decodes, and prompts whose
+ * last chunk this is). */
+typedef struct {
+  int32_t num_seqs, num_tokens;
+  const int32_t* q_start;        /* [num_seqs + 1] */
+  const int32_t* num_cached;     /* [num_seqs] */
+  const int32_t* request_ids;    /* [num_seqs] */
+  const int32_t* table;          /* [num_seqs, max_blocks_per_seq] */
+  const int32_t* decode_tokens;  /* [num_seqs] */
+  const int32_t* emits;          /* [num_seqs] */
+  int32_t max_blocks_per_seq;
+} hl_sched_batch;
+
+typedef struct hl_sched hl_sched;
+
+/* NULL for invalid parameters (or no memory). */
+hl_sched* hl_sched_create(const hl_sched_params* params);
+void hl_sched_destroy(hl_sched* sched);
+/* Queue a request (arrival order = call order). HL_ERR_ARG for lengths < 1, HL_ERR_BLOCK if its
+ * lifetime needs more than max_blocks_per_seq blocks. *handle: its index. */
+int hl_sched_submit(hl_sched* sched, int32_t request_id, int32_t prompt_len,
+                    int32_t max_new_tokens, int32_t* handle);
+/* The next iteration's batch (possibly empty: num_seqs == 0). */
+int hl_sched_next(hl_sched* sched, hl_sched_batch* batch);
+/* After the iteration ran: next_tokens[s] (host, one per sequence of the last batch; read where
+ * emits[s] is 1) advance every sequence; finished requests (their outputs complete) free their
+ * blocks and are listed in finished_ids (optional, room for num_seqs) / *num_finished. */
+int hl_sched_complete(hl_sched* sched, const int32_t* next_tokens, int32_t* finished_ids,
+                      int32_t* num_finished);
+/* Queue sizes and free blocks (any pointer may be NULL). */
+int hl_sched_counts(const hl_sched* sched, int32_t* waiting, int32_t* prefilling,
+                    int32_t* decoding, int32_t* free_blocks);
+
 /* ---- KV transfer between instances ------------------------------------------------------ */
 
 /* One request's token span [start, start + count) of one layer, for the KV hand-off between a

@@ -22,6 +22,7 @@ import torch.nn.functional as F
 
 import oracle.kv_transfer as OKV
 import oracle.model as OM
+import oracle.scheduler as OS
 import oracle.layer as OL
 import workloads
 
@@ -471,6 +472,64 @@ def check_greedy_hand_values():
     assert list(OM.last_rows([(0, 3), (9, 1), (2, 5)])) == [2, 3, 8]
 
 
+# --------------------------------------------------------------------------- scheduler
+
+def check_scheduler_hand_trace():
+    """The hand-worked trace in tests/golden/scheduler_trace.txt (budget 8, 2 slots)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "scheduler_trace.txt")
+    want = [l.split(": ", 1)[1].strip() for l in open(path) if l[0].isdigit()]
+    s = OS.Scheduler(budget=8, max_seqs=2, num_blocks=40)
+    names = {0: "A", 1: "B", 2: "C"}
+    for rid, p, o in [(0, 10, 3), (1, 5, 1), (2, 3, 2)]:
+        s.submit(rid, p, o)
+    got = []
+    for it in range(len(want)):
+        b = s.next()
+        got.append(" ".join(f"{names[e['rid']]}:{e['num_cached']}+{e['q_len']}"
+                            f"{'*' if e['emits'] else ''}" for e in b))
+        s.complete([100 + it] * len(b))
+    assert got == want, got
+    assert len(s.free) == 40
+
+
+def check_scheduler_blocks_and_adaptive_budget():
+    """Blocks for the whole lifetime are taken at admission (lowest ids first) and come back at
+    the end; the adaptive budget is max_chunk with no decodes, min_chunk + decodes at the
+    threshold, and the linear rule in between (chapter 7.8's dynamic chunk sizing)."""
+    s = OS.Scheduler(budget=4, max_seqs=4, num_blocks=10)
+    s.submit(7, 20, 13)            # 32 tokens over its lifetime: 2 blocks
+    s.submit(8, 3, 1)              # 3 tokens: 1 block
+    b = s.next()
+    assert [e["blocks"] for e in b] == [[0, 1]] and len(s.free) == 8
+    # a decoding sequence holds its slot: with one slot, B waits until A has finished
+    one = OS.Scheduler(budget=8, max_seqs=1, num_blocks=10)
+    one.submit(0, 2, 3)
+    one.submit(1, 2, 1)
+    seen = []
+    for it in range(5):
+        b = one.next()
+        seen.append([e["rid"] for e in b])
+        one.complete([5] * len(b))
+    assert seen == [[0], [0], [0], [1], []], seen
+    # decode tokens count against the budget: the prompt in progress gets what they leave
+    tb = OS.Scheduler(budget=4, max_seqs=4, num_blocks=10)
+    tb.submit(0, 2, 3)
+    tb.submit(1, 10, 1)
+    b0 = tb.next()
+    assert [(e["rid"], e["q_len"]) for e in b0] == [(0, 2), (1, 2)]
+    tb.complete([9, 9])
+    b1 = tb.next()
+    assert [(e["rid"], e["num_cached"], e["q_len"]) for e in b1] == [(0, 2, 1), (1, 2, 3)]
+    a = OS.Scheduler(adaptive=True, max_seqs=64, num_blocks=10, min_chunk=128, base_chunk=512,
+                     max_chunk=4096, pressure_threshold=16)
+    assert a.chunk_budget() == 4096
+    a.running = [OS.Request(i, 1, 2) for i in range(16)]
+    assert a.chunk_budget() == 128 + 16
+    a.running = a.running[:4]
+    assert a.chunk_budget() == 512 - 96 + 4       # 512 - 4/16 * (512 - 128), plus 4 decodes
+
+
 ALL_CHECKS = [
     check_attention_bruteforce, check_attention_sdpa_library, check_attention_closed_forms,
     check_gqa_group_mapping, check_rope_hand_values, check_rope_complex_form_and_invariance,
@@ -479,5 +538,6 @@ ALL_CHECKS = [
     check_decode_equals_last_prefill_row, check_sampled_rows_match_full,
     check_block_permutation_addresses, check_kv_export_closed_form, check_kv_import_closed_form,
     check_kv_round_trip_across_tables, check_model_head_library_and_identity_stack,
-    check_model_stack_is_layer_by_layer, check_greedy_hand_values,
+    check_model_stack_is_layer_by_layer, check_greedy_hand_values, check_scheduler_hand_trace,
+    check_scheduler_blocks_and_adaptive_budget,
 ]

@@ -11,6 +11,7 @@ import pytest
 
 import oracle.kv_transfer as OKV
 import oracle.model as OM
+import oracle.scheduler as OS
 import oracle.layer as OL
 from tests import oracle_pins
 
@@ -105,3 +106,36 @@ def test_pins_catch_planted_model_mistake(monkeypatch, fn_name, old, new):
         except Exception:
             caught.append(check.__name__)
     assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
+
+
+# planted mistakes in the scheduler reference (methods of OS.Scheduler)
+SCHED_MUTANTS = [
+    ("next", "n = min(left, r.prompt_len - r.prefilled)", "n = min(left, r.prompt_len)"),
+    ("next", "if len(self.running) + len(self.prefilling) >= self.max_seqs:",
+     "if len(self.prefilling) >= self.max_seqs:"),
+    ("next", '"emits": 1 if dec or r.prefilled + n == r.prompt_len else 0',
+     '"emits": 1 if dec else 0'),
+    ("next", "left -= 1", "left -= 0"),
+    ("complete", "r.generated, r.last_token = 1, tok", "r.generated, r.last_token = 0, tok"),
+    ("chunk_budget", "return chunk + d", "return chunk"),
+]
+
+
+def _method_mutant(name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(OS.Scheduler, name)))
+    assert old in src, f"mutation site not found in Scheduler.{name}: {old!r}"
+    ns = dict(vars(OS))
+    exec(compile(src.replace(old, new, 1), f"<mutant Scheduler.{name}>", "exec"), ns)
+    return ns[name]
+
+
+@pytest.mark.parametrize("name,old,new", SCHED_MUTANTS, ids=[f"{m[0]}:{m[1][:24]}" for m in SCHED_MUTANTS])
+def test_pins_catch_planted_scheduler_mistake(monkeypatch, name, old, new):
+    monkeypatch.setattr(OS.Scheduler, name, _method_mutant(name, old, new))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception:
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the mutant Scheduler.{name}: {old!r} -> {new!r}"
