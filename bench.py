@@ -124,6 +124,22 @@ def main():
     ap.add_argument("--vocab", type=int, default=0,
                     help="vocabulary of --model-layers (default: 151936 for the Qwen3 shapes, "
                          "128256 for the 70B shape)")
+    ap.add_argument("--serve", default=None, choices=["replay", "chunks", "cliff"],
+                    help="serving experiments with the native scheduler driving hl_model_step: "
+                         "replay = Poisson arrivals through the token-budget scheduler, step times "
+                         "against the step-time model; chunks = one 8192-token prompt in chunks of "
+                         "128..8192; cliff = prefill steps at chunk sizes around tile multiples")
+    ap.add_argument("--rate", type=float, default=40.0,
+                    help="--serve replay: request arrival rate (requests per second)")
+    ap.add_argument("--requests", type=int, default=200, help="--serve replay: requests")
+    ap.add_argument("--mean-output", type=int, default=64,
+                    help="--serve replay: mean output length (tokens)")
+    ap.add_argument("--budgets", type=int, nargs="+", default=[512, 2048, 8192],
+                    help="--serve replay: token budgets to replay")
+    ap.add_argument("--chunks", type=int, nargs="+", default=[4096, 2048, 1024, 512, 256, 128],
+                    help="--serve chunks: chunk sizes to compare with the one-shot prefill")
+    ap.add_argument("--kv-blocks", type=int, default=16384,
+                    help="--serve replay: KV blocks per layer (16 tokens each)")
     ap.add_argument("--graph", action="store_true",
                     help="with --model-layers: capture the iteration in a HIP graph and time replays")
     ap.add_argument("--phase-reps", type=int, default=20)
@@ -167,6 +183,8 @@ def main():
                           "reps": args.phase_reps}), flush=True)
         return
     name = args.workload
+    if args.serve:
+        return serve_bench(args, dev)
     spec = workloads.named_spec(name)
     if args.model_layers > 0:
         return model_bench(args, spec, dev)
@@ -421,6 +439,169 @@ def model_bench(args, spec, dev):
         "layers": L, "vocab": vocab, "graph": bool(args.graph), "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the workload's layer shape)",
         "config": {"workload": workloads.describe(spec), "parallelism": "none (1 GPU)"},
+    }), flush=True)
+
+
+def serve_bench(args, dev):
+    """Serving experiments with the native scheduler driving hl_model_step; one JSON line each.
+    Random-init weights of the Qwen3-8B layer shape, synthetic requests."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from hybrid_prefill_decode_amd import binding as B
+    from hybrid_prefill_decode_amd import serving as SV
+
+    shape = workloads.SHAPES["qwen3_8b"]
+    vocab = args.vocab or 151936
+
+    def qs(v, p):
+        return round(float(np.percentile(v, p)), 2) if len(v) else None
+
+    if args.serve == "replay":
+        L = args.model_layers or 8
+        rng = np.random.default_rng(11)
+        n_req = args.requests
+        # Poisson arrivals, lognormal prompt lengths (mean 1000, at most 8192) and output lengths
+        # (mean 250 on the page; --mean-output shortens them to bound the run time)
+        sig = 1.0
+        prompts = np.clip(rng.lognormal(np.log(1000) - sig * sig / 2, sig, n_req), 16, 8192)
+        outs = np.clip(rng.lognormal(np.log(args.mean_output) - sig * sig / 2, sig, n_req), 1,
+                       4 * args.mean_output)
+        prompts, outs = prompts.astype(int), outs.astype(int)
+        arrive = np.cumsum(rng.exponential(1000.0 / args.rate, n_req))  # ms
+        mbs = (8192 + 4 * args.mean_output + 15) // 16 + 1
+        eng = SV.Engine(shape, L, vocab, num_blocks=args.kv_blocks, max_blocks_per_seq=mbs,
+                        device=dev, budget=args.budgets[0], max_seqs=256)
+        kw = dict(layer_params=L * shape.weight_params, head_params=vocab * shape.hidden,
+                  hidden=shape.hidden, layers=L,
+                  kv_bytes_per_token=2 * L * shape.n_kv_heads * shape.head_dim * 2)
+        for budget in args.budgets:
+            eng.reset(budget=budget, max_seqs=256)
+            clock, k, recs = 0.0, 0, []
+            first, last, itl = {}, {}, []
+            wall = time.perf_counter()
+            while True:
+                while k < n_req and arrive[k] <= clock:
+                    eng.submit(k, int(prompts[k]), int(outs[k]))
+                    k += 1
+                r = eng.step()
+                if r is None:
+                    if k == n_req:
+                        break
+                    clock = float(arrive[k])
+                    continue
+                clock += r.ms
+                recs.append(r)
+                if len(recs) % 500 == 0:
+                    print(f"# budget {budget}: {len(recs)} iterations, {k} arrived, "
+                          f"clock {clock:.0f} ms", file=sys.stderr, flush=True)
+                for rid in r.emitted:
+                    if rid in last:
+                        itl.append(clock - last[rid])
+                    else:
+                        first[rid] = clock - arrive[rid]
+                    last[rid] = clock
+            ms = np.array([r.ms for r in recs])
+            fit_o = SV.fit_step_model(recs, overlap=True, **kw)
+            fit_p = SV.fit_step_model(recs, overlap=False, **kw)
+            emitted = sum(len(r.emitted) for r in recs)
+            print(json.dumps({
+                "experiment": "serve_replay", "layers": L, "budget": budget, "requests": n_req,
+                "arrival_rate_per_s": args.rate, "mean_output": args.mean_output,
+                "iterations": len(recs), "gpu_busy_s": round(float(ms.sum()) / 1e3, 3),
+                "span_s": round(clock / 1e3, 3),
+                "output_tokens_per_s": round(emitted / (clock / 1e3), 1),
+                "step_ms": {"p50": qs(ms, 50), "p99": qs(ms, 99), "max": qs(ms, 100)},
+                "ttft_ms": {"p50": qs(list(first.values()), 50),
+                            "p99": qs(list(first.values()), 99)},
+                "itl_ms": {"p50": qs(itl, 50), "p99": qs(itl, 99), "max": qs(itl, 100)},
+                "step_model_fit_overlap": fit_o, "step_model_fit_serial": fit_p,
+                "wall_s": round(time.perf_counter() - wall, 1),
+                "data": "synthetic: Poisson arrivals, lognormal lengths, random-init weights",
+            }), flush=True)
+        return
+
+    if args.serve == "chunks":
+        L = args.model_layers or 36
+        prompt = 8192
+        eng = SV.Engine(shape, L, vocab, num_blocks=prompt // 16 + 8,
+                        max_blocks_per_seq=prompt // 16 + 2, device=dev, budget=prompt,
+                        max_seqs=4)
+        res = {}
+        for chunk in [prompt] + [c for c in args.chunks if c != prompt]:
+            for rep in range(2):  # the first pass loads this chunk size's kernels
+                eng.reset(budget=chunk, max_seqs=4)
+                eng.submit(0, prompt, 1)
+                recs = []
+                while True:
+                    r = eng.step()
+                    if r is None:
+                        break
+                    recs.append(r)
+            res[chunk] = recs
+            print(f"# chunk {chunk}: {len(recs)} iterations, {sum(r.ms for r in recs):.2f} ms",
+                  file=sys.stderr, flush=True)
+        one = sum(r.ms for r in res[prompt])
+        total = {c: sum(r.ms for r in v) for c, v in res.items()}
+        print(json.dumps({
+            "experiment": "chunked_prefill_overhead", "layers": L, "prompt": prompt,
+            "total_ms": {str(c): round(t, 2) for c, t in total.items()},
+            "iterations": {str(c): len(v) for c, v in res.items()},
+            "overhead_vs_one_shot": {str(c): round(t / one - 1.0, 4) for c, t in total.items()},
+            "data": "one synthetic prompt, random-init weights of the Qwen3-8B shape",
+        }), flush=True)
+        return
+
+    # cliff: one prompt chunk at prefix 0 for sizes at and just past tile multiples, whole model
+    # iteration, and the gate/up GEMM alone with the per-launch tile choice vs a fixed 256x256 tile
+    L = args.model_layers or 36
+    eng = SV.Engine(shape, L, vocab, num_blocks=160, max_blocks_per_seq=140, device=dev,
+                    budget=4096, max_seqs=1)
+    sizes = (256, 257, 512, 513, 1024, 1025, 2048, 2049)
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    step, g_choice, g_fixed, choice = {}, {}, {}, {}
+    w = eng.layer_w[0]["w_gate_up"]
+    for c in sizes:
+        table = np.arange(140, dtype=np.int32)[None, :]
+        batch = B.Batch(np.array([0, c], np.int32), np.array([0], np.int32), table, dev)
+        toks = (np.arange(c) * 7919 % vocab).astype(np.int32)
+        tk = torch.from_numpy(toks).to(dev)
+        ws = B.alloc_model_workspace(eng.cfg, batch, eng.model, dev)
+        step[c] = timed(lambda: B.model_step(eng.cfg, batch, eng.model, tk, toks,
+                                             eng.logits[:1], eng.next[:1], ws))
+        a = torch.randn(c, shape.hidden, device=dev).to(torch.bfloat16)
+        out = torch.empty(c, w.shape[0], dtype=torch.bfloat16, device=dev)
+        gws = torch.empty(B.gemm_workspace_bytes(c, w.shape[0], shape.hidden), dtype=torch.uint8,
+                          device=dev)
+        g_choice[c] = timed(lambda: B.gemm_bf16_nt(a, w, out, workspace=gws))
+        g_fixed[c] = timed(lambda: B.gemm_bf16_nt_tiled(a, w, out, 256, 256))
+        choice[c] = B.gemm_tile_choice(c, w.shape[0], shape.hidden)
+        print(f"# cliff {c}: step {step[c]:.3f} ms, gate/up {g_choice[c]:.4f} ms "
+              f"(fixed 256x256 {g_fixed[c]:.4f} ms)", file=sys.stderr, flush=True)
+    ratio = lambda d: {f"{c + 1}/{c}": round(d[c + 1] / d[c], 4) for c in sizes[::2]}
+    print(json.dumps({
+        "experiment": "tile_quantisation_cliff", "layers": L,
+        "model_step_ms": {str(c): round(v, 3) for c, v in step.items()},
+        "model_step_ratio": ratio(step),
+        "gate_up_gemm_ms": {str(c): round(v, 4) for c, v in g_choice.items()},
+        "gate_up_gemm_ratio": ratio(g_choice),
+        "gate_up_tile_choice": {str(c): list(v) if isinstance(v, tuple) else v
+                                for c, v in choice.items()},
+        "gate_up_fixed_256x256_ms": {str(c): round(v, 4) for c, v in g_fixed.items()},
+        "gate_up_fixed_256x256_ratio": ratio(g_fixed),
+        "data": "one synthetic prompt chunk, random-init weights of the Qwen3-8B shape",
     }), flush=True)
 
 
