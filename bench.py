@@ -15,6 +15,7 @@ oracle timed on the host cores as a baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -60,7 +61,7 @@ def pct(v):
         return None
     q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
     return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4),
-            "n": len(v)}
+            "max": round(v[-1], 4), "n": len(v)}
 
 
 def gpu_clocks():
@@ -213,8 +214,12 @@ def main():
         torch.cuda.synchronize()
     else:
         args.steps = 0
-    # K timed steps back to back; an event after every step gives the per-step distribution
+    # K timed steps back to back; an event after every step gives the per-step distribution.
+    # The collector stays off meanwhile: a collection pause of the launching thread leaves the
+    # GPU idle between steps once the queued work runs out.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     evs[0].record(stream)
@@ -223,6 +228,7 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    gc.enable()
     ms_step = evs[0].elapsed_time(evs[-1]) / max(args.steps, 1)
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     clocks = gpu_clocks() if args.only_phase is None else None

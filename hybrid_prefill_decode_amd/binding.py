@@ -96,6 +96,7 @@ _SIGS = {
     "hl_version": ([], ctypes.c_int),
     "hl_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "hl_workspace_bytes": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "hl_attention_plan": ([ctypes.POINTER(BatchDesc)] + [_c_i32p] * 6, ctypes.c_int),
     "hybrid_layer_step": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(Weights),
                            ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable), ctypes.c_void_p],
                           ctypes.c_int),
@@ -359,6 +360,17 @@ def workspace_bytes(cfg: LayerCfg, b: Batch) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().hl_workspace_bytes(ctypes.byref(d), ctypes.byref(n)), "hl_workspace_bytes")
     return int(n.value)
+
+
+def attention_plan(cfg: LayerCfg, b: Batch) -> Dict[str, int]:
+    """hl_attention_plan: how the batch's attention work is laid out (host-only)."""
+    d = _desc(cfg, b, with_stream=False)
+    v = [ctypes.c_int32(0) for _ in range(6)]
+    _check(lib().hl_attention_plan(ctypes.byref(d), *[ctypes.byref(x) for x in v]),
+           "hl_attention_plan")
+    keys = ("fused", "split_pages", "decode_units", "prefill_parts", "prefill_split",
+            "prefill_merges")
+    return {k: x.value for k, x in zip(keys, v)}
 
 
 def alloc_workspace(cfg: LayerCfg, b: Batch, device="cuda"):

@@ -26,9 +26,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 struct HostPlan {
   int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
+  int32_t n_pre_merge = 0, n_pre_slots = 0, pre_split = 1 << 30;
   bool fused = false;  // prefill and decode attention in one launch
   // workspace byte offsets
-  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_counters = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
+  size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_pre_merge = 0, o_pre_po = 0,
+         o_pre_ml = 0, o_counters = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
          o_blk = 0, o_cs = 0, o_qlo = 0, o_qrot = 0, o_attn = 0, o_h2 = 0, o_mlp = 0, o_part = 0,
          o_gemm = 0, total = 0;
   size_t gemm_bytes = 0;
@@ -180,6 +182,34 @@ int pick_split_fused(const hl_batch_desc* b) {
   return (int)sp;
 }
 
+// Key tiles per prefill work part. Items are (tile or part, query head), two resident per compute
+// unit; an item's time is a start-up (query load, pipeline fill) plus one step per key tile.
+// Whole tiles are kept whenever the batch has at least one item per compute unit: equalising
+// uneven tiles by splitting them was measured slower there (the start-up, the partial write and
+// the merge outweigh the shorter tail). With fewer items — a short chunk after a long cached
+// prefix has only Hq — most compute units would idle, so tiles are cut into near-equal parts
+// sized to give every slot about one part, never below kMinPart key tiles. The choice depends on
+// the batch only, so the fused and the separate launches run the same parts and stay
+// bit-identical.
+int pick_pre_split(const hl_batch_desc* b) {
+  constexpr int64_t kMinPart = 8;
+  int64_t work = 0, longest = 0, tiles = 0;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    const int n = b->h_q_start[s + 1] - b->h_q_start[s], c = b->h_num_cached[s];
+    if (n < 2) continue;
+    for (int r0 = 0; r0 < n; r0 += hl::kPrefillQTile) {
+      const int64_t k = hl::prefill_key_tiles(c, r0, std::min(hl::kPrefillQTile, n - r0));
+      work += k;
+      longest = std::max(longest, k);
+      ++tiles;
+    }
+  }
+  const int64_t hq = b->cfg->n_q_heads, cus = device_cus();
+  if (tiles * hq >= cus) return 1 << 30;
+  const int64_t split = std::max<int64_t>(kMinPart, (work * hq + 2 * cus - 1) / (2 * cus));
+  return split >= longest ? 1 << 30 : (int)split;
+}
+
 void make_plan(const hl_batch_desc* b, HostPlan* p) {
   const hl_layer_cfg& c = *b->cfg;
   *p = HostPlan{};
@@ -198,6 +228,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
   p->fused = pre_flops > 0 && dec_bytes > 0 &&
              (pre_us >= 0.5 * dec_us || (dec_us >= 1000.0 && pre_us >= 0.02 * dec_us));
   p->split_pages = p->fused ? pick_split_fused(b) : pick_split(b);
+  p->pre_split = pick_pre_split(b);
   for (int s = 0; s < b->num_seqs; ++s) {
     const int qlen = b->h_q_start[s + 1] - b->h_q_start[s];
     if (qlen == 1) {
@@ -205,7 +236,17 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
       p->n_dec_units += (pages + p->split_pages - 1) / p->split_pages;
       p->n_dec_seqs += 1;
     } else {
-      p->n_pre_tiles += (qlen + hl::kPrefillQTile - 1) / hl::kPrefillQTile;
+      // the plan kernel's count of entries, partial slots and merges (same functions)
+      for (int r0 = 0; r0 < qlen; r0 += hl::kPrefillQTile) {
+        const int parts = hl::prefill_parts(
+            hl::prefill_key_tiles(b->h_num_cached[s], r0, std::min(hl::kPrefillQTile, qlen - r0)),
+            p->pre_split);
+        p->n_pre_tiles += parts;
+        if (parts > 1) {
+          p->n_pre_slots += parts;
+          p->n_pre_merge += 1;
+        }
+      }
     }
   }
   const size_t T = (size_t)b->num_tokens;
@@ -220,7 +261,11 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
   p->o_counters = take(sizeof(int32_t) * hl::kPlanCounters * hl::kCounterStride);
   p->o_dec_units = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_units);
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
-  p->o_pre_tiles = take(sizeof(int32_t) * 2 * (size_t)p->n_pre_tiles);
+  p->o_pre_tiles = take(sizeof(int32_t) * hl::kPreEntry * (size_t)p->n_pre_tiles);
+  p->o_pre_merge = take(sizeof(int32_t) * 4 * (size_t)p->n_pre_merge);
+  const size_t pre_rows = (size_t)p->n_pre_slots * c.n_q_heads * hl::kPrefillQTile;
+  p->o_pre_po = take(sizeof(float) * pre_rows * c.head_dim);
+  p->o_pre_ml = take(sizeof(float) * 2 * pre_rows);
   p->o_h1 = take(2 * T * c.hidden);
   p->o_rs = take(4 * T);
   p->o_pos = take(4 * T);
@@ -243,13 +288,17 @@ hl::Plan device_plan(const HostPlan& hp, void* ws) {
   p.dec_units = reinterpret_cast<int32_t*>(base + hp.o_dec_units);
   p.dec_seqs = reinterpret_cast<int32_t*>(base + hp.o_dec_seqs);
   p.pre_tiles = reinterpret_cast<int32_t*>(base + hp.o_pre_tiles);
+  p.pre_merge = reinterpret_cast<int32_t*>(base + hp.o_pre_merge);
+  p.pre_part_o = reinterpret_cast<float*>(base + hp.o_pre_po);
+  p.pre_part_ml = reinterpret_cast<float2*>(base + hp.o_pre_ml);
   p.dec_part = reinterpret_cast<float*>(base + hp.o_part);
   p.counters = reinterpret_cast<int32_t*>(base + hp.o_counters);
   p.n_dec_units = hp.n_dec_units;
   p.n_dec_seqs = hp.n_dec_seqs;
   p.n_pre_tiles = hp.n_pre_tiles;
+  p.n_pre_merge = hp.n_pre_merge;
   p.split_pages = hp.split_pages;
-  p.max_pre_kv = 0;
+  p.pre_split = hp.pre_split;
   return p;
 }
 
@@ -339,8 +388,7 @@ int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q
                   const HostPlan& hp, bool do_prefill, bool do_decode) {
   hipStream_t st = static_cast<hipStream_t>(b->stream);
   const hl::Plan dp = device_plan(hp, b->workspace);
-  int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, hp.split_pages,
-                                  hl::kPrefillQTile, dp, st));
+  int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, dp, st));
   if (rc) return rc;
   if (do_prefill && do_decode && hp.fused) {
     // both paths in one fused launch: prefill and decode overlap on every compute unit
@@ -438,6 +486,25 @@ const char* hl_strerror(int code) {
     case HL_ERR_ARG: return "invalid argument";
     default: return "unknown error code";
   }
+}
+
+int hl_attention_plan(const hl_batch_desc* batch, int32_t* fused, int32_t* split_pages,
+                      int32_t* decode_units, int32_t* prefill_parts, int32_t* prefill_split,
+                      int32_t* prefill_merges) {
+  if (!fused || !split_pages || !decode_units || !prefill_parts || !prefill_split ||
+      !prefill_merges)
+    return HL_ERR_NULL;
+  int rc = check_batch(batch);
+  if (rc) return rc;
+  HostPlan hp;
+  if (batch->num_seqs > 0) make_plan(batch, &hp);
+  *fused = hp.fused ? 1 : 0;
+  *split_pages = hp.split_pages;
+  *decode_units = hp.n_dec_units;
+  *prefill_parts = hp.n_pre_tiles;
+  *prefill_split = hp.pre_split;
+  *prefill_merges = hp.n_pre_merge;
+  return HL_OK;
 }
 
 int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes) {

@@ -21,8 +21,8 @@
 // the other kind, and exits once every queue is empty. A queue is read before it is incremented,
 // so drained queues cost no atomic. (One shared decode counter serialised every claim at one
 // memory location: with a few hundred workers that cost tens of microseconds per launch.)
-// Each item runs the same code as in the separate kernels, so the results are bit-identical to
-// theirs.
+// Each item runs the same code as in the separate kernels (and the same merges follow), so the
+// results are bit-identical to theirs.
 #include "attn_decode_core.h"
 #include "attn_prefill_core.h"
 
@@ -197,7 +197,7 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   const float scale_log2 = scale * 1.4426950408889634f;
   const PrefillArgs pa{q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
                        max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       attn_out};
+                       attn_out, plan.pre_part_o, plan.pre_part_ml};
   const decode::DecodeArgs da{q_start,        num_cached,     q_rot,          q_lo,
                               kpool,          vpool,          (long long)num_blocks, table,
                               max_blocks,     plan.dec_units, plan.dec_seqs,  plan.split_pages,
@@ -206,8 +206,9 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   hipError_t e = cfg.head_dim == 128
                      ? launch<128>(pa, da, plan.counters, n_pre_items, n_dec_items, cus, st)
                      : launch<64>(pa, da, plan.counters, n_pre_items, n_dec_items, cus, st);
-  if (e != hipSuccess || n_dec_items == 0) return e;
-  return launch_decode_merge(cfg, q_start, plan, attn_out, st);
+  if (e == hipSuccess && n_dec_items > 0) e = launch_decode_merge(cfg, q_start, plan, attn_out, st);
+  if (e == hipSuccess && n_pre_items > 0) e = launch_prefill_merge(cfg, q_start, plan, attn_out, st);
+  return e;
 }
 
 }  // namespace hl

@@ -1,6 +1,6 @@
-// One ragged causal prefill work item (128 query rows of one sequence, one query head), shared
-// by the standalone prefill-attention kernel and the fused hybrid-attention kernel. The method and
-// the design are described in attention_prefill.hip.
+// One ragged causal prefill work item (128 query rows of one sequence, one query head, a range of
+// its key tiles), shared by the standalone prefill-attention kernel and the fused hybrid-attention
+// kernel. The method and the design are described in attention_prefill.hip.
 #pragma once
 #include <type_traits>
 
@@ -11,7 +11,8 @@ namespace prefill {
 
 
 constexpr int kThreads = 256;
-constexpr int kKeys = 64;  // keys per step = 4 pages
+constexpr int kKeys = kPrefillKeyTile;  // keys per step = 4 pages
+static_assert(kKeys == 64 && kPrefillQTile == 128, "the item's tiling");
 
 template <int D>
 struct PrefillSmem {
@@ -48,15 +49,21 @@ struct PrefillArgs {
   long long num_blocks;
   const int32_t* table;
   int max_blocks;
-  const int32_t* tiles;  // [n][2]: (sequence, first query row of the tile)
+  const int32_t* tiles;  // [n][kPreEntry]: (sequence, first query row, key tiles [kt0, kt1),
+                         // partial slot or -1)
   int Hq, Hkv;
   float scale_log2;
   hl_bf16* attn_out;
+  float* part_o;         // [slot][Hq][128][D]: unnormalised o of a part
+  float2* part_ml;       // [slot][Hq][128]: (m, l) of a part, m in the exp2 domain
 };
 
-// Work item (tile, query head h). Every thread of a kThreads-thread workgroup calls it; `smem`
-// holds PrefillSmem<D>::kTotal bytes. Consecutive items of one workgroup must be separated by a
-// barrier (the LDS stages are reused).
+// Work item (entry, query head h): the entry's query rows against its key tiles [kt0, kt1). An
+// entry that covers the tile's whole key range writes the normalised rows; a part of a split tile
+// writes its unnormalised o and its (m, l) to slot `slot`, and a merge pass combines the parts.
+// Every thread of a kThreads-thread workgroup calls it; `smem` holds PrefillSmem<D>::kTotal
+// bytes. Consecutive items of one workgroup must be separated by a barrier (the LDS stages are
+// reused).
 template <int D>
 HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
   using SM = PrefillSmem<D>;
@@ -71,14 +78,14 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
   const float scale_log2 = a.scale_log2;
   hl_bf16* __restrict__ attn_out = a.attn_out;
   const int g = Hq / Hkv;
-  const int s = a.tiles[2 * tile], r0 = a.tiles[2 * tile + 1];
+  const int32_t* ent = a.tiles + (size_t)kPreEntry * tile;
+  const int s = ent[0], r0 = ent[1], kt0 = ent[2], kt1 = ent[3], slot = ent[4];
   const int qs = q_start[s], n = q_start[s + 1] - qs, c = num_cached[s];
   const int kvh = h / g;
   const int kv_len = c + n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl32 = lane >> 5;
   const int tile_rows = min(128, n - r0);
-  const int key_end = c + r0 + tile_rows;  // exclusive key bound of the whole tile
-  const int nkt = (key_end + kKeys - 1) / kKeys;
+  const int nkt = prefill_key_tiles(c, r0, tile_rows);  // key tiles of the whole tile
   const int wr0 = r0 + 32 * wave;
   const int my_row = wr0 + (lane & 31);
   const bool row_ok = my_row < n;
@@ -173,9 +180,9 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     const uint8_t* vb = kb + SM::kKBytes;
     // the next tile into the other buffer (last read one step ago, before the barrier), then
     // the loads of the two tiles after it (past the end they repeat the last tile, unused)
-    sstore(buf ^ 1, min(kt + 1, nkt - 1), masked);
+    sstore(buf ^ 1, min(kt + 1, kt1 - 1), masked);
     gload();
-    tload(min(kt + 3, nkt - 1));
+    tload(min(kt + 3, kt1 - 1));
     // S^T for the two 32-key halves of the tile; half hb holds keys
     // 32 hb + 8 (i / 4) + 4 hl32 + (i & 3) of query lane & 31
     f32x16 st[2] = {f32x16{}, f32x16{}};
@@ -249,22 +256,39 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     __syncthreads();
   };
 
-  tload(0);
+  tload(kt0);
   gload();
-  tload(min(1, nkt - 1));
-  sstore(0, 0, std::true_type{});
+  tload(min(kt0 + 1, kt1 - 1));
+  sstore(kt0 & 1, kt0, std::true_type{});
   gload();
-  tload(min(2, nkt - 1));
+  tload(min(kt0 + 2, kt1 - 1));
   __syncthreads();
   // Tiles wholly at or below the tile's first query position need neither the mask nor V
-  // zeroing; the step before the first tile that needs them already stores it, so runs masked.
+  // zeroing (only the last of the tile's key tiles holds rows past the sequence end); the step
+  // before the first tile that needs them already stores it, so runs masked.
   const int kt_m = (c + r0 + 1) / kKeys;
   const int kt_a = max(0, min(kt_m - 1, nkt));
-  for (int kt = 0; kt < kt_a; ++kt) step(kt, std::false_type{});
-  for (int kt = kt_a; kt < nkt; ++kt) step(kt, std::true_type{});
+  for (int kt = kt0; kt < min(kt_a, kt1); ++kt) step(kt, std::false_type{});
+  for (int kt = max(kt0, kt_a); kt < kt1; ++kt) step(kt, std::true_type{});
 
   if (!row_ok) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (slot >= 0) {
+    // a part: o relative to 2^m_run, its weight sum and m_run (rows with no key in this part
+    // keep m_run = -1e30, l = 0, o = 0 and drop out of the merge)
+    const size_t prow = ((size_t)slot * Hq + h) * kPrefillQTile + (my_row - r0);
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * mt + 8 * g4 + 4 * hl32;
+        *reinterpret_cast<f32x4*>(po + d0) =
+            f32x4{o[mt][4 * g4], o[mt][4 * g4 + 1], o[mt][4 * g4 + 2], o[mt][4 * g4 + 3]};
+      }
+    if (hl32 == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
+    return;
+  }
   const float inv = 1.f / l_tot;
   hl_bf16* op = attn_out + ((size_t)(qs + my_row) * Hq + h) * D;
 #pragma unroll

@@ -52,17 +52,35 @@ HL_DEV float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64
 // Internal launchers (each returns hipSuccess or the launch error).
 namespace hl {
 
+constexpr int kPrefillQTile = 128;   // query rows per prefill work tile
+constexpr int kPrefillKeyTile = 64;  // keys per step of a prefill work item
+constexpr int kPreEntry = 5;         // ints per prefill work entry (see Plan::pre_tiles)
+
+// Key tiles a prefill tile of `rows` query rows from row r0 of a chunk after c cached tokens
+// reads (causal: up to its last row's position), and the parts it is split into when a part
+// holds at most `split` key tiles. Host and plan kernel count work with these same functions.
+__host__ __device__ inline int prefill_key_tiles(int c, int r0, int rows) {
+  return (c + r0 + rows + kPrefillKeyTile - 1) / kPrefillKeyTile;
+}
+__host__ __device__ inline int prefill_parts(int key_tiles, int split) {
+  return (key_tiles + split - 1) / split;
+}
+
 struct Plan {
   // device work lists inside the workspace
   int32_t* dec_units;      // [n_dec_units][3]: (seq, first page, decode index)
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
-  int32_t* pre_tiles;      // [n_pre_tiles][2]: (seq, first query row within the sequence)
+  int32_t* pre_tiles;      // [n_pre_tiles][kPreEntry]: (seq, first query row within the sequence,
+                           // first key tile, end key tile, partial slot or -1 if unsplit)
+  int32_t* pre_merge;      // [n_pre_merge][4]: (seq, first query row, first slot, part count)
   float* dec_part;         // [n_dec_units][Hkv][group][head_dim + 2] partial (o, m, l)
+  float* pre_part_o;       // [slots][Hq][kPrefillQTile][head_dim] unnormalised partial o
+  float2* pre_part_ml;     // [slots][Hq][kPrefillQTile] partial (m, l)
   int32_t* counters;       // [kPlanCounters][kCounterStride] work-queue counters of the fused
                            // attention kernel (one per 256-byte line), zeroed by the plan kernel
-  int32_t n_dec_units, n_dec_seqs, n_pre_tiles;
+  int32_t n_dec_units, n_dec_seqs, n_pre_tiles, n_pre_merge;
   int32_t split_pages;     // pages per decode work unit
-  int32_t max_pre_kv;      // longest key range of any prefill tile (host-side estimate)
+  int32_t pre_split;       // key tiles per prefill work part
 };
 
 // Per-token data of one step (filled by the first prep pass, read by the QKV GEMM epilogue).
@@ -102,7 +120,7 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
                        int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
                        hipStream_t st);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
-                       int32_t split_pages, int32_t q_tile, const Plan& plan, hipStream_t st);
+                       const Plan& plan, hipStream_t st);
 constexpr int kPlanCounters = 16;
 constexpr int kCounterStride = 64;  // int32 slots per counter: each on its own 256-byte line
 constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
@@ -147,6 +165,8 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
 
 hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, const Plan& plan,
                                hl_bf16* attn_out, hipStream_t st);
+hipError_t launch_prefill_merge(const hl_layer_cfg& cfg, const int32_t* q_start, const Plan& plan,
+                                hl_bf16* attn_out, hipStream_t st);
 // Prefill and decode attention of one batch in a single launch (plus the decode merge); `cus`
 // is the device's compute-unit count.
 hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
@@ -155,8 +175,6 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
                                    const hl_bf16* vpool, int64_t num_blocks, const int32_t* table,
                                    int32_t max_blocks, const Plan& plan, int32_t cus,
                                    hl_bf16* attn_out, hipStream_t st);
-
-constexpr int kPrefillQTile = 128;  // query rows per prefill work tile
 
 // Model-level kernels (model.hip).
 hipError_t launch_embed(const int32_t* tokens, const hl_bf16* table, hl_bf16* x, int T, int H,

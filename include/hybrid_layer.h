@@ -159,6 +159,21 @@ int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* weights, hl_
  * Writes the byte count to *bytes. */
 int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes);
 
+/* How the attention of this batch is laid out (host-only, from the host mirrors; no GPU needed),
+ * for tuning and tests. Work splits follow from the batch alone ("Chunked prefill (stall-free
+ * batching), explained", "How it works, step by step": a chunk attends to its cached prefix plus
+ * itself; decode attention is split over the KV length). Outputs:
+ *   fused          1 if prefill and decode attention run in one launch, else 0;
+ *   split_pages    KV pages per decode work unit;
+ *   decode_units   decode work units (each covers all KV heads);
+ *   prefill_parts  prefill work entries: 128-query-row tiles, or parts of a tile's key range;
+ *   prefill_split  key tiles (64 keys) per part, or 2^30 when no tile is split;
+ *   prefill_merges tiles whose parts are merged by the merge pass.
+ * Errors: HL_ERR_NULL, and those of hl_workspace_bytes. */
+int hl_attention_plan(const hl_batch_desc* batch, int32_t* fused, int32_t* split_pages,
+                      int32_t* decode_units, int32_t* prefill_parts, int32_t* prefill_split,
+                      int32_t* prefill_merges);
+
 /* Static text for an HL_* code; never NULL. */
 const char* hl_strerror(int code);
 

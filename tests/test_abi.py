@@ -259,3 +259,54 @@ def test_kv_span_argument_checks():
         assert f(span(count=0)) == B.HL_OK                       # empty span: nothing launched
         # a span whose pages are all valid is accepted up to the launch (which fails here: no GPU)
         assert f(span(table=np.array([3, 9, 7], dtype=np.int32), start=0, count=16)) == B.HL_ERR_HIP
+
+
+def _plan(shape, seqs):
+    spec = workloads.custom_spec(shape, seqs, seed=1)
+    table, _ = workloads.block_table(spec)
+    return B.attention_plan(B.layer_cfg(shape), B.Batch(spec.q_start, spec.num_cached, table,
+                                                       device="cpu"))
+
+
+def _key_tiles(c, n):
+    return [(c + r0 + min(128, n - r0) + 63) // 64 for r0 in range(0, n, 128)]
+
+
+@pytest.mark.parametrize("name,shape,seqs,splits", [
+    # a short chunk after a long prefix: one tile, a long key range -> split
+    ("chunk128_at_8064", "qwen3_8b", [(8064, 128)], True),
+    # a causal chunk alone with fewer tiles x heads than compute units: its long tiles split
+    ("causal_1000_d128", "small_d128", [(0, 1000)], True),
+    # config 2's 1024-token chunk: 8 tiles x 32 heads, one item per compute unit -> whole tiles
+    ("cfg2", "qwen3_8b", [(0, 1024)] + [(8192, 1)] * 16, False),
+    # config 3's 2048-token chunk at 16K: 640 even items fill the launch -> whole tiles
+    ("cfg3", "qwen3_14b", [(16384, 2048)] + [(3000, 1)] * 96, False),
+    ("tiny_chunk", "tiny", [(64, 64), (32, 1)], False),
+])
+def test_attention_plan_prefill_parts(name, shape, seqs, splits):
+    """Prefill tiles are cut into parts only where a few long tiles would idle the launch; the
+    counts agree with the parts the split size implies (host-only)."""
+    shape = workloads.LayerShape(1024, 8, 2, 128, 512) if shape == "small_d128" else \
+        workloads.SHAPES[shape]
+    p = _plan(shape, seqs)
+    tiles = [k for c, n in seqs if n > 1 for k in _key_tiles(c, n)]
+    split = p["prefill_split"]
+    parts = [-(-k // split) for k in tiles]
+    assert p["prefill_parts"] == sum(parts)
+    assert p["prefill_merges"] == sum(1 for q in parts if q > 1)
+    assert (p["prefill_merges"] > 0) == splits, p
+    if splits:
+        assert 8 <= split < max(tiles)
+    else:
+        assert split >= max(tiles) and p["prefill_parts"] == len(tiles)
+
+
+def test_attention_plan_argument_checks():
+    spec, b, _ = _fake_batch([(3, 1)])
+    d = B._desc(B.layer_cfg(spec.shape), b, with_stream=False)
+    v = [ctypes.c_int32(0) for _ in range(6)]
+    assert B.lib().hl_attention_plan(ctypes.byref(d), *[ctypes.byref(x) for x in v[:5]],
+                                     None) == B.HL_ERR_NULL
+    assert B.lib().hl_attention_plan(None, *[ctypes.byref(x) for x in v]) == B.HL_ERR_NULL
+    p = _plan(workloads.SHAPES["tiny"], [])
+    assert p["prefill_parts"] == 0 and p["decode_units"] == 0

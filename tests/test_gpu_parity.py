@@ -319,6 +319,11 @@ ATTN_CASES = {
     "many_decodes": (workloads.SHAPES["tiny"], [(7, 200)] + [(17 * i % 1500, 1) for i in range(300)]),
     "many_prefill": (workloads.LayerShape(1280, 10, 2, 128, 512),
                      [(64 * i, 257 + 31 * i) for i in range(6)] + [(900, 1), (3, 1)]),
+    # prefill tiles cut into key-range parts and merged: a short chunk after a long prefix, a
+    # d = 128 chunk with a ragged last tile, a causal chunk alone (its last tiles are the longest)
+    "split_long_prefix": (workloads.SHAPES["tiny"], [(3000, 100), (2500, 1), (40, 1)]),
+    "split_d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(5000, 200), (70, 1)]),
+    "split_causal": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 1000)]),
 }
 
 
@@ -330,6 +335,10 @@ def test_attention_paths_vs_oracle(case):
     table, pool, full, kp, vp, q = _attention_inputs(spec, 5)
     cfg = B.layer_cfg(spec.shape)
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
+    if case.startswith("split"):
+        plan = B.attention_plan(cfg, b)
+        say(f"  plan {plan}")
+        assert plan["prefill_merges"] > 0, plan
     ws = B.alloc_workspace(cfg, b, DEV)
     out = torch.full_like(q, float("nan"))
     B.attention(cfg, b, q, kp, vp, out, ws)
