@@ -130,7 +130,7 @@ _SIGS = {
                      ctypes.c_int),
     "hl_kv_import": ([ctypes.POINTER(KvSpan), ctypes.c_void_p, ctypes.POINTER(KvPages)],
                      ctypes.c_int),
-    "hl_gemm_tile_choice": ([ctypes.c_int32] * 6 + [ctypes.POINTER(ctypes.c_int32)] * 3,
+    "hl_gemm_tile_choice": ([ctypes.c_int32] * 6 + [ctypes.POINTER(ctypes.c_int32)] * 4,
                             ctypes.c_int),
     "hl_rope_kv_append": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable)], ctypes.c_int),
@@ -405,14 +405,16 @@ def gemm_bf16_nt(a, w, c, residual=None, epilogue: int = HL_EPI_NONE, workspace=
            "hl_gemm_bf16_nt")
 
 
-def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: bool = False, residual=None,
+def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: int = 0, residual=None,
                        epilogue: int = HL_EPI_NONE, workspace=None, stream=None,
                        row_scale=None) -> None:
+    """stream_k: 0 one tile per workgroup, 1 stream-K (plain / residual), s >= 2 split-K into s
+    K ranges (SwiGLU)."""
     m, k = a.shape
     n = w.shape[0]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hl_gemm_bf16_nt_tiled(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), _ptr(row_scale),
-                                       m, n, k, epilogue, tile_m, tile_n, int(bool(stream_k)),
+                                       m, n, k, epilogue, tile_m, tile_n, int(stream_k),
                                        _ptr(workspace), wsb, _stream_ptr(stream)),
            "hl_gemm_bf16_nt_tiled")
 
@@ -430,14 +432,16 @@ def gemm_workspace_bytes(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE) ->
 
 def gemm_tile_choice(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE,
                      with_workspace: bool = True, qkv_head_dim: int = 0):
-    """(tile_m, tile_n, schedule) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's QKV
-    projection) uses for this shape; schedule 0 = one tile per workgroup, 1 = stream-K, 2 = the
-    split-K path of up to 64 token rows. Host-only."""
-    tm, tn, sk = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    """(tile_m, tile_n, schedule, splits) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's
+    QKV projection) uses for this shape; schedule 0 = one tile per workgroup, 1 = stream-K, 2 =
+    the weight-streaming path of up to 64 token rows, 3 = split-K into `splits` K ranges.
+    Host-only."""
+    tm, tn, sk, sp = (ctypes.c_int32(0) for _ in range(4))
     _check(lib().hl_gemm_tile_choice(m, n, k, epilogue, int(bool(with_workspace)), qkv_head_dim,
-                                     ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sk)),
+                                     ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sk),
+                                     ctypes.byref(sp)),
            "hl_gemm_tile_choice")
-    return tm.value, tn.value, int(sk.value)
+    return tm.value, tn.value, int(sk.value), int(sp.value)
 
 
 def rms_scale(x, gain, xg, row_scale, eps: float, stream=None) -> None:

@@ -536,8 +536,10 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
 }
 
 int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t with_workspace,
-                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k) {
-  if (!tile_m || !tile_n || !stream_k) return HL_ERR_NULL;
+                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k,
+                        int32_t* splits) {
+  if (!tile_m || !tile_n || !stream_k || !splits) return HL_ERR_NULL;
+  *splits = 0;
   if (epilogue != HL_EPI_NONE && epilogue != HL_EPI_RESIDUAL && epilogue != HL_EPI_SWIGLU)
     return HL_ERR_ARG;
   if (m < 0 || n <= 0 || k <= 0 || k % 64 || n % 128) return HL_ERR_ARG;
@@ -548,11 +550,14 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
     *stream_k = 2;
     return HL_OK;
   }
-  const bool split = !qkv_head_dim && epilogue != HL_EPI_SWIGLU && with_workspace;
-  const hl::TileChoice tc = hl::choose_tiles(m, n, k, split, qkv_head_dim ? qkv_head_dim : 1);
+  int sched = 0;
+  if (with_workspace)
+    sched = (qkv_head_dim || epilogue == HL_EPI_SWIGLU) ? hl::kSchedSplitK : hl::kSchedStreamK;
+  const hl::TileChoice tc = hl::choose_tiles(m, n, k, sched, qkv_head_dim ? qkv_head_dim : 1);
   *tile_m = tc.bm;
   *tile_n = tc.bn;
-  *stream_k = tc.sk ? 1 : 0;
+  *stream_k = tc.sk ? 1 : (tc.splits >= 2 ? 3 : 0);
+  *splits = tc.splits >= 2 ? tc.splits : 0;
   return HL_OK;
 }
 
@@ -595,13 +600,18 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
   const int rc = check_gemm_args(a, w, c, residual, m, n, k, epilogue);
   if (rc) return rc;
   if (!hl::gemm_tile_supported(tile_m, tile_n) || n % tile_n) return HL_ERR_ARG;
-  if (stream_k && (epilogue == HL_EPI_SWIGLU || !workspace ||
-                   workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
+  if (stream_k < 0) return HL_ERR_ARG;
+  if (stream_k && (!workspace || workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
+    return HL_ERR_ARG;
+  // 1: stream-K (plain / residual); s >= 2: split-K into s K ranges (SwiGLU)
+  if (stream_k == 1 && epilogue == HL_EPI_SWIGLU) return HL_ERR_ARG;
+  if (stream_k >= 2 && (epilogue != HL_EPI_SWIGLU || stream_k > k / 64 ||
+                        !hl::gemm_split_fits(m, n, tile_m, tile_n, stream_k)))
     return HL_ERR_ARG;
   if (m == 0) return HL_OK;
+  const hl::TileChoice tc{tile_m, tile_n, stream_k == 1, stream_k >= 2 ? stream_k : 0};
   return hip_rc(hl::launch_gemm_tiles(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),
-                                      hl::TileChoice{tile_m, tile_n, stream_k != 0}, workspace,
-                                      static_cast<hipStream_t>(stream)));
+                                      tc, workspace, static_cast<hipStream_t>(stream)));
 }
 
 // Host checks of a KV span (nothing is launched on failure).

@@ -14,7 +14,13 @@
 //     one (its tiles run with less contention);
 //   stream-K: t = 1.39 * ceil(tiles * k_steps / 256) * c(BM, BN) + 0.05 us per MB of fp32 pieces
 //     (one piece per run end plus one per split tile, written and read back by the fix-up; a run
-//     that changes tiles loses cache locality, hence the 1.39).
+//     that changes tiles loses cache locality, hence the 1.39);
+//   split-K into S ranges (SwiGLU, RoPE; 128-wide tiles): t = 1.36 * ceil(k_steps / S) * c(BM, BN)
+//     * (rounds of tiles * S) + 0.05 us per MB of pieces (S per tile) + 11 us (the fix-up pass
+//     and the pieces' round trip). Fitted to every 128-wide tile x S in {2, 3, 4, 6, 8} on the
+//     SwiGLU and QKV projections of the 8B and 70B shapes at 65..1040 rows (relative rms error
+//     12 %; the model's picks take 0.8 % longer than the measured best); wider split tiles were
+//     never the best and fit badly, so they are not candidates.
 //
 // c(BM, BN) is the time of one 64-deep k-step of a BM x BN tile with every compute unit busy,
 // fitted, together with the other constants, to times of all shapes below on the layer GEMMs of
@@ -29,7 +35,7 @@ namespace {
 struct TileCost {
   int bm, bn;
   float kstep_us;
-  bool streamk;  // also considered as a stream-K run
+  bool streamk;  // also considered as a stream-K run (and, if 128 wide, as split-K)
 };
 constexpr TileCost kTiles[] = {
     {256, 256, 1.579f, true},  {224, 256, 1.473f, true},  {192, 256, 1.285f, true},
@@ -38,12 +44,25 @@ constexpr TileCost kTiles[] = {
 };
 constexpr int kCUs = kStreamKGrid;
 constexpr float kPartialRound = 0.84f, kStreamKStep = 1.39f, kPieceUsPerMB = 0.05f;
+constexpr float kSplitStep = 1.36f, kSplitFixed = 11.0f;
+constexpr int kSplitCandidates[] = {2, 3, 4, 6, 8, 12, 16};
+constexpr int kMinSplitSteps = 4;  // k-steps of 64 per split at least
+
+float rounds(long items) {
+  const long full = items / kCUs, rem = items % kCUs;
+  return (float)full + (rem ? kPartialRound + (1.f - kPartialRound) * (float)rem / kCUs : 0.f);
+}
 
 float one_tile_cost(const TileCost& t, int m, int n, int nk) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
-  const long full = tiles / kCUs, rem = tiles % kCUs;
-  const float part = rem ? kPartialRound + (1.f - kPartialRound) * (float)rem / kCUs : 0.f;
-  return nk * t.kstep_us * ((float)full + part);
+  return nk * t.kstep_us * rounds(tiles);
+}
+
+float split_cost(const TileCost& t, int m, int n, int nk, int s) {
+  const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
+  const float mb = (float)s * tiles * t.bm * t.bn * 8 / 1e6f;
+  return (float)((nk + s - 1) / s) * t.kstep_us * rounds(tiles * s) * kSplitStep +
+         kPieceUsPerMB * mb + kSplitFixed;
 }
 
 float streamk_cost(const TileCost& t, int m, int n, int nk) {
@@ -59,10 +78,10 @@ float streamk_cost(const TileCost& t, int m, int n, int nk) {
 
 namespace hl {
 
-// Cheapest tile shape (and schedule) by the model above. `split_ok`: the epilogue can be split
-// (plain / residual) and a stream-K workspace is present. `col_align`: N-tile widths must be a
-// multiple of it (the RoPE epilogue needs whole heads per tile).
-TileChoice choose_tiles(int m, int n, int k, bool split_ok, int col_align) {
+// Cheapest tile shape (and schedule) by the model above. `schedules`: kSchedStreamK (plain /
+// residual epilogues) and / or kSchedSplitK (SwiGLU / RoPE) when a workspace is present.
+// `col_align`: N-tile widths must be a multiple of it (the RoPE epilogue needs whole heads).
+TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align) {
   const int nk = k / BK;
   TileChoice best{128, 128, false};
   float best_t = 3.4e38f;
@@ -70,16 +89,26 @@ TileChoice choose_tiles(int m, int n, int k, bool split_ok, int col_align) {
     if (n % t.bn || t.bn % col_align) continue;
     const float c1 = one_tile_cost(t, m, n, nk);
     if (c1 < best_t) best_t = c1, best = TileChoice{t.bm, t.bn, false};
-    if (split_ok && t.streamk && nk >= 4) {
+    if ((schedules & kSchedStreamK) && t.streamk && nk >= 4) {
       const float c2 = streamk_cost(t, m, n, nk);
       if (c2 < best_t) best_t = c2, best = TileChoice{t.bm, t.bn, true};
     }
+    if ((schedules & kSchedSplitK) && t.bn == 128)
+      for (int s : kSplitCandidates) {
+        if (nk < s * kMinSplitSteps || !split_fits(m, n, t.bm, t.bn, s)) continue;
+        const float c3 = split_cost(t, m, n, nk, s);
+        if (c3 < best_t) best_t = c3, best = TileChoice{t.bm, t.bn, false, s};
+      }
   }
   return best;
 }
 
 bool use_skinny(int m, int n, int k, size_t ws_bytes) {
   return m > 0 && m <= kSkinnyMaxM && n % 64 == 0 && ws_bytes >= skinny_workspace_bytes(m, n, k);
+}
+
+bool gemm_split_fits(int m, int n, int bm, int bn, int splits) {
+  return split_fits(m, n, bm, bn, splits);
 }
 
 bool gemm_tile_supported(int bm, int bn) {
@@ -95,7 +124,7 @@ hipError_t launch_gemm_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int
   switch (epi.kind) {
     case HL_EPI_NONE: return launch_gemm_plain(tc, a, w, c, m, n, k, epi, part, st);
     case HL_EPI_RESIDUAL: return launch_gemm_residual(tc, a, w, c, m, n, k, epi, part, st);
-    default: return launch_gemm_swiglu(tc, a, w, c, m, n, k, epi, st);
+    default: return launch_gemm_swiglu(tc, a, w, c, m, n, k, epi, part, st);
   }
 }
 
@@ -111,16 +140,17 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
     return launch_gemm_skinny(a, w, c, m, n, k, epi, static_cast<float*>(ws), st);
   switch (epi.kind) {
     case HL_EPI_NONE:
-      return launch_gemm_plain(choose_tiles(m, n, k, part != nullptr, 1), a, w, c, m, n, k, epi,
-                               part, st);
+      return launch_gemm_plain(choose_tiles(m, n, k, part ? kSchedStreamK : 0, 1), a, w, c, m, n,
+                               k, epi, part, st);
     case HL_EPI_RESIDUAL:
-      return launch_gemm_residual(choose_tiles(m, n, k, part != nullptr, 1), a, w, c, m, n, k,
-                                  epi, part, st);
+      return launch_gemm_residual(choose_tiles(m, n, k, part ? kSchedStreamK : 0, 1), a, w, c, m,
+                                  n, k, epi, part, st);
     case HL_EPI_SWIGLU:
-      return launch_gemm_swiglu(choose_tiles(m, n, k, false, 1), a, w, c, m, n, k, epi, st);
+      return launch_gemm_swiglu(choose_tiles(m, n, k, part ? kSchedSplitK : 0, 1), a, w, c, m, n,
+                                k, epi, part, st);
     default:
-      return launch_gemm_rope(choose_tiles(m, n, k, false, epi.head_dim), a, w, c, m, n, k, epi,
-                              st);
+      return launch_gemm_rope(choose_tiles(m, n, k, part ? kSchedSplitK : 0, epi.head_dim), a, w,
+                              c, m, n, k, epi, part, st);
   }
 }
 

@@ -25,7 +25,11 @@
 // projections leaves fewer tiles than compute units) run stream-K: exactly one workgroup per CU,
 // each taking an equal run of (tile, k-step) iterations; a tile split between workgroups is written
 // as fp32 pieces to the workspace and finished by a fix-up kernel that sums the pieces and applies
-// the epilogue.
+// the epilogue. The SwiGLU and RoPE epilogues need a whole tile (gate and up columns together,
+// whole heads), so when their tiles are too few to fill the compute units (a batch of a few
+// hundred tokens) they run split-K instead: workgroup (tile, s) takes the s-th of S equal K
+// ranges and writes its fp32 accumulators as a piece; the fix-up sums the S pieces in order and
+// applies the epilogue.
 //
 // Epilogues, after an optional per-row scale (the RMSNorm factor, see prep.hip): plain, + residual,
 // SwiGLU (the W tile holds BN/2 gate rows and the matching BN/2 up rows; a lane holds a gate and
@@ -42,9 +46,10 @@ hipError_t launch_gemm_residual(const TileChoice& tc, const hl_bf16* a, const hl
                                 hl_bf16* c, int m, int n, int k, const GemmEpi& epi, float* part,
                                 hipStream_t st);
 hipError_t launch_gemm_swiglu(const TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
-                              int m, int n, int k, const GemmEpi& epi, hipStream_t st);
+                              int m, int n, int k, const GemmEpi& epi, float* part,
+                              hipStream_t st);
 hipError_t launch_gemm_rope(const TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
-                            int m, int n, int k, const GemmEpi& epi, hipStream_t st);
+                            int m, int n, int k, const GemmEpi& epi, float* part, hipStream_t st);
 }  // namespace hl
 
 namespace {
@@ -643,6 +648,155 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
   }
 }
 
+// Split-K main kernel: workgroup (tile, s) runs k-steps [s nk / S, (s + 1) nk / S) of its tile
+// and stores the fp32 accumulators in register order as piece (s, tile): block (i, t) of wave w
+// is 64 lanes x 4 floats at ((w MT + i) NT + t) 256. Workgroups are numbered tile-fastest per
+// split and dealt XCD-contiguously, so the M tiles of one weight column run together.
+template <int EPI, int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
+    const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N, int K,
+    int splits, int mtiles, int tiles, float* __restrict__ part) {
+  using CF = Cfg<BM, BN>;
+  constexpr int MT = CF::MT, NT = CF::NT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int u = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile = u % tiles, s = u / tiles;
+  const int nk = K / BK;
+  const int kb = (int)((long)s * nk / splits), ke = (int)((long)(s + 1) * nk / splits);
+  f32x4 acc[MT][NT];
+  mainloop<EPI, BM, BN>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* dst = part + ((size_t)s * tiles + tile) * BM * BN + lane * 4;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) = acc[i][t];
+}
+
+// Split-K fix-up, SwiGLU: a thread takes one lane quad (4 columns x 4 rows) of a gate block and
+// the same quad of its up block (NT / 2 blocks later in the same wave), sums the S pieces of
+// each in split order, and writes silu(gate) * up.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_split_swiglu_fixup(hl_bf16* __restrict__ C, int M,
+                                                               int N, GemmEpi ep, int splits,
+                                                               int mtiles, int tiles,
+                                                               const float* __restrict__ part) {
+  using CF = Cfg<BM, BN>;
+  constexpr int MT = CF::MT, NT = CF::NT, NH = NT / 2;
+  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  const int g = blockIdx.y * 256 + threadIdx.x;
+  const int q = g & 15, hb = g >> 4;  // lane quad, gate block (w, i, t < NH)
+  if (hb >= 4 * MT * NH) return;
+  const int t = hb % NH, i = (hb / NH) % MT, w = hb / (NH * MT);
+  const int bg = (w * MT + i) * NT + t, bu = bg + NH;
+  f32x4 vg[4] = {}, vu[4] = {};
+  for (int s = 0; s < splits; ++s) {
+    const float* src = part + ((size_t)s * tiles + tile) * BM * BN + q * 16;
+    const f32x4* pg = reinterpret_cast<const f32x4*>(src + bg * 256);
+    const f32x4* pu = reinterpret_cast<const f32x4*>(src + bu * 256);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      vg[l] += pg[l];
+      vu[l] += pu[l];
+    }
+  }
+  const int half_n = N >> 1;
+  const int row0 = mt * BM + (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
+  const int col = nt * (BN / 2) + (w & 1) * (CF::WN / 2) + t * 16 + (q & 3) * 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gm = row0 + r;
+    if (gm >= M) break;
+    const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
+    float e[4];
+#pragma unroll
+    for (int l = 0; l < 4; ++l) e[l] = silu(vg[l][r] * rs) * (vu[l][r] * rs);
+    *reinterpret_cast<u32x2*>(C + (size_t)gm * half_n + col) =
+        u32x2{pack_bf2(e[0], e[1]), pack_bf2(e[2], e[3])};
+  }
+}
+
+// Split-K fix-up, RoPE + KV append: a workgroup takes 32 rows of a tile, sums the S pieces of
+// each quad into an fp32 LDS stage (row-scaled), then rotates and routes whole 8-element runs of
+// each head exactly as the one-tile epilogue does.
+template <int BM, int BN, int HD>
+__global__ __launch_bounds__(256) void gemm_split_rope_fixup(int M, GemmEpi ep, int splits,
+                                                             int mtiles, int tiles,
+                                                             const float* __restrict__ part) {
+  using CF = Cfg<BM, BN>;
+  constexpr int MT = CF::MT, NT = CF::NT, SROW = kStageRow<BN>, ROWS = 32;
+  constexpr int CB = BN / 16;  // 16-column blocks of the tile
+  __shared__ float st[ROWS * SROW];
+  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  const int r0 = blockIdx.y * ROWS;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < (ROWS / 16) * CB * 16; e += 256) {
+    const int q = e & 15, cb = (e >> 4) % CB, rb = (e >> 4) / CB;
+    const int R = r0 / 16 + rb;  // 16-row block of the tile
+    const int blk = (((R / MT) * 2 + cb / NT) * MT + R % MT) * NT + cb % NT;
+    f32x4 v[4] = {};
+    for (int s = 0; s < splits; ++s) {
+      const f32x4* src =
+          reinterpret_cast<const f32x4*>(part + ((size_t)s * tiles + tile) * BM * BN + blk * 256 + q * 16);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) v[l] += src[l];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = rb * 16 + (q >> 2) * 4 + r, gm = mt * BM + r0 + rr;
+      const float rs = (ep.row_scale && gm < M) ? ep.row_scale[gm] : 1.f;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) st[rr * SROW + cb * 16 + (q & 3) * 4 + l] = v[l][r] * rs;
+    }
+  }
+  __syncthreads();
+  constexpr int heads = BN / HD, chunks = HD / 16;
+  for (int e = tid; e < ROWS * heads * chunks; e += 256) {
+    const int c = e % chunks, rest = e / chunks, hi = rest % heads, rr = rest / heads;
+    const int gm = mt * BM + r0 + rr;
+    if (gm >= M) continue;
+    const int pos = ep.tok_pos[gm];
+    rope_store_row<HD>(ep, gm, nt * heads + hi, ep.tok_blk[gm], pos & (HL_BLOCK_SIZE - 1),
+                       (pos & hl::kDecodeBit) != 0, st + rr * SROW + hi * HD, c);
+  }
+}
+
+// Pieces of a split-K launch must fit the stream-K workspace.
+inline bool split_fits(int m, int n, int bm, int bn, int splits) {
+  const size_t tiles = (size_t)((m + bm - 1) / bm) * (n / bn);
+  return (size_t)splits * tiles * bm * bn * 4 <= kStreamKWorkspace;
+}
+
+template <int EPI, int BM, int BN, int HD>
+hipError_t launch_split(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
+                        const GemmEpi& epi, float* part, int splits, hipStream_t st) {
+  using CF = Cfg<BM, BN>;
+  static_assert(EPI == HL_EPI_SWIGLU || EPI == kEpiRopeAppend, "split-K epilogues");
+  auto kern = gemm_split_kernel<EPI, BM, BN>;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, CF::MAIN_LDS);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  const int mtiles = (m + BM - 1) / BM, tiles = mtiles * (n / BN);
+  hipLaunchKernelGGL(kern, dim3(tiles * splits), dim3(kThreads), CF::MAIN_LDS, st, a, w, m, n, k,
+                     splits, mtiles, tiles, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (EPI == HL_EPI_SWIGLU) {
+    constexpr int quads = 4 * CF::MT * (CF::NT / 2) * 16;
+    hipLaunchKernelGGL((gemm_split_swiglu_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256),
+                       dim3(256), 0, st, c, m, n, epi, splits, mtiles, tiles, part);
+  } else {
+    hipLaunchKernelGGL((gemm_split_rope_fixup<BM, BN, HD>), dim3(tiles, BM / 32), dim3(256), 0,
+                       st, m, epi, splits, mtiles, tiles, part);
+  }
+  return hipGetLastError();
+}
+
 template <int EPI, int BM, int BN, int HD = 0>
 hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
                         const GemmEpi& epi, float* part, bool streamk, hipStream_t st) {
@@ -698,6 +852,24 @@ template <int EPI, int HD = 0>
 hipError_t launch_choice(const hl::TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                          int m, int n, int k, const GemmEpi& epi, float* part, hipStream_t st) {
   const bool sk = tc.sk && part != nullptr;
+  if constexpr (EPI == HL_EPI_SWIGLU || EPI == kEpiRopeAppend) {
+    if (tc.splits >= 2) {
+      if (!part || !split_fits(m, n, tc.bm, tc.bn, tc.splits) || tc.splits > k / BK)
+        return hipErrorInvalidValue;
+      switch (tc.bm * 1000 + tc.bn) {
+        case 256256: return launch_split<EPI, 256, 256, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 224256: return launch_split<EPI, 224, 256, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 192256: return launch_split<EPI, 192, 256, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 160256: return launch_split<EPI, 160, 256, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 128256: return launch_split<EPI, 128, 256, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 256128: return launch_split<EPI, 256, 128, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 224128: return launch_split<EPI, 224, 128, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 160128: return launch_split<EPI, 160, 128, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        case 128128: return launch_split<EPI, 128, 128, HD>(a, w, c, m, n, k, epi, part, tc.splits, st);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (tc.bm * 1000 + tc.bn) {
     case 256256: return launch_tiles<EPI, 256, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
     case 224256: return launch_tiles<EPI, 224, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);

@@ -345,28 +345,32 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
 
 /* hl_gemm_bf16_nt with the tile shape and schedule given by the caller instead of chosen (for
  * tuning and tests). tile_m x tile_n must be one of 256x256, 224x256, 192x256, 160x256, 128x256,
- * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0; stream_k != 0 runs a stream-K schedule
- * (HL_EPI_NONE / HL_EPI_RESIDUAL only, and `workspace` must hold hl_gemm_workspace_bytes()).
- * Results agree with hl_gemm_bf16_nt to fp32 summation order. Errors as hl_gemm_bf16_nt, and
- * HL_ERR_ARG for an unsupported tile or schedule. */
+ * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0. stream_k: 0 one tile per workgroup;
+ * 1 a stream-K schedule (HL_EPI_NONE / HL_EPI_RESIDUAL); s >= 2 split-K into s equal K ranges
+ * (HL_EPI_SWIGLU; s <= k / 64, and the s fp32 pieces per tile must fit the workspace). Any
+ * schedule but 0 needs `workspace` of hl_gemm_workspace_bytes(). Results agree with
+ * hl_gemm_bf16_nt to fp32 summation order. Errors as hl_gemm_bf16_nt, and HL_ERR_ARG for an
+ * unsupported tile or schedule. */
 int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                           const hl_bf16* residual, const float* row_scale, int32_t m, int32_t n,
                           int32_t k, int32_t epilogue, int32_t tile_m, int32_t tile_n,
                           int32_t stream_k, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The tile shape (*tile_m x *tile_n outputs per workgroup) and schedule (*stream_k: 1 for a
- * stream-K run with a fix-up pass, 0 for one tile per workgroup, 2 for the split-K path of up to
- * 64 token rows, whose workgroups each cover 64 columns of all rows over a K range) that
- * hl_gemm_bf16_nt uses for
+ * stream-K run with a fix-up pass, 0 for one tile per workgroup, 2 for the weight-streaming path of
+ * up to 64 token rows, whose workgroups each cover 64 columns of all rows over a K range, 3 for
+ * split-K into *splits equal K ranges summed by a fix-up pass that applies the epilogue; *splits
+ * is 0 otherwise) that hl_gemm_bf16_nt uses for
  * these arguments (with_workspace != 0: a stream-K workspace is passed). qkv_head_dim 64 or 128
- * asks instead for the QKV projection of the layer step (RoPE + KV-append epilogue: one tile per
- * workgroup, whole heads per tile); 0 otherwise. Host-only: no device work, no GPU needed. The
- * choice minimises a cost model of the launch (rounds of tiles over the compute units, or the
- * stream-K run length plus its fix-up traffic); the token count of a hybrid batch is arbitrary, so
+ * asks instead for the QKV projection of the layer step (RoPE + KV-append epilogue: whole heads
+ * per tile); 0 otherwise. Host-only: no device work, no GPU needed. The choice minimises a cost
+ * model of the launch (rounds of tiles over the compute units, the stream-K run length, or the
+ * split-K rounds, plus the fix-up traffic); the token count of a hybrid batch is arbitrary, so
  * fixed tiles would hit the tile-quantisation cliff that the chunked-prefill page describes.
  * Errors: HL_ERR_NULL, HL_ERR_ARG (the same size rules as hl_gemm_bf16_nt). */
 int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32_t with_workspace,
-                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k);
+                        int32_t qkv_head_dim, int32_t* tile_m, int32_t* tile_n, int32_t* stream_k,
+                        int32_t* splits);
 
 /* First half of the layer up to attention, as the step runs it: RMSNorm of batch->x (gain
  * w->attn_norm), the QKV projection (w->w_qkv) and, in the same kernel's epilogue, the rotary

@@ -198,6 +198,11 @@ def test_gemm_tiled_argument_checks():
     assert g(p, p, p, None, None, 8, 256, 64, 0, 128, 256, 1, p, 1024, None) == B.HL_ERR_ARG  # small workspace
     assert g(p, p, p, None, None, 8, 256, 60, 0, 128, 256, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
     assert g(p, p, p, None, None, 0, 256, 64, 0, 128, 256, 0, None, 0, None) == B.HL_OK  # m == 0: nothing
+    big = 1 << 30
+    assert g(p, p, p, None, None, 8, 256, 256, 0, 128, 256, 2, p, big, None) == B.HL_ERR_ARG  # plain split-K
+    assert g(p, p, p, None, None, 8, 256, 64, 2, 128, 256, 2, p, big, None) == B.HL_ERR_ARG  # 2 ranges > 1 k-step
+    assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, 2, None, 0, None) == B.HL_ERR_ARG  # no workspace
+    assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -1, p, big, None) == B.HL_ERR_ARG  # negative
 
 
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
@@ -212,13 +217,18 @@ def test_gemm_tile_choice_is_valid(epi):
         k = 64 * int(rng.integers(1, 500))
         ws = bool(rng.integers(0, 2))
         hd = int(rng.choice([0, 64, 128])) if epi == B.HL_EPI_NONE else 0
-        bm, bn, sk = B.gemm_tile_choice(m, n, k, epi, ws, hd)
-        if sk == 2:  # split-K path of few token rows
+        bm, bn, sk, sp = B.gemm_tile_choice(m, n, k, epi, ws, hd)
+        if sk == 2:  # weight-streaming path of few token rows
             assert ws and 0 < m <= 64 and bn == 64 and bm == 16 * ((m + 15) // 16), (m, n, k)
             continue
         assert (bm, bn) in tiles and n % bn == 0, (m, n, k, bm, bn)
-        if sk:
+        assert (sp >= 2) == (sk == 3), (sk, sp)
+        if sk == 1:
             assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)
+        if sk == 3:  # split-K: SwiGLU or the QKV projection, at least 4 k-steps per range
+            assert ws and (hd or epi == B.HL_EPI_SWIGLU) and k // 64 >= 4 * sp, (m, n, k, sp)
+            tiles_n = -(-m // bm) * (n // bn)
+            assert sp * tiles_n * bm * bn * 4 <= 256 * 2 * 256 * 256 * 4, (m, n, bm, bn, sp)
         if hd:
             assert bn % hd == 0
     with pytest.raises(RuntimeError):
@@ -230,7 +240,7 @@ def test_gemm_tile_choice_fits_the_batch():
     whose row count wastes less than a 256-row tile would (5 x 256 = 1280 rows for 1040)."""
     for n, k, epi in [(4096, 4096, B.HL_EPI_RESIDUAL), (24576, 4096, B.HL_EPI_SWIGLU),
                       (4096, 12288, B.HL_EPI_RESIDUAL)]:
-        bm, bn, sk = B.gemm_tile_choice(1040, n, k, epi)
+        bm, bn, sk, _ = B.gemm_tile_choice(1040, n, k, epi)
         assert sk or bm * math.ceil(1040 / bm) < 1280, (n, k, bm, bn, sk)
 
 

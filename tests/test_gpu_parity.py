@@ -85,17 +85,20 @@ def test_gemm_streamk_vs_oracle(m, n, k, epi):
 
 
 @pytest.mark.parametrize("tile", B.GEMM_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
-@pytest.mark.parametrize("epi,stream_k", [(B.HL_EPI_NONE, False), (B.HL_EPI_RESIDUAL, False),
-                                          (B.HL_EPI_SWIGLU, False), (B.HL_EPI_NONE, True),
-                                          (B.HL_EPI_RESIDUAL, True)],
-                         ids=["plain", "residual", "swiglu", "plain-sk", "residual-sk"])
+@pytest.mark.parametrize("epi,stream_k", [(B.HL_EPI_NONE, 0), (B.HL_EPI_RESIDUAL, 0),
+                                          (B.HL_EPI_SWIGLU, 0), (B.HL_EPI_NONE, 1),
+                                          (B.HL_EPI_RESIDUAL, 1), (B.HL_EPI_SWIGLU, 2),
+                                          (B.HL_EPI_SWIGLU, 3)],
+                         ids=["plain", "residual", "swiglu", "plain-sk", "residual-sk",
+                              "swiglu-split2", "swiglu-split3"])
 def test_gemm_every_tile_shape(tile, epi, stream_k):
-    """Every compiled tile shape, one tile per workgroup and stream-K, through the explicit-tile
-    entry point. 300 rows leave a ragged last M tile for every BM; the stream-K shape (2100 x 8192
-    x 192: 3 k-steps per tile, runs of 4 or more) mixes tiles split across runs (fix-up) with tiles
-    whole inside one run (finished in the main kernel), and uses a row scale."""
+    """Every compiled tile shape, one tile per workgroup, stream-K and split-K, through the
+    explicit-tile entry point. 300 rows leave a ragged last M tile for every BM; the stream-K shape
+    (2100 x 8192 x 192: 3 k-steps per tile, runs of 4 or more) mixes tiles split across runs
+    (fix-up) with tiles whole inside one run (finished in the main kernel); split-K cuts the 5
+    k-steps of K = 320 into unequal ranges (2 + 3, or 1 + 2 + 2). Both use a row scale."""
     bm, bn = tile
-    shapes = [(300, 512, 320)] + ([(2100, 8192, 192)] if stream_k else [])
+    shapes = [(300, 512, 320)] + ([(2100, 8192, 192)] if stream_k == 1 else [])
     for m, n, k in shapes:
         say(f"gemm tile {bm}x{bn} stream_k={stream_k} epi={epi} m={m} n={n} k={k}")
         a = _randn((m, k), 41 + m + bm)
@@ -239,6 +242,15 @@ for _t, _rows in _QKV_TILE_ROWS.items():
 for _t in [(160, 128), (224, 256), (256, 128)]:
     QKV_CASES[f"tile{_t[0]}x{_t[1]}_d64"] = (workloads.LayerShape(1024, 16, 4, 64, 512),
                                             _qkv_rows_case(_QKV_TILE_ROWS[_t]))
+# a few hundred rows: too few tiles for the compute units, so the projection runs split-K (K cut
+# into equal ranges whose fp32 pieces the fix-up sums before the RoPE / append epilogue)
+_QKV_SPLIT = {"split160x128_d128": ((4096, 8, 2, 128), 150),
+              "split128x128_d64": ((4096, 16, 4, 64), 100),
+              "split224x128_d128": ((4096, 24, 8, 128), 200),
+              "split160x128_d64": ((4096, 16, 4, 64), 300)}
+for _name, (_dims, _rows) in _QKV_SPLIT.items():
+    QKV_CASES[_name] = (workloads.LayerShape(*_dims, 512),
+                        [(0, _rows - 69), (777, 40), (5000, 1), (33, 1), (15, 26), (4096, 1)])
 
 
 @pytest.mark.parametrize("case", sorted(QKV_CASES))
@@ -247,12 +259,12 @@ def test_qkv_rope_append_vs_oracle(case):
     spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 3)
     say(f"qkv+rope+append {case}: {spec.seqs}")
     s = spec.shape
-    if case.startswith("tile"):
-        want = tuple(int(v) for v in case[4:].split("_")[0].split("x"))
+    if case.startswith("tile") or case.startswith("split"):
+        want = tuple(int(v) for v in case[5 if case[0] == "s" else 4:].split("_")[0].split("x"))
         qkv_cols = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
         got = B.gemm_tile_choice(spec.num_tokens, qkv_cols, s.hidden, B.HL_EPI_NONE, True,
                                  s.head_dim)
-        assert got[:2] == want, (case, got)
+        assert got[:2] == want and (got[2] == 3) == case.startswith("split"), (case, got)
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
