@@ -19,6 +19,7 @@ HL_OK = 0
 HL_ERR_NULL, HL_ERR_SHAPE, HL_ERR_DESC, HL_ERR_BLOCK = -1, -2, -3, -4
 HL_ERR_ALIGN, HL_ERR_WORKSPACE, HL_ERR_HIP, HL_ERR_ARG = -5, -6, -7, -8
 HL_EPI_NONE, HL_EPI_RESIDUAL, HL_EPI_SWIGLU = 0, 1, 2
+HL_ATTN_AUTO, HL_ATTN_FUSED, HL_ATTN_SEPARATE = 0, 1, 2
 BLOCK_SIZE = 16
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -39,7 +40,8 @@ class BatchDesc(ctypes.Structure):
                 ("h_num_cached", _c_i32p), ("x", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", ctypes.c_void_p), ("tap_q_rot", ctypes.c_void_p),
-                ("tap_attn_out", ctypes.c_void_p), ("tap_h2", ctypes.c_void_p)]
+                ("tap_attn_out", ctypes.c_void_p), ("tap_h2", ctypes.c_void_p),
+                ("attention", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -194,8 +196,10 @@ def layer_cfg(shape, softmax_scale: float = 0.0) -> LayerCfg:
 class Batch:
     """Batch descriptor arrays: host mirrors (numpy int32) plus device copies (torch)."""
 
-    def __init__(self, q_start, num_cached, table, device="cuda"):
+    def __init__(self, q_start, num_cached, table, device="cuda", attention: int = 0):
+        """attention: HL_ATTN_AUTO (0), HL_ATTN_FUSED (1) or HL_ATTN_SEPARATE (2)."""
         import torch
+        self.attention = attention
         self.h_q_start = np.ascontiguousarray(q_start, dtype=np.int32)
         self.h_num_cached = np.ascontiguousarray(num_cached, dtype=np.int32)
         self.h_table = np.ascontiguousarray(table, dtype=np.int32)
@@ -225,6 +229,7 @@ def _desc(cfg: LayerCfg, b: Batch, x=None, workspace=None, stream=None, taps=Non
     d.tap_q_rot = _ptr(taps.get("q_rot"))
     d.tap_attn_out = _ptr(taps.get("attn_out"))
     d.tap_h2 = _ptr(taps.get("h2"))
+    d.attention = getattr(b, "attention", 0)
     return d
 
 
@@ -409,7 +414,7 @@ def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: int = 0, res
                        epilogue: int = HL_EPI_NONE, workspace=None, stream=None,
                        row_scale=None) -> None:
     """stream_k: 0 one tile per workgroup, 1 stream-K (plain / residual), s >= 2 split-K into s
-    K ranges (SwiGLU)."""
+    K ranges."""
     m, k = a.shape
     n = w.shape[0]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()

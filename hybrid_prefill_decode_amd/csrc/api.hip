@@ -63,6 +63,7 @@ int check_batch(const hl_batch_desc* b) {
   int rc = check_cfg(b->cfg);
   if (rc) return rc;
   if (b->num_seqs < 0 || b->num_tokens < 0) return HL_ERR_DESC;
+  if (b->attention < HL_ATTN_AUTO || b->attention > HL_ATTN_SEPARATE) return HL_ERR_DESC;
   if (b->num_seqs == 0) return b->num_tokens == 0 ? HL_OK : HL_ERR_DESC;
   if (!b->h_q_start || !b->h_num_cached || !b->q_start || !b->num_cached) return HL_ERR_NULL;
   if (b->h_q_start[0] != 0) return HL_ERR_DESC;
@@ -213,20 +214,31 @@ int pick_pre_split(const hl_batch_desc* b) {
 void make_plan(const hl_batch_desc* b, HostPlan* p) {
   const hl_layer_cfg& c = *b->cfg;
   *p = HostPlan{};
-  // Fused attention pays when the prefill work is comparable to the decode work (it then hides
-  // behind the decode streams) or when the decode work is so large that unit granularity does not
-  // matter; a small prefill next to a moderate decode runs best as two tuned launches. The
-  // estimates use sustained rates of the two kernels on this part (prefill ~0.7 PFLOP/s, decode
-  // ~5 TB/s); only their ratio matters.
+  // Fused attention pays when a long prefill with many work items can absorb the decode streams
+  // (its dynamic queues fill the tail of uneven causal tiles with decode units), or when the
+  // decode work is so large that unit granularity does not matter. Otherwise two tuned launches
+  // win: the fused kernel's prefill items run slower than the standalone kernel's (the kernel
+  // holds both paths' registers), which a short prefill or a little decode work cannot repay.
+  // Rule measured on a grid of 8B / 70B batches (prompt chunks of 128..2048 tokens at prefixes
+  // 0..8192, 16..256 decodes at 512..8192) and the four large workloads; the estimates use
+  // sustained rates of the two kernels (prefill ~0.7 PFLOP/s, decode ~5 TB/s).
   double pre_flops = 0.0, dec_bytes = 0.0;
+  int64_t pre_items = 0;
   for (int s = 0; s < b->num_seqs; ++s) {
     const double n = b->h_q_start[s + 1] - b->h_q_start[s], kv = b->h_num_cached[s] + n;
-    if (n == 1) dec_bytes += kv * c.n_kv_heads * c.head_dim * 4.0;
-    else pre_flops += 4.0 * c.head_dim * c.n_q_heads * (n * b->h_num_cached[s] + n * (n + 1) / 2);
+    if (n == 1) {
+      dec_bytes += kv * c.n_kv_heads * c.head_dim * 4.0;
+    } else {
+      pre_flops += 4.0 * c.head_dim * c.n_q_heads * (n * b->h_num_cached[s] + n * (n + 1) / 2);
+      pre_items += (int64_t)((n + hl::kPrefillQTile - 1) / hl::kPrefillQTile) * c.n_q_heads;
+    }
   }
   const double pre_us = pre_flops / 0.7e9, dec_us = dec_bytes / 5.0e6;  // flop/us, byte/us
-  p->fused = pre_flops > 0 && dec_bytes > 0 &&
-             (pre_us >= 0.5 * dec_us || (dec_us >= 1000.0 && pre_us >= 0.02 * dec_us));
+  p->fused = pre_flops > 0 && dec_bytes > 0 && pre_us >= 90.0 &&
+             ((pre_items >= 512 && dec_us <= 4.0 * pre_us) ||
+              (dec_us >= 1000.0 && pre_us >= 0.02 * dec_us));
+  if (b->attention == HL_ATTN_FUSED) p->fused = pre_flops > 0 && dec_bytes > 0;
+  if (b->attention == HL_ATTN_SEPARATE) p->fused = false;
   p->split_pages = p->fused ? pick_split_fused(b) : pick_split(b);
   p->pre_split = pick_pre_split(b);
   for (int s = 0; s < b->num_seqs; ++s) {
@@ -603,10 +615,9 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
   if (stream_k < 0) return HL_ERR_ARG;
   if (stream_k && (!workspace || workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
     return HL_ERR_ARG;
-  // 1: stream-K (plain / residual); s >= 2: split-K into s K ranges (SwiGLU)
+  // 1: stream-K (plain / residual); s >= 2: split-K into s K ranges
   if (stream_k == 1 && epilogue == HL_EPI_SWIGLU) return HL_ERR_ARG;
-  if (stream_k >= 2 && (epilogue != HL_EPI_SWIGLU || stream_k > k / 64 ||
-                        !hl::gemm_split_fits(m, n, tile_m, tile_n, stream_k)))
+  if (stream_k >= 2 && (stream_k > k / 64 || !hl::gemm_split_fits(m, n, tile_m, tile_n, stream_k)))
     return HL_ERR_ARG;
   if (m == 0) return HL_OK;
   const hl::TileChoice tc{tile_m, tile_n, stream_k == 1, stream_k >= 2 ? stream_k : 0};

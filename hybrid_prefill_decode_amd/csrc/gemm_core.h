@@ -623,10 +623,30 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
   const int row0 = (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
   const int col = (w & 1) * CF::WN + t * 16 + (q & 3) * 4;
   f32x4 v[4] = {};  // v[l][r]: column col + l, row row0 + r
-  for (int wg = w0; wg <= w1; ++wg) {
-    const int slot = ((wg * sc.ipw) / sc.nk == tile) ? 0 : 1;  // first segment of wg's run?
-    const f32x4* src = reinterpret_cast<const f32x4*>(sc.part + ((size_t)wg * 2 + slot) * BM * BN +
-                                                      blk * 256 + q * 16);
+  // piece of run wg (slot 0 if the tile is the first segment of wg's run)
+  auto piece = [&](int wg) {
+    const int slot = ((wg * sc.ipw) / sc.nk == tile) ? 0 : 1;
+    return reinterpret_cast<const f32x4*>(sc.part + ((size_t)wg * 2 + slot) * BM * BN + blk * 256 +
+                                          q * 16);
+  };
+  // a short K split over many runs leaves a tile in many pieces: four pieces' loads are issued
+  // together, then added in run order
+  int wg = w0;
+  for (; wg + 3 <= w1; wg += 4) {
+    f32x4 t[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4* src = piece(wg + u);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) t[u][l] = src[l];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int l = 0; l < 4; ++l) v[l] += t[u][l];
+  }
+  for (; wg <= w1; ++wg) {
+    const f32x4* src = piece(wg);
 #pragma unroll
     for (int l = 0; l < 4; ++l) v[l] += src[l];
   }
@@ -674,6 +694,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
       *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) = acc[i][t];
 }
 
+// Split-K fix-up, plain / residual: a thread takes one lane quad (4 columns x 4 rows) of one
+// 16 x 16 block, sums its S pieces in split order and applies the epilogue.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_split_fixup(hl_bf16* __restrict__ C, int M, int N,
+                                                        GemmEpi ep, int splits, int mtiles,
+                                                        int tiles, const float* __restrict__ part) {
+  using CF = Cfg<BM, BN>;
+  constexpr int MT = CF::MT, NT = CF::NT;
+  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  const int g = blockIdx.y * 256 + threadIdx.x;
+  const int q = g & 15, blk = g >> 4;  // lane quad, block (w MT + i) NT + t
+  if (blk >= 4 * MT * NT) return;
+  const int t = blk % NT, i = (blk / NT) % MT, w = blk / (NT * MT);
+  f32x4 v[4] = {};
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(part + ((size_t)s * tiles + tile) * BM * BN +
+                                                      blk * 256 + q * 16);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) v[l] += src[l];
+  }
+  const int row0 = mt * BM + (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
+  const int col = nt * BN + (w & 1) * CF::WN + t * 16 + (q & 3) * 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gm = row0 + r;
+    if (gm >= M) break;
+    const size_t o = (size_t)gm * N + col;
+    const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
+    float e[4] = {v[0][r] * rs, v[1][r] * rs, v[2][r] * rs, v[3][r] * rs};
+    if (ep.kind == HL_EPI_RESIDUAL) {
+      const u32x2 rr = *reinterpret_cast<const u32x2*>(ep.residual + o);
+      e[0] += bf_lo(rr[0]);
+      e[1] += bf_hi(rr[0]);
+      e[2] += bf_lo(rr[1]);
+      e[3] += bf_hi(rr[1]);
+    }
+    *reinterpret_cast<u32x2*>(C + o) = u32x2{pack_bf2(e[0], e[1]), pack_bf2(e[2], e[3])};
+  }
+}
+
 // Split-K fix-up, SwiGLU: a thread takes one lane quad (4 columns x 4 rows) of a gate block and
 // the same quad of its up block (NT / 2 blocks later in the same wave), sums the S pieces of
 // each in split order, and writes silu(gate) * up.
@@ -691,6 +752,7 @@ __global__ __launch_bounds__(256) void gemm_split_swiglu_fixup(hl_bf16* __restri
   const int t = hb % NH, i = (hb / NH) % MT, w = hb / (NH * MT);
   const int bg = (w * MT + i) * NT + t, bu = bg + NH;
   f32x4 vg[4] = {}, vu[4] = {};
+#pragma unroll 4
   for (int s = 0; s < splits; ++s) {
     const float* src = part + ((size_t)s * tiles + tile) * BM * BN + q * 16;
     const f32x4* pg = reinterpret_cast<const f32x4*>(src + bg * 256);
@@ -736,6 +798,7 @@ __global__ __launch_bounds__(256) void gemm_split_rope_fixup(int M, GemmEpi ep, 
     const int R = r0 / 16 + rb;  // 16-row block of the tile
     const int blk = (((R / MT) * 2 + cb / NT) * MT + R % MT) * NT + cb % NT;
     f32x4 v[4] = {};
+#pragma unroll 4
     for (int s = 0; s < splits; ++s) {
       const f32x4* src =
           reinterpret_cast<const f32x4*>(part + ((size_t)s * tiles + tile) * BM * BN + blk * 256 + q * 16);
@@ -772,7 +835,7 @@ template <int EPI, int BM, int BN, int HD>
 hipError_t launch_split(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
                         const GemmEpi& epi, float* part, int splits, hipStream_t st) {
   using CF = Cfg<BM, BN>;
-  static_assert(EPI == HL_EPI_SWIGLU || EPI == kEpiRopeAppend, "split-K epilogues");
+
   auto kern = gemm_split_kernel<EPI, BM, BN>;
   static bool attr = false;
   if (!attr) {
@@ -790,6 +853,10 @@ hipError_t launch_split(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
     constexpr int quads = 4 * CF::MT * (CF::NT / 2) * 16;
     hipLaunchKernelGGL((gemm_split_swiglu_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256),
                        dim3(256), 0, st, c, m, n, epi, splits, mtiles, tiles, part);
+  } else if constexpr (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL) {
+    constexpr int quads = 4 * CF::MT * CF::NT * 16;
+    hipLaunchKernelGGL((gemm_split_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256), dim3(256), 0,
+                       st, c, m, n, epi, splits, mtiles, tiles, part);
   } else {
     hipLaunchKernelGGL((gemm_split_rope_fixup<BM, BN, HD>), dim3(tiles, BM / 32), dim3(256), 0,
                        st, m, epi, splits, mtiles, tiles, part);
@@ -852,7 +919,7 @@ template <int EPI, int HD = 0>
 hipError_t launch_choice(const hl::TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                          int m, int n, int k, const GemmEpi& epi, float* part, hipStream_t st) {
   const bool sk = tc.sk && part != nullptr;
-  if constexpr (EPI == HL_EPI_SWIGLU || EPI == kEpiRopeAppend) {
+  {
     if (tc.splits >= 2) {
       if (!part || !split_fits(m, n, tc.bm, tc.bn, tc.splits) || tc.splits > k / BK)
         return hipErrorInvalidValue;

@@ -96,7 +96,12 @@ typedef struct {
  * (validation and launch planning, so the call never waits for the device); both must hold the
  * same values. The tap pointers, when non-NULL, receive copies of intermediate tensors:
  * tap_q_rot [T, Hq*d] (rotated queries), tap_attn_out [T, Hq*d] (attention output before W_o),
- * tap_h2 [T, hidden] (residual stream after attention). */
+ * tap_h2 [T, hidden] (residual stream after attention). `attention` picks how prefill and decode
+ * attention are launched when the batch has both: HL_ATTN_AUTO (0, a zero-initialised
+ * descriptor) lets the library choose (hl_attention_plan reports the choice), HL_ATTN_FUSED one
+ * launch for both paths, HL_ATTN_SEPARATE two launches; the results are bit-identical either way.
+ * The workspace size depends on it: pass the same descriptor to hl_workspace_bytes. */
+enum { HL_ATTN_AUTO = 0, HL_ATTN_FUSED = 1, HL_ATTN_SEPARATE = 2 };
 typedef struct {
   const hl_layer_cfg* cfg;
   int32_t num_seqs;
@@ -112,6 +117,7 @@ typedef struct {
   hl_bf16* tap_q_rot;          /* device, optional */
   hl_bf16* tap_attn_out;       /* device, optional */
   hl_bf16* tap_h2;             /* device, optional */
+  int32_t attention;           /* HL_ATTN_AUTO / HL_ATTN_FUSED / HL_ATTN_SEPARATE */
 } hl_batch_desc;
 
 /* Weights, all device, row-major [out_features, in_features] (each row one output feature). */
@@ -347,7 +353,7 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
  * tuning and tests). tile_m x tile_n must be one of 256x256, 224x256, 192x256, 160x256, 128x256,
  * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0. stream_k: 0 one tile per workgroup;
  * 1 a stream-K schedule (HL_EPI_NONE / HL_EPI_RESIDUAL); s >= 2 split-K into s equal K ranges
- * (HL_EPI_SWIGLU; s <= k / 64, and the s fp32 pieces per tile must fit the workspace). Any
+ * (any epilogue; s <= k / 64, and the s fp32 pieces per tile must fit the workspace). Any
  * schedule but 0 needs `workspace` of hl_gemm_workspace_bytes(). Results agree with
  * hl_gemm_bf16_nt to fp32 summation order. Errors as hl_gemm_bf16_nt, and HL_ERR_ARG for an
  * unsupported tile or schedule. */

@@ -199,7 +199,7 @@ def test_gemm_tiled_argument_checks():
     assert g(p, p, p, None, None, 8, 256, 60, 0, 128, 256, 0, None, 0, None) == B.HL_ERR_ARG  # k % 64
     assert g(p, p, p, None, None, 0, 256, 64, 0, 128, 256, 0, None, 0, None) == B.HL_OK  # m == 0: nothing
     big = 1 << 30
-    assert g(p, p, p, None, None, 8, 256, 256, 0, 128, 256, 2, p, big, None) == B.HL_ERR_ARG  # plain split-K
+    assert g(p, p, p, None, None, 8, 256, 256, 0, 128, 256, 5, p, big, None) == B.HL_ERR_ARG  # 5 ranges > 4 k-steps
     assert g(p, p, p, None, None, 8, 256, 64, 2, 128, 256, 2, p, big, None) == B.HL_ERR_ARG  # 2 ranges > 1 k-step
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, 2, None, 0, None) == B.HL_ERR_ARG  # no workspace
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -1, p, big, None) == B.HL_ERR_ARG  # negative
@@ -320,3 +320,20 @@ def test_attention_plan_argument_checks():
     assert B.lib().hl_attention_plan(None, *[ctypes.byref(x) for x in v]) == B.HL_ERR_NULL
     p = _plan(workloads.SHAPES["tiny"], [])
     assert p["prefill_parts"] == 0 and p["decode_units"] == 0
+
+
+def test_attention_option_checks_and_choice():
+    spec, b, _ = _fake_batch([(300, 200), (40, 1), (500, 1)])
+    cfg = B.layer_cfg(spec.shape)
+    n = ctypes.c_size_t(0)
+    for bad in (-1, 3):
+        b.attention = bad
+        d = B._desc(cfg, b, with_stream=False)
+        assert B.lib().hl_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == B.HL_ERR_DESC
+    # forced modes: fused only when the batch has both paths
+    for mode, want in ((B.HL_ATTN_AUTO, 0), (B.HL_ATTN_FUSED, 1), (B.HL_ATTN_SEPARATE, 0)):
+        b.attention = mode
+        assert B.attention_plan(cfg, b)["fused"] == want, mode
+    spec2, b2, _ = _fake_batch([(300, 200)])
+    b2.attention = B.HL_ATTN_FUSED
+    assert B.attention_plan(B.layer_cfg(spec2.shape), b2)["fused"] == 0

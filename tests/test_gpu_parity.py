@@ -88,9 +88,11 @@ def test_gemm_streamk_vs_oracle(m, n, k, epi):
 @pytest.mark.parametrize("epi,stream_k", [(B.HL_EPI_NONE, 0), (B.HL_EPI_RESIDUAL, 0),
                                           (B.HL_EPI_SWIGLU, 0), (B.HL_EPI_NONE, 1),
                                           (B.HL_EPI_RESIDUAL, 1), (B.HL_EPI_SWIGLU, 2),
-                                          (B.HL_EPI_SWIGLU, 3)],
+                                          (B.HL_EPI_SWIGLU, 3), (B.HL_EPI_NONE, 3),
+                                          (B.HL_EPI_RESIDUAL, 2)],
                          ids=["plain", "residual", "swiglu", "plain-sk", "residual-sk",
-                              "swiglu-split2", "swiglu-split3"])
+                              "swiglu-split2", "swiglu-split3", "plain-split3",
+                              "residual-split2"])
 def test_gemm_every_tile_shape(tile, epi, stream_k):
     """Every compiled tile shape, one tile per workgroup, stream-K and split-K, through the
     explicit-tile entry point. 300 rows leave a ragged last M tile for every BM; the stream-K shape
@@ -339,14 +341,19 @@ ATTN_CASES = {
 }
 
 
+@pytest.mark.parametrize("attention", [B.HL_ATTN_AUTO, B.HL_ATTN_FUSED],
+                         ids=["auto", "fused"])
 @pytest.mark.parametrize("case", sorted(ATTN_CASES))
-def test_attention_paths_vs_oracle(case):
+def test_attention_paths_vs_oracle(case, attention):
     shape, seqs = ATTN_CASES[case]
     spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 77)
     say(f"attention {case}: seqs={spec.seqs[:6]}")
     table, pool, full, kp, vp, q = _attention_inputs(spec, 5)
     cfg = B.layer_cfg(spec.shape)
-    b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV, attention=attention)
+    if attention == B.HL_ATTN_FUSED and spec.num_tokens > len(spec.seqs) and \
+            any(n == 1 for _, n in spec.seqs):
+        assert B.attention_plan(cfg, b)["fused"] == 1
     if case.startswith("split"):
         plan = B.attention_plan(cfg, b)
         say(f"  plan {plan}")
