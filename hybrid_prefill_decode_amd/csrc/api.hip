@@ -369,15 +369,16 @@ hl::GemmEpi plain_epi(int kind, const hl_bf16* residual, const float* row_scale)
   return e;
 }
 
-// prep(x) + QKV GEMM with the RoPE / KV-append epilogue.
+// prep(x) + QKV GEMM with the RoPE / KV-append epilogue; with `plan`, the prep pass also builds
+// the attention work lists.
 int run_qkv(const hl_batch_desc* b, const hl_weights* w, hl_bf16* q_rot, const hl_kv_pages* kv,
-            const hl_block_table* bt, const Buffers& B) {
+            const hl_block_table* bt, const Buffers& B, const hl::Plan* plan = nullptr) {
   const hl_layer_cfg& c = *b->cfg;
   hipStream_t st = static_cast<hipStream_t>(b->stream);
   hl::TokenInfo ti{b->q_start, b->num_cached, b->num_seqs, bt->table, bt->max_blocks_per_seq,
                    kv->num_blocks, c.head_dim, c.rope_theta, B.pos, B.blk, B.cs};
   int rc = hip_rc(hl::launch_prep(b->x, w->attn_norm, B.h1, B.rs, b->num_tokens, c.hidden,
-                                  c.rms_eps, &ti, st));
+                                  c.rms_eps, &ti, st, plan));
   if (rc) return rc;
   hl::GemmEpi e = plain_epi(hl::kEpiRopeAppend, nullptr, B.rs);
   e.n_q_heads = c.n_q_heads;
@@ -395,12 +396,14 @@ int run_qkv(const hl_batch_desc* b, const hl_weights* w, hl_bf16* q_rot, const h
                                 B.gemm_ws, B.gemm_bytes, st));
 }
 
+// plan_built: the work lists are already in the workspace (built by the step's prep pass).
 int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q_lo,
                   const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
-                  const HostPlan& hp, bool do_prefill, bool do_decode) {
+                  const HostPlan& hp, bool do_prefill, bool do_decode, bool plan_built = false) {
   hipStream_t st = static_cast<hipStream_t>(b->stream);
   const hl::Plan dp = device_plan(hp, b->workspace);
-  int rc = hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, dp, st));
+  int rc = plan_built ? HL_OK
+                      : hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, dp, st));
   if (rc) return rc;
   if (do_prefill && do_decode && hp.fused) {
     // both paths in one fused launch: prefill and decode overlap on every compute unit
@@ -443,8 +446,9 @@ int run_layer(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
   hipStream_t st = static_cast<hipStream_t>(batch->stream);
   const Buffers B = buffers(batch, hp);
   int rc;
-  if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B))) return rc;
-  if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true))) return rc;
+  const hl::Plan dp = device_plan(hp, batch->workspace);
+  if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B, &dp))) return rc;
+  if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true, true))) return rc;
   if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
                                    plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), B.gemm_ws,
                                    B.gemm_bytes, st))))

@@ -116,9 +116,10 @@ struct GemmEpi {
   const float2* rope_cs;
 };
 
+// plan: also build the attention work lists (one extra workgroup; needs ti).
 hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* rscale,
                        int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
-                       hipStream_t st);
+                       hipStream_t st, const Plan* plan = nullptr);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
                        const Plan& plan, hipStream_t st);
 constexpr int kPlanCounters = 16;

@@ -10,7 +10,9 @@
 // the rotary cos/sin of every pair j < d/2 at that position (angles formed in fp64), which the
 // QKV GEMM epilogue uses to rotate q and k and to append K/V ("Chunked prefill (stall-free
 // batching), explained", "How it works, step by step": new tokens write their K/V into the cache).
-#include "common.h"
+// When asked, one extra workgroup of that pass builds the step's attention work lists
+// (plan_core.h), which saves the step a separate launch.
+#include "plan_core.h"
 
 namespace {
 
@@ -23,8 +25,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     float* __restrict__ rscale, int cols, float eps, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ num_cached, int num_seqs, const int32_t* __restrict__ table,
     int max_blocks, long long num_blocks, int D, float theta, int32_t* __restrict__ tok_pos,
-    int32_t* __restrict__ tok_blk, float2* __restrict__ rope_cs) {
+    int32_t* __restrict__ tok_blk, float2* __restrict__ rope_cs, hl::Plan plan, int rows) {
   const int row = blockIdx.x;
+  if (TOKEN_INFO && row == rows) {  // the extra workgroup: the attention work lists
+    __shared__ int wt[5][kThreads / 64];
+    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, plan, wt);
+    return;
+  }
   if (TOKEN_INFO) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
@@ -104,17 +111,18 @@ namespace hl {
 
 hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* rscale,
                        int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
-                       hipStream_t st) {
+                       hipStream_t st, const Plan* plan) {
   if (rows <= 0) return hipSuccess;
   if (ti) {
-    hipLaunchKernelGGL(prep_kernel<true>, dim3(rows), dim3(kThreads), 0, st, x, gain, xg, rscale,
-                       cols, eps, ti->q_start, ti->num_cached, ti->num_seqs, ti->table,
-                       ti->max_blocks, (long long)ti->num_blocks, ti->head_dim, ti->rope_theta,
-                       ti->tok_pos, ti->tok_blk, ti->rope_cs);
+    const Plan pl = plan ? *plan : Plan{};
+    hipLaunchKernelGGL(prep_kernel<true>, dim3(rows + (plan ? 1 : 0)), dim3(kThreads), 0, st, x,
+                       gain, xg, rscale, cols, eps, ti->q_start, ti->num_cached, ti->num_seqs,
+                       ti->table, ti->max_blocks, (long long)ti->num_blocks, ti->head_dim,
+                       ti->rope_theta, ti->tok_pos, ti->tok_blk, ti->rope_cs, pl, rows);
   } else {
     hipLaunchKernelGGL(prep_kernel<false>, dim3(rows), dim3(kThreads), 0, st, x, gain, xg, rscale,
                        cols, eps, nullptr, nullptr, 0, nullptr, 0, 0LL, 0, 0.f, nullptr, nullptr,
-                       nullptr);
+                       nullptr, Plan{}, rows);
   }
   return hipGetLastError();
 }
