@@ -348,7 +348,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations and cached K/V, N(0,0.02^2) weights; random block table)",
-        "config": {"workload": workloads.describe(spec), "parallelism": "none (1 GPU)"},
+        "config": {**workloads.describe(spec), "parallelism": "none (1 GPU)"},
         "roofline": {
             "kernel": "gemm_bf16_nt<SwiGLU> (gate/up projection)",
             "bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -444,7 +444,7 @@ def model_bench(args, spec, dev):
         "ms_per_step": round(ms, 3), "step_ms": pct(per), "steps": steps, "warmup": args.warmup,
         "layers": L, "vocab": vocab, "graph": bool(args.graph), "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the workload's layer shape)",
-        "config": {"workload": workloads.describe(spec), "parallelism": "none (1 GPU)"},
+        "config": {**workloads.describe(spec), "parallelism": "none (1 GPU)"},
     }), flush=True)
 
 

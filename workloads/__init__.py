@@ -233,8 +233,13 @@ def describe(spec: BatchSpec) -> dict:
     s = spec.shape
     dec = [c for c, n in spec.seqs if n == 1]
     pre = [(c, n) for c, n in spec.seqs if n > 1]
+    shape_name = next((k for k, v in SHAPES.items() if v == s), "custom")
+    parts = [f"{n}-token chunk at prefix {c}" for c, n in pre]
+    if dec:
+        parts.append(f"{len(dec)} decodes at mean context {float(np.mean(dec)):.0f}")
+    label = f"{spec.name}: {shape_name} layer, " + " + ".join(parts)
     return {
-        "workload": spec.name, "hidden": s.hidden, "n_q_heads": s.n_q_heads,
+        "workload": label, "name": spec.name, "hidden": s.hidden, "n_q_heads": s.n_q_heads,
         "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "d_ff": s.d_ff,
         "tokens": spec.num_tokens, "prefill_chunks": [list(p) for p in pre],
         "decodes": len(dec), "decode_ctx_mean": (float(np.mean(dec)) if dec else 0.0),
