@@ -55,6 +55,9 @@ def algorithmic_counts(spec):
     }
 
 
+ATTN_MODES = {"auto": 0, "fused": 1, "separate": 2}
+
+
 def pct(v):
     """median, p10 and p90 of a sorted list of milliseconds"""
     if not v:
@@ -115,6 +118,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--attention", default="auto", choices=sorted(ATTN_MODES),
+                    help="how prefill and decode attention are launched (auto = the library's "
+                         "choice)")
     ap.add_argument("--workload", default="cfg2",
                     help="cfg1..cfg5, cfgN_prefill_only / cfgN_decode_only (the batch split), or "
                          "p1_16dec_8k (16 decodes at 8K context, Qwen3-14B-shaped)")
@@ -193,7 +199,7 @@ def main():
     T = spec.num_tokens
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
-    batch = B.Batch(spec.q_start, spec.num_cached, table, dev)
+    batch = B.Batch(spec.q_start, spec.num_cached, table, dev, attention=ATTN_MODES[args.attention])
     x = workloads.hidden_states(spec, dev)
     w = workloads.weights(spec, dev)
     kp, vp = kvcache.alloc_pools(pool, s.n_kv_heads, s.head_dim, dev, fill=0.0)
@@ -391,7 +397,7 @@ def model_bench(args, spec, dev):
     vocab = args.vocab or (128256 if s.hidden == 8192 else 151936)
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
-    batch = B.Batch(spec.q_start, spec.num_cached, table, dev)
+    batch = B.Batch(spec.q_start, spec.num_cached, table, dev, attention=ATTN_MODES[args.attention])
     # every layer has its own weights; the cached K/V of layer 0 is copied into every layer's
     # own pools (distinct memory, same values: the values do not change the work)
     kp0, vp0 = kvcache.alloc_pools(pool, s.n_kv_heads, s.head_dim, dev, fill=0.0)
