@@ -396,13 +396,16 @@ int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q
  * writes attn_out [T, Hq d]. Uses the batch workspace. hl_prefill_attention computes only rows of
  * sequences with q_len > 1, hl_decode_attention only rows of sequences with q_len == 1 (other
  * rows are left untouched). hl_attention computes both: when the batch holds both kinds it runs
- * them in ONE fused launch whose persistent workers share every compute unit between the
- * compute-bound prefill items and the bandwidth-bound decode units (the two attention paths of a
- * hybrid step are independent and overlap: "ConfluxServe" summary, "Why can linear layers be
- * batched but attention cannot?"; a fused prefill-decode kernel is what the overlap needs,
- * "Chunked prefill (stall-free batching), explained", "Simulated numbers: choosing the budget").
- * Its rows are bit-identical to those of the two separate entry points. hybrid_layer_step uses
- * the same path. */
+ * them either as two launches or in ONE fused launch whose persistent workers share every compute
+ * unit between the compute-bound prefill items and the bandwidth-bound decode units (the two
+ * attention paths of a hybrid step are independent and overlap: "ConfluxServe" summary, "Why can
+ * linear layers be batched but attention cannot?"; a fused prefill-decode kernel is what the
+ * overlap needs, "Chunked prefill (stall-free batching), explained", "Simulated numbers: choosing
+ * the budget"). batch->attention picks one, or lets the library choose from the batch (fused for
+ * a long prefill with many work items, or very large decode work; hl_attention_plan reports it).
+ * A prompt tile whose key range is long while the batch has few prefill work items is split into
+ * key-range parts merged by a second pass. Rows are bit-identical whichever launch form runs, and
+ * to those of the two separate entry points. hybrid_layer_step uses the same path. */
 int hl_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_kv_pages* kv,
                  const hl_block_table* block_table, hl_bf16* attn_out);
 int hl_prefill_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
