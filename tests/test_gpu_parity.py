@@ -126,6 +126,31 @@ def test_gemm_every_tile_shape(tile, epi, stream_k):
         assert_close(f64(c), ref, f"gemm {bm}x{bn} sk={stream_k}")
 
 
+@pytest.mark.parametrize("tile", [(128, 128), (160, 256), (256, 256)], ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
+def test_gemm_tall_one_tile(tile, epi):
+    """Many M tiles (34, the last ragged) in the one-tile schedule: every tile id maps to one
+    output tile, dealt across the XCDs."""
+    bm, bn = tile
+    m, n, k = 33 * bm + 7, 3 * bn, 128
+    say(f"gemm tall {bm}x{bn} epi={epi} m={m} n={n} k={k}")
+    a = _randn((m, k), 61 + bm)
+    w = _randn((n, k), 62 + bn, 0.05)
+    out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
+    res = _randn((m, out_n), 63) if epi == B.HL_EPI_RESIDUAL else None
+    c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt_tiled(a, w, c, bm, bn, 0, res, epi)
+    torch.cuda.synchronize()
+    A, W = f64(a), f64(w)
+    if epi == B.HL_EPI_SWIGLU:
+        ref = OL.swiglu(A, W, n // 2)
+    else:
+        ref = OL.linear(A, W)
+        if epi == B.HL_EPI_RESIDUAL:
+            ref = ref + f64(res)
+    assert_close(f64(c), ref, f"gemm tall {bm}x{bn}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 33, 64])
 @pytest.mark.parametrize("n,k", [(384, 320), (1024, 4096)])
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
