@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--compare-split", action="store_true",
+                    help="time the workload's mixed batch and its prefill-only and decode-only "
+                         "halves (cfg2..cfg5)")
     ap.add_argument("--attention", default="auto", choices=sorted(ATTN_MODES),
                     help="how prefill and decode attention are launched (auto = the library's "
                          "choice)")
@@ -192,6 +195,8 @@ def main():
     name = args.workload
     if args.serve:
         return serve_bench(args, dev)
+    if args.compare_split:
+        return split_bench(args, dev)
     spec = workloads.named_spec(name)
     if args.model_layers > 0:
         return model_bench(args, spec, dev)
@@ -368,6 +373,9 @@ def main():
         "decode_attn_hbm_gbps": None if dec_gbps is None else round(dec_gbps, 1),
         "decode_attn_hbm_frac": None if dec_gbps is None else round(dec_gbps / PEAK_HBM_GBPS, 4),
         "prefill_attn_tflops": None if pre_tflops is None else round(pre_tflops, 1),
+        # weight bytes of the four projections over their phase time (phases repeat one layer, so
+        # part of the weights may be served by the last-level cache)
+        "gemm_weight_gbps": round(cnt["weight_bytes"] / (gemm_us * 1e-6) / 1e9, 1),
         "kv_transfer": {
             "tokens": span_len, "bytes_per_layer_slice": 2 * xfer.numel(),
             "export_gbps": round(2 * 2 * xfer.numel() / (phase_us["kv_export"] * 1e-6) / 1e9, 1),
@@ -451,6 +459,59 @@ def model_bench(args, spec, dev):
         "layers": L, "vocab": vocab, "graph": bool(args.graph), "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the workload's layer shape)",
         "config": {**workloads.describe(spec), "parallelism": "none (1 GPU)"},
+    }), flush=True)
+
+
+def split_bench(args, dev):
+    """The workload's mixed batch against the same data split into a prefill-only and a
+    decode-only step (median step times, same process): what batching the decodes into the
+    prefill's linear layers costs ("Chunked prefill (stall-free batching), explained", "The
+    bottleneck: prefill-decode interference")."""
+    import torch
+
+    import workloads
+    from hybrid_prefill_decode_amd import binding as B
+    from hybrid_prefill_decode_amd import kvcache
+    cfg_id = int(args.workload[3:].split("_")[0])
+    res = {}
+    for variant in ("mixed", "prefill_only", "decode_only"):
+        spec = workloads.make_spec(cfg_id, variant)
+        s = spec.shape
+        table, pool = workloads.block_table(spec)
+        cfg = B.layer_cfg(s)
+        batch = B.Batch(spec.q_start, spec.num_cached, table, dev)
+        x = workloads.hidden_states(spec, dev)
+        w = workloads.weights(spec, dev)
+        kp, vp = kvcache.alloc_pools(pool, s.n_kv_heads, s.head_dim, dev, fill=0.0)
+        for si, (c, _) in enumerate(spec.seqs):
+            if c:
+                k, v = workloads.cached_kv(spec, si, dev)
+                kvcache.write_positions(kp, vp, table[si], range(c), k, v)
+        out = torch.empty(spec.num_tokens, s.hidden, dtype=torch.bfloat16, device=dev)
+        ws = B.alloc_workspace(cfg, batch, dev)
+        step = lambda: B.hybrid_layer_step(cfg, batch, x, w, kp, vp, out, ws)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record()
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        res[variant] = pct(sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)))
+        print(f"# {variant}: {res[variant]}", file=sys.stderr, flush=True)
+        del kp, vp, w, x, out, ws
+        torch.cuda.empty_cache()
+    mixed = res["mixed"]["median"]
+    split = res["prefill_only"]["median"] + res["decode_only"]["median"]
+    print(json.dumps({
+        "experiment": "mixed_vs_split", "workload": args.workload,
+        "step_ms": res, "mixed_ms": mixed, "prefill_plus_decode_ms": round(split, 4),
+        "mixed_over_split": round(mixed / split, 4),
+        "decode_alone_ms": res["decode_only"]["median"],
+        "extra_for_decodes_in_mixed_ms": round(mixed - res["prefill_only"]["median"], 4),
+        "data": "synthetic (seeded), the workload's batch and its two halves",
     }), flush=True)
 
 
