@@ -544,8 +544,8 @@ def serve_bench(args, dev):
         prompts, outs = prompts.astype(int), outs.astype(int)
         arrive = np.cumsum(rng.exponential(1000.0 / args.rate, n_req))  # ms
         mbs = (8192 + 4 * args.mean_output + 15) // 16 + 1
-        eng = SV.Engine(shape, L, vocab, num_blocks=args.kv_blocks, max_blocks_per_seq=mbs,
-                        device=dev, budget=args.budgets[0], max_seqs=256)
+        eng = SV.Engine(shape, **workloads.engine_model(shape, L, vocab, args.kv_blocks, dev),
+                        max_blocks_per_seq=mbs, device=dev, budget=args.budgets[0], max_seqs=256)
         kw = dict(layer_params=L * shape.weight_params, head_params=vocab * shape.hidden,
                   hidden=shape.hidden, layers=L,
                   kv_bytes_per_token=2 * L * shape.n_kv_heads * shape.head_dim * 2)
@@ -598,7 +598,7 @@ def serve_bench(args, dev):
     if args.serve == "chunks":
         L = args.model_layers or 36
         prompt = 8192
-        eng = SV.Engine(shape, L, vocab, num_blocks=prompt // 16 + 8,
+        eng = SV.Engine(shape, **workloads.engine_model(shape, L, vocab, prompt // 16 + 8, dev),
                         max_blocks_per_seq=prompt // 16 + 2, device=dev, budget=prompt,
                         max_seqs=4)
         res = {}
@@ -629,7 +629,8 @@ def serve_bench(args, dev):
     # cliff: one prompt chunk at prefix 0 for sizes at and just past tile multiples, whole model
     # iteration, and the gate/up GEMM alone with the per-launch tile choice vs a fixed 256x256 tile
     L = args.model_layers or 36
-    eng = SV.Engine(shape, L, vocab, num_blocks=160, max_blocks_per_seq=140, device=dev,
+    eng = SV.Engine(shape, **workloads.engine_model(shape, L, vocab, 160, dev),
+                    max_blocks_per_seq=140, device=dev,
                     budget=4096, max_seqs=1)
     sizes = (256, 257, 512, 513, 1024, 1025, 2048, 2049)
 

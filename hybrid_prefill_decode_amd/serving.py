@@ -5,19 +5,18 @@ The loop is the chunked-prefill iteration ("Chunked prefill (stall-free batching
 "How it works, step by step"): schedule within the budget, one forward pass over the flattened
 tokens, completed prompts take their first token and decode from the next iteration. Everything
 numeric happens in the library; this module moves host arrays to the device and back, and keeps
-the clock. Prompt token ids are synthetic (a fixed function of request id and position).
+the clock. The caller provides the model (weights, KV pools, embedding, final norm, LM head) and
+the prompts' token ids.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional, Sequence
 
 import numpy as np
 import torch
 
-import workloads
 from . import binding as B
-from . import kvcache
 
 
 @dataclass
@@ -32,27 +31,26 @@ class IterationRecord:
     emitted: List[int] = field(default_factory=list)   # request ids that took a token
 
 
-def prompt_token(rid: int, pos: np.ndarray, vocab: int) -> np.ndarray:
-    return ((rid * 1000003 + pos * 7919) % vocab).astype(np.int32)
-
-
 class Engine:
-    def __init__(self, shape: workloads.LayerShape, layers: int, vocab: int, num_blocks: int,
-                 max_blocks_per_seq: int, device: str = "cuda", seed: int = 2024,
-                 pool_fill: float = 0.0, **sched):
+    """shape: the layer dimensions (hidden, n_q_heads, n_kv_heads, head_dim, d_ff, rms_eps,
+    rope_theta); layer_weights / pools: per layer, the weight dict and the (K, V) pools of
+    `num_blocks` pages each; embed / lm_head [vocab, hidden], final_norm [hidden];
+    prompt_tokens(request id, positions) -> int32 token ids of those prompt positions."""
+
+    def __init__(self, shape, layer_weights: Sequence[Dict[str, torch.Tensor]],
+                 pools: Sequence, embed: torch.Tensor, final_norm: torch.Tensor,
+                 lm_head: torch.Tensor, num_blocks: int, max_blocks_per_seq: int,
+                 prompt_tokens: Callable[[int, np.ndarray], np.ndarray], device: str = "cuda",
+                 **sched):
+        vocab = int(embed.shape[0])
         self.shape, self.vocab, self.dev = shape, vocab, device
         self.cfg = B.layer_cfg(shape)
         self.num_blocks, self.mb = num_blocks, max_blocks_per_seq
+        self.prompt_tokens = prompt_tokens
         self.reset(**sched)
-        base = workloads.custom_spec(shape, [(0, 1)], seed)
-        self.layer_w = [workloads.weights(workloads.layer_spec(base, l), device)
-                        for l in range(layers)]
-        self.pools = [kvcache.alloc_pools(num_blocks, shape.n_kv_heads, shape.head_dim, device,
-                                          fill=pool_fill) for _ in range(layers)]
-        t = workloads.model_tensors(base, vocab, device)
-        self.tensors = t
-        self.model = B.ModelHandle(self.layer_w, self.pools, t["embed"], t["final_norm"],
-                                   t["lm_head"])
+        self.layer_w, self.pools = list(layer_weights), list(pools)
+        self.tensors = {"embed": embed, "final_norm": final_norm, "lm_head": lm_head}
+        self.model = B.ModelHandle(self.layer_w, self.pools, embed, final_norm, lm_head)
         self.ws = torch.empty(256, dtype=torch.uint8, device=device)
         self.logits = torch.empty(1, vocab, dtype=torch.bfloat16, device=device)
         self.next = torch.empty(1, dtype=torch.int32, device=device)
@@ -81,8 +79,8 @@ class Engine:
                 toks[qs[s]] = b["decode_tokens"][s]
                 dec += 1
             else:
-                toks[qs[s]:qs[s + 1]] = prompt_token(int(b["request_ids"][s]),
-                                                     c + np.arange(n), self.vocab)
+                toks[qs[s]:qs[s + 1]] = self.prompt_tokens(int(b["request_ids"][s]),
+                                                           c + np.arange(n))
                 pre += n
             vis += n * c + n * (n + 1) // 2
         batch = B.Batch(qs, nc, b["table"], self.dev)

@@ -33,8 +33,9 @@ def oracle_logits(eng, layers, tokens):
 def test_engine_chunked_requests_vs_oracle():
     shape = workloads.LayerShape(256, 4, 2, 64, 512)
     L, vocab = 2, 512
-    eng = SV.Engine(shape, L, vocab, num_blocks=48, max_blocks_per_seq=16, device=DEV, seed=7,
-                    pool_fill=float("nan"), budget=48, max_seqs=3)
+    eng = SV.Engine(shape, **workloads.engine_model(shape, L, vocab, 48, DEV, seed=7,
+                                                    pool_fill=float("nan")),
+                    max_blocks_per_seq=16, device=DEV, budget=48, max_seqs=3)
     reqs = {0: (150, 4), 1: (100, 3), 2: (23, 2)}  # prompt length, tokens to generate
     late = {5: 2}  # request 2 arrives before iteration 5
     for rid in (0, 1):
@@ -59,7 +60,7 @@ def test_engine_chunked_requests_vs_oracle():
             if not b["emits"][s]:
                 continue
             p = reqs[rid][0]
-            seq = list(SV.prompt_token(rid, np.arange(p), vocab)) + gen[rid]
+            seq = list(workloads.prompt_token(rid, np.arange(p), vocab)) + gen[rid]
             assert_close(f64(logits[s]), oracle_logits(eng, layers, seq),
                          f"logits of request {rid} token {len(gen[rid])}")
             gen[rid].append(int(picks[s]))

@@ -271,3 +271,31 @@ def model_tensors(spec: BatchSpec, vocab: int, device="cpu") -> Dict[str, "objec
         "lm_head": _randn_bf16((vocab, s.hidden), 0.02, _torch_seed(ss, 2), device),
         "final_norm": torch.ones(s.hidden, dtype=torch.bfloat16, device=device),
     }
+
+
+# ---------------------------------------------------------------------- serving-loop inputs
+
+def prompt_token(rid: int, pos: np.ndarray, vocab: int) -> np.ndarray:
+    """Synthetic prompt token ids: a fixed function of request id and position."""
+    return ((rid * 1000003 + pos * 7919) % vocab).astype(np.int32)
+
+
+def engine_model(shape: LayerShape, layers: int, vocab: int, num_blocks: int, device="cuda",
+                 seed: int = 2024, pool_fill: float = 0.0) -> dict:
+    """Random-init model of `layers` layers for the serving loop: per-layer weights (each layer
+    its own seed), KV pools of `num_blocks` pages per layer, embedding, final norm and LM head
+    (keyword arguments of serving.Engine)."""
+    import torch
+    base = custom_spec(shape, [(0, 1)], seed)
+    layer_w = [weights(layer_spec(base, l), device) for l in range(layers)]
+    pools = []
+    for _ in range(layers):
+        k = torch.full((num_blocks, shape.n_kv_heads, BLOCK_SIZE, shape.head_dim), pool_fill,
+                       dtype=torch.bfloat16, device=device)
+        v = torch.full((num_blocks, shape.n_kv_heads, shape.head_dim, BLOCK_SIZE), pool_fill,
+                       dtype=torch.bfloat16, device=device)
+        pools.append((k, v))
+    t = model_tensors(base, vocab, device)
+    return {"layer_weights": layer_w, "pools": pools, "embed": t["embed"],
+            "final_norm": t["final_norm"], "lm_head": t["lm_head"], "num_blocks": num_blocks,
+            "prompt_tokens": lambda rid, pos: prompt_token(rid, pos, vocab)}
