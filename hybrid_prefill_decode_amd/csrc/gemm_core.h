@@ -94,6 +94,12 @@ struct Cfg {
   static_assert(A_CH * kThreads * 16 == A_BYTES && W_CH * kThreads * 16 == W_BYTES, "staging");
 };
 
+// Load depth of the one-tile main loop (k-steps from a tile's load to its use). The 128-wide
+// tiles have the shortest k-steps and take their weights from HBM in a model iteration, so their
+// loads get an extra k-step in flight.
+template <int BM, int BN>
+constexpr int kLoadDepth = BN == 128 ? 3 : 2;
+
 // fp32 row stride (floats) of the RoPE epilogue's LDS stage of a BN-wide tile
 template <int BN>
 constexpr int kStageRow = BN + 4;
@@ -119,7 +125,7 @@ constexpr int read_after(int q, int nm, int nr) {
 }
 
 // One tile's K range [kb, ke) into acc (acc zeroed here).
-template <int EPI, int BM, int BN>
+template <int EPI, int BM, int BN, int D = kLoadDepth<BM, BN>>
 HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N,
                      int K, int mt, int nt, int kb, int ke, uint8_t* smem,
                      f32x4 (&acc)[Cfg<BM, BN>::MT][Cfg<BM, BN>::NT]) {
@@ -176,12 +182,27 @@ HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ 
   int w_row[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) w_row[t] = 128 * w_block_row<EPI, BN, C::WN, NT>(wn, t);
+  if constexpr (BN == 128) {
+    // cleared through the matrix core: with a plain zero store the split-K kernels' loops moved
+    // every accumulator block to other registers once per k-step (the 256-wide loops are clean
+    // either way and keep the plain store)
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{};
+      for (int t = 0; t < NT; ++t) acc[i][t] = mfma16x16x32(z, z, f32x4{});
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{};
+  }
 
-  u32x4 rg[NCH];
+  // D = load depth: tile t + D - 1 is loaded while tile t is multiplied. D = 3 keeps two staging
+  // register sets in flight (k-step t writes set (t - kb) % 2, which holds tile t + 1, to LDS and
+  // refills it with tile t + 3), which gives a load two k-steps to arrive instead of one.
+  static_assert(D == 2 || D == 3, "load depth");
+  u32x4 rg[D - 1][NCH];
   u32x4 fa[MT], fw[2][NT];
   // fragment read j of a step: W block j (j < NT) into set `set`, else A block j - NT
   auto rd1 = [&](const uint8_t* base, int set, int ks, int j) {
@@ -190,12 +211,29 @@ HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ 
   };
 
   const int last = (ke - 1) * BK;
+  // With two staging sets the loop runs k-steps in pairs; an odd count starts one step early on
+  // a tile of zeros (A and W), which adds nothing to the sums. (A lone last step after the paired
+  // loop, or a second loop for odd counts, makes the register allocator rotate the accumulators
+  // inside the loop.)
+  const int kf = D == 3 ? kb - ((ke - kb) & 1) : kb;
+  if (kf < kb) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) rg[i] = gload(i, kb * BK);
+    for (int i = 0; i < NCH; ++i) rg[0][i] = u32x4{0u, 0u, 0u, 0u};
+  } else {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(smem + dst(i)) = rg[i];
+    for (int i = 0; i < NCH; ++i) rg[0][i] = gload(i, kb * BK);
+  }
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) rg[i] = gload(i, min((kb + 1) * BK, last));
+  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4*>(smem + dst(i)) = rg[0][i];
+  // two sets are loaded one after the other, so the wait counts at the loop head are the steady
+  // ones
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s) {
+    if constexpr (D == 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) rg[s][i] = gload(i, min((kf + 1 + s) * BK, last));
+  }
+  if constexpr (D == 3) __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NR; ++j) rd1(smem, 0, 0, j);
@@ -204,11 +242,11 @@ HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ 
   // (j + 1) NM / NR - 1, which for an A block j - NT is never before the step's last use of it;
   // staging pair i (step 0 only) follows MFMA i NM / NCH. Step 1 follows the barrier and reads
   // the next tile's step-0 fragments from the other buffer.
-  for (int kt = kb; kt < ke; ++kt) {
-    const int buf = (kt - kb) & 1;
+  auto kstep = [&](const int kt, u32x4 (&rgs)[NCH]) __attribute__((always_inline)) {
+    const int buf = (kt - kf) & 1;
     const uint8_t* ab = smem + buf * C::STAGE;
     uint8_t* nb = smem + (buf ^ 1) * C::STAGE;
-    const int knext = min((kt + 2) * BK, last);  // past the end: re-read the last tile (unused)
+    const int knext = min((kt + D) * BK, last);  // past the end: re-read the last tile (unused)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = ks, nx = ks ^ 1;
@@ -224,16 +262,24 @@ HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ 
         acc[q / NT][q % NT] = mfma16x16x32(fa[q / NT], fw[cur][q % NT], acc[q / NT][q % NT]);
         const int si = stage_after(q, NM, NCH), rj = read_after(q, NM, NR);
         if (ks == 0 && si >= 0) {
-          *reinterpret_cast<u32x4*>(nb + dst(si)) = rg[si];
+          *reinterpret_cast<u32x4*>(nb + dst(si)) = rgs[si];
           // keeps the write before the load that reuses its registers: without the pin the
           // register allocator splits the staging ranges and evicts an accumulator set
           __builtin_amdgcn_sched_barrier(0);
-          rg[si] = gload(si, knext);
+          rgs[si] = gload(si, knext);
         }
         if (rj >= 0) rd1(rbase, nx, rks, rj);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  if constexpr (D == 3) {
+    for (int kt = kf; kt < ke; kt += 2) {
+      kstep(kt, rg[0]);
+      kstep(kt + 1, rg[1]);
+    }
+  } else {
+    for (int kt = kb; kt < ke; ++kt) kstep(kt, rg[0]);
   }
   // the next call (stream-K) or the epilogue reuses the LDS
   __syncthreads();
@@ -684,14 +730,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
   const int nk = K / BK;
   const int kb = (int)((long)s * nk / splits), ke = (int)((long)(s + 1) * nk / splits);
   f32x4 acc[MT][NT];
-  mainloop<EPI, BM, BN>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
+  mainloop<EPI, BM, BN, 2>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* dst = part + ((size_t)s * tiles + tile) * BM * BN + lane * 4;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) = acc[i][t];
+      *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) =
+          f32x4{agpr_read(acc[i][t][0]), agpr_read(acc[i][t][1]), agpr_read(acc[i][t][2]),
+                agpr_read(acc[i][t][3])};
 }
 
 // Split-K fix-up, plain / residual: a thread takes one lane quad (4 columns x 4 rows) of one
