@@ -125,7 +125,7 @@ constexpr int read_after(int q, int nm, int nr) {
 }
 
 // One tile's K range [kb, ke) into acc (acc zeroed here).
-template <int EPI, int BM, int BN, int D = kLoadDepth<BM, BN>>
+template <int EPI, int BM, int BN, int D = kLoadDepth<BM, BN>, bool MC = BN == 128>
 HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N,
                      int K, int mt, int nt, int kb, int ke, uint8_t* smem,
                      f32x4 (&acc)[Cfg<BM, BN>::MT][Cfg<BM, BN>::NT]) {
@@ -182,10 +182,10 @@ HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ 
   int w_row[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) w_row[t] = 128 * w_block_row<EPI, BN, C::WN, NT>(wn, t);
-  if constexpr (BN == 128) {
+  if constexpr (MC) {
     // cleared through the matrix core: with a plain zero store the split-K kernels' loops moved
-    // every accumulator block to other registers once per k-step (the 256-wide loops are clean
-    // either way and keep the plain store)
+    // every accumulator block to other registers once per k-step (the 256-wide one-tile loops
+    // are clean either way and keep the plain store)
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -730,16 +730,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
   const int nk = K / BK;
   const int kb = (int)((long)s * nk / splits), ke = (int)((long)(s + 1) * nk / splits);
   f32x4 acc[MT][NT];
-  mainloop<EPI, BM, BN, 2>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
+  mainloop<EPI, BM, BN, 2, true>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* dst = part + ((size_t)s * tiles + tile) * BM * BN + lane * 4;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) =
-          f32x4{agpr_read(acc[i][t][0]), agpr_read(acc[i][t][1]), agpr_read(acc[i][t][2]),
-                agpr_read(acc[i][t][3])};
+      *reinterpret_cast<f32x4*>(dst + ((wave * MT + i) * NT + t) * 256) = acc[i][t];
 }
 
 // Split-K fix-up, plain / residual: a thread takes one lane quad (4 columns x 4 rows) of one
