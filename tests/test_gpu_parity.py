@@ -151,6 +151,28 @@ def test_gemm_tall_one_tile(tile, epi):
     assert_close(f64(c), ref, f"gemm tall {bm}x{bn}")
 
 
+@pytest.mark.parametrize("tile", [(128, 128), (160, 128), (224, 128), (256, 128)],
+                         ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("k", [64, 192, 256])
+@pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL])
+def test_gemm_load_depth_k_steps(tile, k, epi):
+    """The 128-wide tiles run their k-steps in pairs with two staging sets in flight; an odd count
+    (1 or 3 here) starts one step early on a tile of zeros, an even one (4) does not."""
+    bm, bn = tile
+    m, n = 2 * bm + 5, 2 * bn
+    say(f"gemm load depth {bm}x{bn} epi={epi} m={m} n={n} k={k}")
+    a = _randn((m, k), 71 + k)
+    w = _randn((n, k), 72 + bm, 0.05)
+    res = _randn((m, n), 73) if epi == B.HL_EPI_RESIDUAL else None
+    c = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt_tiled(a, w, c, bm, bn, 0, res, epi)
+    torch.cuda.synchronize()
+    ref = OL.linear(f64(a), f64(w))
+    if epi == B.HL_EPI_RESIDUAL:
+        ref = ref + f64(res)
+    assert_close(f64(c), ref, f"gemm load depth {bm}x{bn} k={k}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 33, 64])
 @pytest.mark.parametrize("n,k", [(384, 320), (1024, 4096)])
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
