@@ -142,6 +142,11 @@ _SIGS = {
                               ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
     "hl_decode_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
                              ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
+    "hl_attention_build_lists": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(KvPages),
+                                  ctypes.POINTER(BlockTable)], ctypes.c_int),
+    "hl_attention_run": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable), ctypes.c_void_p,
+                          ctypes.c_int32], ctypes.c_int),
 }
 
 
@@ -496,3 +501,27 @@ def prefill_attention(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream
 
 def decode_attention(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream=None) -> None:
     _attn("hl_decode_attention", cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, stream)
+
+
+ATTN_PREFILL, ATTN_DECODE, ATTN_BOTH = 1, 2, 3
+
+
+def attention_build_lists(cfg, b, k_pool, v_pool, workspace, stream=None) -> None:
+    """hl_attention_build_lists: the batch's attention work lists into the workspace."""
+    d = _desc(cfg, b, None, workspace, stream)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hl_attention_build_lists(ctypes.byref(d), ctypes.byref(kv), ctypes.byref(bt)),
+           "hl_attention_build_lists")
+
+
+def attention_run(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, q_lo=None,
+                  paths: int = ATTN_BOTH, stream=None) -> None:
+    """hl_attention_run on lists built by attention_build_lists (paths: 1 prompt-chunk rows,
+    2 decode rows, 3 both; q_lo: optional low half of a two-part query)."""
+    d = _desc(cfg, b, None, workspace, stream)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hl_attention_run(ctypes.byref(d), _ptr(q_rot), _ptr(q_lo), ctypes.byref(kv),
+                                  ctypes.byref(bt), _ptr(attn_out), int(paths)),
+           "hl_attention_run")

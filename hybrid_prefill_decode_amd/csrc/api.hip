@@ -712,6 +712,29 @@ int hl_decode_attention(const hl_batch_desc* batch, const hl_bf16* q_rot, const 
   return attention_entry(batch, q_rot, kv, bt, attn_out, false, true);
 }
 
+int hl_attention_build_lists(const hl_batch_desc* batch, const hl_kv_pages* kv,
+                             const hl_block_table* bt) {
+  HostPlan hp;
+  int rc = prepare(batch, kv, bt, &hp);
+  if (rc || batch->num_seqs == 0) return rc;
+  const hl::Plan dp = device_plan(hp, batch->workspace);
+  return hip_rc(hl::launch_plan(batch->q_start, batch->num_cached, batch->num_seqs, dp,
+                                static_cast<hipStream_t>(batch->stream)));
+}
+
+int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                     const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                     int32_t paths) {
+  if (paths < 1 || paths > 3) return HL_ERR_ARG;
+  HostPlan hp;
+  int rc = prepare(batch, kv, bt, &hp);
+  if (rc || batch->num_seqs == 0) return rc;
+  if (!q_rot || !attn_out) return HL_ERR_NULL;
+  if (!aligned16(q_rot) || !aligned16(attn_out) || (q_lo && !aligned16(q_lo))) return HL_ERR_ALIGN;
+  return run_attention(batch, q_rot, q_lo, kv, bt, attn_out, hp, (paths & 1) != 0,
+                       (paths & 2) != 0, true);
+}
+
 int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
                       const hl_block_table* bt, hl_bf16* out) {
   HostPlan hp;

@@ -6,8 +6,10 @@
 // offset p_done; then waiting requests in arrival order while budget, sequence slots and KV blocks
 // remain, each given as many prompt tokens as fit. A request whose last prompt chunk completes
 // takes its first token from that iteration and decodes from the next one. The budget is fixed,
-// or follows the adaptive rule of chapter 7.8 ("Dynamic chunk sizing"): the largest chunk while
-// nothing decodes, the smallest once decodes reach a pressure threshold, linear in between.
+// or the iteration's prompt share follows chapter 7.8's dynamic chunk sizing ("Priority and
+// Preemption Policies"): the largest chunk while nothing decodes, the smallest once decodes reach
+// a pressure threshold, the straight line from the base chunk down to the smallest in between
+// (rounded down to whole tokens); decode tokens come on top of that share.
 //
 // KV blocks (16 tokens each) come from one free pool shared by all layers' pools, lowest free id
 // first. Reading of "the request can be allocated": a request is admitted only if blocks for its
@@ -74,8 +76,10 @@ int hl_sched_submit(hl_sched* s, int32_t request_id, int32_t prompt_len, int32_t
                     int32_t* handle) {
   if (!s || !handle) return HL_ERR_NULL;
   if (prompt_len < 1 || max_new_tokens < 1) return HL_ERR_ARG;
-  if (blocks_for((int64_t)prompt_len + max_new_tokens - 1) > s->p.max_blocks_per_seq)
-    return HL_ERR_BLOCK;
+  // a request whose lifetime outgrows its table row or the whole pool could never be admitted,
+  // and arrival-order admission would then hold back every later request behind it
+  const int32_t need = blocks_for((int64_t)prompt_len + max_new_tokens - 1);
+  if (need > s->p.max_blocks_per_seq || need > s->p.num_blocks) return HL_ERR_BLOCK;
   Req r;
   r.id = request_id;
   r.prompt_len = prompt_len;
@@ -86,40 +90,35 @@ int hl_sched_submit(hl_sched* s, int32_t request_id, int32_t prompt_len, int32_t
   return HL_OK;
 }
 
-// Budget of the next iteration: fixed, or the adaptive chunk plus one token per decode (decode
-// tokens count against the budget, so the prefill share is what the rule returns).
-static int32_t next_budget(const hl_sched* s) {
-  if (!s->p.adaptive) return s->p.budget;
-  const int32_t d = (int32_t)s->decoding.size();
-  int32_t chunk;
-  if (d == 0) {
-    chunk = s->p.max_chunk;
-  } else if (d >= s->p.pressure_threshold) {
-    chunk = s->p.min_chunk;
-  } else {
-    const double ratio = (double)d / s->p.pressure_threshold;
-    chunk = (int32_t)(s->p.base_chunk - ratio * (s->p.base_chunk - s->p.min_chunk));
-    chunk = std::max(s->p.min_chunk, std::min(chunk, s->p.base_chunk));
-  }
-  return chunk + d;
+// Prompt tokens the next iteration may carry after every decode has its one token. Adaptive:
+// max_chunk at no decode load, min_chunk at or past the pressure threshold, and in between
+// floor(base - d (base - min) / threshold) = base - ceil(d (base - min) / threshold), in exact
+// integer arithmetic.
+static int64_t prompt_share(const hl_sched* s) {
+  const int64_t d = (int64_t)s->decoding.size();
+  if (!s->p.adaptive) return (int64_t)s->p.budget - d;
+  const hl_sched_params& p = s->p;
+  if (d == 0) return p.max_chunk;
+  if (d >= p.pressure_threshold) return p.min_chunk;
+  const int64_t span = (int64_t)p.base_chunk - p.min_chunk;
+  return p.base_chunk - (d * span + p.pressure_threshold - 1) / p.pressure_threshold;
 }
 
 int hl_sched_next(hl_sched* s, hl_sched_batch* out) {
   if (!s || !out) return HL_ERR_NULL;
   s->b_handle.clear();
   s->n_new.clear();
-  int32_t left = next_budget(s);
-  // 1. every running decode: one token
+  int64_t left = prompt_share(s);
+  // 1. every running decode: one token (on top of the prompt share)
   for (int32_t h : s->decoding) {
     s->b_handle.push_back(h);
     s->n_new.push_back(1);
-    --left;
   }
   // 2. prompts already being prefilled, then 3. admissions in arrival order
   for (int32_t h : s->prefill) {
     if (left <= 0) break;
     const Req& r = s->reqs[h];
-    const int32_t n = std::min(left, r.prompt_len - r.prefilled);
+    const int32_t n = (int32_t)std::min<int64_t>(left, r.prompt_len - r.prefilled);
     s->b_handle.push_back(h);
     s->n_new.push_back(n);
     left -= n;
@@ -137,7 +136,7 @@ int hl_sched_next(hl_sched* s, hl_sched_batch* out) {
     }
     r.state = kPrefill;
     s->prefill.push_back(h);
-    const int32_t n = std::min(left, r.prompt_len);
+    const int32_t n = (int32_t)std::min<int64_t>(left, r.prompt_len);
     s->b_handle.push_back(h);
     s->n_new.push_back(n);
     left -= n;

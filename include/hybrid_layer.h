@@ -229,9 +229,12 @@ int hl_model_step(const hl_model* model, const hl_batch_desc* batch, const int32
  * iteration fills a token budget with one token per running decode, then the next chunk of the
  * prompt being prefilled, then waiting requests in arrival order while budget, sequence slots and
  * KV blocks remain ("Chunked prefill (stall-free batching), explained", "How it works, step by
- * step"). With adaptive != 0 the prefill share follows chapter 7.8's dynamic chunk sizing:
- * max_chunk while no request decodes, min_chunk once pressure_threshold or more do, linear from
- * base_chunk to min_chunk in between (decode tokens come on top). A request is admitted only when
+ * step"). With adaptive != 0 the prefill share follows chapter 7.8's dynamic chunk sizing
+ * ("Priority and Preemption Policies"): max_chunk while no request decodes, min_chunk once
+ * pressure_threshold or more do, and with d decoding in between the line from base_chunk down to
+ * min_chunk rounded down, base_chunk - ceil(d (base_chunk - min_chunk) / pressure_threshold).
+ * That share is the iteration's whole prompt-token count, however many prompts it is spread
+ * over; the decode tokens come on top of it. A request is admitted only when
  * blocks for its whole lifetime (prompt + outputs, 16 tokens per block) are free; they are taken
  * from one free list of num_blocks ids (the pages of every layer's pool) and returned when it
  * finishes, so nothing is ever preempted. Host memory only; not thread-safe. */
@@ -267,7 +270,9 @@ typedef struct hl_sched hl_sched;
 hl_sched* hl_sched_create(const hl_sched_params* params);
 void hl_sched_destroy(hl_sched* sched);
 /* Queue a request (arrival order = call order). HL_ERR_ARG for lengths < 1, HL_ERR_BLOCK if its
- * lifetime needs more than max_blocks_per_seq blocks. *handle: its index. */
+ * lifetime needs more than max_blocks_per_seq blocks or more than the pool's num_blocks (such a
+ * request could never be admitted, and admission in arrival order would then hold back every
+ * later one). *handle: its index. */
 int hl_sched_submit(hl_sched* sched, int32_t request_id, int32_t prompt_len,
                     int32_t max_new_tokens, int32_t* handle);
 /* The next iteration's batch (possibly empty: num_seqs == 0). */
@@ -320,18 +325,30 @@ int hl_kv_import(const hl_kv_span* span, const hl_bf16* src, hl_kv_pages* kv);
 /* ---- the phases the step is composed of (same conventions; used by tests and benchmarks) --- */
 
 /* y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain, rows x cols, all device bf16.
- * cols % 8 == 0. */
+ * cols % 8 == 0. No page defines the normalisation inside the layer: the pages name the linears
+ * and attention of the step, and RMSNorm is the norm of the layer shapes the step is measured on
+ * (a pre-norm block, the Qwen3 / Llama-70B shapes). This is its standard definition. Errors:
+ * HL_ERR_NULL, HL_ERR_ARG (rows < 0, cols not a positive multiple of 8, eps < 0), HL_ERR_ALIGN,
+ * HL_ERR_HIP. */
 int hl_rmsnorm(const hl_bf16* x, const hl_bf16* gain, hl_bf16* y, int32_t rows, int32_t cols,
                float eps, void* stream);
 
 /* RMSNorm split into its two factors, for a following linear layer: xg[r, :] = x[r, :] * gain
  * (bf16) and row_scale[r] = 1 / sqrt(mean(x[r, :]^2) + eps) (fp32 [rows]), so that
- * RMSNorm(x) W^T = row_scale * (xg W^T) with no rounding of the normalised row. cols % 8 == 0. */
+ * RMSNorm(x) W^T = row_scale * (xg W^T) with no rounding of the normalised row. cols % 8 == 0.
+ * As for hl_rmsnorm, no page defines the norm; it is the standard RMSNorm of the measured layer
+ * shapes, factored so that the token-batched linear that follows applies it. Errors as
+ * hl_rmsnorm. */
 int hl_rms_scale(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* row_scale,
                  int32_t rows, int32_t cols, float eps, void* stream);
 
 /* Token-batched linear layer C = s * (A W^T) with A [m, k] and W [n, k] (both k-contiguous), bf16
  * in, fp32 accumulation, bf16 out; s = row_scale[row] (fp32 [m]) or 1 when row_scale is NULL.
+ * The rows of A are the tokens of every request of the batch, prompt chunks and decodes alike:
+ * a linear layer treats each token row on its own, so one multiply serves the whole hybrid batch
+ * and reads the weights once ("ConfluxServe" summary, "Why can linear layers be batched but
+ * attention cannot?"; "Chunked prefill (stall-free batching), explained", "The bottleneck:
+ * prefill-decode interference", on decode rows riding along in the prompt's multiply).
  * epilogue:
  *   HL_EPI_NONE     c [m, n] = s * A W^T
  *   HL_EPI_RESIDUAL c [m, n] = residual [m, n] + s * A W^T
@@ -385,9 +402,18 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
 int hl_qkv_rope_append(const hl_batch_desc* batch, const hl_weights* weights, hl_bf16* q_rot,
                        hl_kv_pages* kv, const hl_block_table* block_table);
 
-/* Rotary embedding of q and k and KV append, on its own. qkv [num_tokens, (Hq + 2 Hkv) d] (device, the QKV
- * projection output); writes q_rot [num_tokens, Hq d] and the new K (rotated) and V rows into
- * their pages: position p of sequence s goes to block table[s][p / 16], slot p % 16. */
+/* Rotary embedding of q and k and KV append, on its own. qkv [num_tokens, (Hq + 2 Hkv) d]
+ * (device, the QKV projection output); writes q_rot [num_tokens, Hq d] and the new K (rotated)
+ * and V rows into their pages: position p of sequence s goes to block table[s][p / 16], slot
+ * p % 16. Every new token is written at its absolute position: a prompt chunk of n tokens after
+ * num_cached cached ones writes positions num_cached .. num_cached + n - 1 and a decode appends
+ * one ("Chunked prefill (stall-free batching), explained", "How it works, step by step", the
+ * forward pass over (start_pos, n) per request; "7.8 Disaggregated Prefill/Decode & Chunked
+ * Prefill", "Attention on Partial KV Caches", a chunk's keys and values written into the cache
+ * before its attention). Rotation: pair (j, j + d/2) turns by p * theta^(-2j/d), applied to q and
+ * k, never v. Only the slots of the batch's new tokens change; every other byte of both pools is
+ * left as it was. Errors: HL_ERR_NULL, HL_ERR_ALIGN, those of the batch descriptor
+ * (HL_ERR_SHAPE, HL_ERR_DESC) and of the table (HL_ERR_BLOCK), HL_ERR_HIP. */
 int hl_rope_kv_append(const hl_batch_desc* batch, const hl_bf16* qkv, hl_bf16* q_rot,
                       hl_kv_pages* kv, const hl_block_table* block_table);
 
@@ -414,6 +440,28 @@ int hl_prefill_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
 int hl_decode_attention(const hl_batch_desc* batch, const hl_bf16* q_rot,
                         const hl_kv_pages* kv, const hl_block_table* block_table,
                         hl_bf16* attn_out);
+
+/* The attention phase in two calls, as the layer step itself runs it: the work lists are built
+ * first (the step builds them in its first normalisation pass), then the kernels run on them.
+ * hl_attention_build_lists writes the batch's work lists (decode units, prefill tiles or
+ * key-range parts, merges) and zeroes the fused launch's work-queue counters in the batch
+ * workspace (one small kernel on batch->stream). hl_attention_run then runs attention on those
+ * lists: paths 1 = prompt-chunk rows only, 2 = decode rows only, 3 = both (fused in one launch or
+ * as two launches, as hl_attention chooses for the batch). q_lo (device [T, Hq d], optional) is
+ * the low half of a two-part query, bf16(q - bf16(q)) with q_rot = bf16(q): decode rows then score
+ * with q_rot + q_lo, as the layer step does; prompt-chunk rows ignore it; NULL means a one-part
+ * query. The batch (its descriptor values and its workspace) must be the one the lists were
+ * built for; a fused launch consumes the work-queue counters, so every run of paths 3 whose batch
+ * fuses needs a build of its own before it (the separate kernels only read the lists). Rows agree
+ * with hl_attention bit for bit when q_lo is NULL. The split is what makes each launch timeable on
+ * its own; the mathematics is that of hl_attention ("ConfluxServe" summary, "Why can linear
+ * layers be batched but attention cannot?"). Errors: those of hl_attention, HL_ERR_ARG for paths
+ * outside 1..3. */
+int hl_attention_build_lists(const hl_batch_desc* batch, const hl_kv_pages* kv,
+                             const hl_block_table* block_table);
+int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                     const hl_kv_pages* kv, const hl_block_table* block_table, hl_bf16* attn_out,
+                     int32_t paths);
 
 #ifdef __cplusplus
 }

@@ -335,6 +335,45 @@ def check_block_permutation_addresses():
         assert len(set(map(tuple, a[:, 2:].tolist()))) == a.shape[0]
 
 
+def check_cfg1_kv_slots_literal():
+    """Where the tiny workload's new K/V rows land, worked by hand from the reading that a decode
+    "at context c" appends position c and a chunk (c, n) writes positions c .. c+n-1, position p
+    going to slot p mod 16 of logical page p // 16 of its own table row ("Chunked prefill ...
+    explained", "How it works, step by step"; paged blocks of "7.8 ...", "Attention on Partial KV
+    Caches"). The block table is written out by hand with scrambled ids, and the expected
+    (sequence, position, block, slot) rows below are literals: decode at 32 -> slot 0 of a fresh
+    page 2; 57 -> slot 9 of page 3; 96 -> slot 0 of page 6; 128 -> slot 0 of page 8; the chunk
+    (64, 64) fills logical pages 4..7 completely."""
+    spec = workloads.make_spec(1)
+    assert spec.seqs == [(64, 64), (32, 1), (57, 1), (96, 1), (128, 1)]
+    table = np.full((5, 9), -1, dtype=np.int32)
+    table[0, :8] = [17, 3, 29, 8, 41, 12, 36, 5]
+    table[1, :3] = [22, 40, 9]
+    table[2, :4] = [1, 33, 27, 14]
+    table[3, :7] = [31, 6, 19, 44, 2, 25, 38]
+    table[4, :9] = [10, 34, 7, 21, 45, 0, 28, 16, 30]
+    want = [(0, 64 + j, 41, j) for j in range(16)] + [(0, 80 + j, 12, j) for j in range(16)] + \
+           [(0, 96 + j, 36, j) for j in range(16)] + [(0, 112 + j, 5, j) for j in range(16)] + \
+           [(1, 32, 9, 0), (2, 57, 14, 9), (3, 96, 38, 0), (4, 128, 30, 0)]
+    rng = np.random.default_rng(3)
+    sh = spec.shape
+    w = {"attn_norm": np.ones(sh.hidden), "mlp_norm": np.ones(sh.hidden),
+         "w_qkv": 0.02 * rng.standard_normal((sh.qkv_cols, sh.hidden)),
+         "w_o": 0.02 * rng.standard_normal((sh.hidden, sh.n_q_heads * sh.head_dim)),
+         "w_gate_up": 0.02 * rng.standard_normal((2 * sh.d_ff, sh.hidden)),
+         "w_down": 0.02 * rng.standard_normal((sh.hidden, sh.d_ff))}
+    x = rng.standard_normal((spec.num_tokens, sh.hidden))
+    cached = [(rng.standard_normal((c, sh.n_kv_heads, sh.head_dim)),
+               rng.standard_normal((c, sh.n_kv_heads, sh.head_dim))) for c, _ in spec.seqs]
+    r = OL.layer_step(sh, x, w, spec.seqs, cached, table)
+    got = [tuple(int(v) for v in row) for row in r["kv_addr"]]
+    assert got == want, got
+    # the addressed rows are the new tokens' K/V in batch row order: the decode at context 57
+    # (batch row 65) carries the rotated K of that token alone
+    alone = OL.sequence_step(sh, x[65:66], w, 57, *cached[2])
+    assert _rel(r["k_new"][65], alone["k_new"][0]) < TOL
+
+
 # --------------------------------------------------------------------------- KV transfer
 
 def _code(b, h, s, d):
@@ -474,34 +513,61 @@ def check_greedy_hand_values():
 
 # --------------------------------------------------------------------------- scheduler
 
-def check_scheduler_hand_trace():
-    """The hand-worked trace in tests/golden/scheduler_trace.txt (budget 8, 2 slots)."""
+def _golden_lines(name):
     import os
-    path = os.path.join(os.path.dirname(__file__), "golden", "scheduler_trace.txt")
-    want = [l.split(": ", 1)[1].strip() for l in open(path) if l[0].isdigit()]
-    s = OS.Scheduler(budget=8, max_seqs=2, num_blocks=40)
-    names = {0: "A", 1: "B", 2: "C"}
-    for rid, p, o in [(0, 10, 3), (1, 5, 1), (2, 3, 2)]:
-        s.submit(rid, p, o)
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    return [l.split(":", 1)[1].strip() for l in open(path) if l[0].isdigit()]
+
+
+def _run_trace(sched, reqs, names, iters):
+    for rid, p, o in reqs:
+        sched.submit(rid, p, o)
     got = []
-    for it in range(len(want)):
-        b = s.next()
+    for it in range(iters):
+        b = sched.next()
         got.append(" ".join(f"{names[e['rid']]}:{e['num_cached']}+{e['q_len']}"
                             f"{'*' if e['emits'] else ''}" for e in b))
-        s.complete([100 + it] * len(b))
+        sched.complete([100 + it] * len(b))
+    return got
+
+
+def check_scheduler_hand_trace():
+    """The hand-worked trace in tests/golden/scheduler_trace.txt (budget 8, 2 slots)."""
+    want = _golden_lines("scheduler_trace.txt")
+    s = OS.Scheduler(budget=8, max_seqs=2, num_blocks=40)
+    got = _run_trace(s, [(0, 10, 3), (1, 5, 1), (2, 3, 2)], {0: "A", 1: "B", 2: "C"}, len(want))
+    assert got == want, got
+    assert len(s.free) == 40
+
+
+def check_scheduler_adaptive_two_prompt_trace():
+    """The hand-worked trace in tests/golden/scheduler_adaptive_trace.txt: the adaptive prompt
+    share at decode loads 0, 1 and 2, and an iteration in which one prompt finishes and the next
+    starts inside the same share."""
+    want = _golden_lines("scheduler_adaptive_trace.txt")
+    s = OS.Scheduler(adaptive=True, max_seqs=4, num_blocks=40, min_chunk=4, base_chunk=8,
+                     max_chunk=12, pressure_threshold=4)
+    got = _run_trace(s, [(0, 3, 4), (1, 20, 2), (2, 20, 2)], {0: "C", 1: "A", 2: "B"}, len(want))
     assert got == want, got
     assert len(s.free) == 40
 
 
 def check_scheduler_blocks_and_adaptive_budget():
     """Blocks for the whole lifetime are taken at admission (lowest ids first) and come back at
-    the end; the adaptive budget is max_chunk with no decodes, min_chunk + decodes at the
-    threshold, and the linear rule in between (chapter 7.8's dynamic chunk sizing)."""
+    the end; the adaptive prompt share is max_chunk with no decodes, min_chunk at the threshold,
+    and the linear rule rounded down in between (chapter 7.8's dynamic chunk sizing), with the
+    decode tokens on top."""
     s = OS.Scheduler(budget=4, max_seqs=4, num_blocks=10)
     s.submit(7, 20, 13)            # 32 tokens over its lifetime: 2 blocks
     s.submit(8, 3, 1)              # 3 tokens: 1 block
     b = s.next()
     assert [e["blocks"] for e in b] == [[0, 1]] and len(s.free) == 8
+    # a request that could never fit the pool is refused at submission
+    try:
+        s.submit(9, 170, 2)        # 171 tokens: 11 blocks > 10
+        raise AssertionError("oversized request accepted")
+    except ValueError:
+        pass
     # a decoding sequence holds its slot: with one slot, B waits until A has finished
     one = OS.Scheduler(budget=8, max_seqs=1, num_blocks=10)
     one.submit(0, 2, 3)
@@ -523,11 +589,17 @@ def check_scheduler_blocks_and_adaptive_budget():
     assert [(e["rid"], e["num_cached"], e["q_len"]) for e in b1] == [(0, 2, 1), (1, 2, 3)]
     a = OS.Scheduler(adaptive=True, max_seqs=64, num_blocks=10, min_chunk=128, base_chunk=512,
                      max_chunk=4096, pressure_threshold=16)
-    assert a.chunk_budget() == 4096
+    assert a.prompt_share() == 4096
     a.running = [OS.Request(i, 1, 2) for i in range(16)]
-    assert a.chunk_budget() == 128 + 16
+    assert a.prompt_share() == 128
     a.running = a.running[:4]
-    assert a.chunk_budget() == 512 - 96 + 4       # 512 - 4/16 * (512 - 128), plus 4 decodes
+    assert a.prompt_share() == 416                 # 512 - 4/16 * (512 - 128)
+    a.running = a.running[:3]
+    assert a.prompt_share() == 440                 # 512 - 72
+    a.min_chunk, a.threshold = 100, 7
+    assert a.prompt_share() == 335                 # 512 - 3/7 * 412 = 335.43, rounded down
+    a.running = a.running[:1]
+    assert a.prompt_share() == 453                 # 512 - 412/7 = 453.14, rounded down
 
 
 ALL_CHECKS = [
@@ -539,5 +611,6 @@ ALL_CHECKS = [
     check_block_permutation_addresses, check_kv_export_closed_form, check_kv_import_closed_form,
     check_kv_round_trip_across_tables, check_model_head_library_and_identity_stack,
     check_model_stack_is_layer_by_layer, check_greedy_hand_values, check_scheduler_hand_trace,
-    check_scheduler_blocks_and_adaptive_budget,
+    check_scheduler_adaptive_two_prompt_trace, check_scheduler_blocks_and_adaptive_budget,
+    check_cfg1_kv_slots_literal,
 ]

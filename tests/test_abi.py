@@ -337,3 +337,36 @@ def test_attention_option_checks_and_choice():
     spec2, b2, _ = _fake_batch([(300, 200)])
     b2.attention = B.HL_ATTN_FUSED
     assert B.attention_plan(B.layer_cfg(spec2.shape), b2)["fused"] == 0
+
+
+def test_attention_run_argument_checks():
+    """hl_attention_run: paths outside 1..3, a misaligned low query half, a NULL output and a
+    small workspace are refused on the host; hl_attention_build_lists validates like the step."""
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    cfg = B.layer_cfg(spec.shape)
+    s = spec.shape
+    need = B.workspace_bytes(cfg, b)
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    off = (-ws.data_ptr()) % 256
+    d = B._desc(cfg, b, None, None, None, with_stream=False)
+    d.workspace = ws.data_ptr() + off
+    d.workspace_bytes = need
+    q = torch.zeros(spec.num_tokens * s.n_q_heads * s.head_dim + 64, dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    kp = torch.zeros(pool * s.n_kv_heads * 16 * s.head_dim, dtype=torch.bfloat16)
+    kv = B.KvPages(kp.data_ptr(), kp.data_ptr(), pool)
+    bt = B.BlockTable(b.table.data_ptr(), b.h_table.ctypes.data_as(B._c_i32p), b.max_blocks)
+    run = lambda qlo, out, paths: B.lib().hl_attention_run(
+        ctypes.byref(d), q.data_ptr(), qlo, ctypes.byref(kv), ctypes.byref(bt), out, paths)
+    for bad in (0, 4, -1):
+        assert run(None, o.data_ptr(), bad) == B.HL_ERR_ARG
+    assert run(q.data_ptr() + 2, o.data_ptr(), 3) == B.HL_ERR_ALIGN
+    assert run(None, None, 2) == B.HL_ERR_NULL
+    d.workspace_bytes = need - 256
+    assert run(None, o.data_ptr(), 3) == B.HL_ERR_WORKSPACE
+    assert B.lib().hl_attention_build_lists(ctypes.byref(d), ctypes.byref(kv),
+                                            ctypes.byref(bt)) == B.HL_ERR_WORKSPACE
+    b.h_table[1, 0] = pool
+    d.workspace_bytes = need
+    assert B.lib().hl_attention_build_lists(ctypes.byref(d), ctypes.byref(kv),
+                                            ctypes.byref(bt)) == B.HL_ERR_BLOCK

@@ -36,6 +36,9 @@ MUTANTS = [
     ("sequence_step", "out = h2 + linear(", "out = linear("),
     ("sequence_step", "q_rot = rope(q, pos, shape.rope_theta)", "q_rot = q"),
     ("kv_slot_addresses", "positions % block_size", "positions % (block_size + 1)"),
+    ("kv_slot_addresses", "positions % block_size", "(positions + 1) % block_size"),
+    ("kv_slot_addresses", "block_table_row[positions // block_size]",
+     "block_table_row[(positions + 1) // block_size]"),
     ("layer_step", "pos = c + np.arange(n)", "pos = np.arange(n)"),
 ]
 # planted mistakes in the KV-transfer reference
@@ -110,14 +113,23 @@ def test_pins_catch_planted_model_mistake(monkeypatch, fn_name, old, new):
 
 # planted mistakes in the scheduler reference (methods of OS.Scheduler)
 SCHED_MUTANTS = [
-    ("next", "n = min(left, r.prompt_len - r.prefilled)", "n = min(left, r.prompt_len)"),
-    ("next", "if len(self.running) + len(self.prefilling) >= self.max_seqs:",
-     "if len(self.prefilling) >= self.max_seqs:"),
+    ("next", "take = min(share, r.prompt_len - r.prefilled)", "take = min(share, r.prompt_len)"),
+    ("_admit", "if busy >= self.max_seqs or need > len(self.free):",
+     "if len(self.prefilling) >= self.max_seqs or need > len(self.free):"),
+    ("_admit", "r.blocks, self.free = self.free[:need], self.free[need:]",
+     "r.blocks, self.free = self.free[-need:], self.free[:-need]"),
     ("next", '"emits": 1 if dec or r.prefilled + n == r.prompt_len else 0',
      '"emits": 1 if dec else 0'),
-    ("next", "left -= 1", "left -= 0"),
+    ("next", "share -= take", "share -= take - 1"),
     ("complete", "r.generated, r.last_token = 1, tok", "r.generated, r.last_token = 0, tok"),
-    ("chunk_budget", "return chunk + d", "return chunk"),
+    ("prompt_share", "return self.budget - d", "return self.budget"),
+    ("submit", "if lifetime_blocks(r) > self.num_blocks:", "if False:"),
+]
+# planted mistakes in the adaptive prompt-share rule (a module function of the scheduler oracle)
+SHARE_MUTANTS = [
+    ("adaptive_chunk", "drop = -(-d * (base - lo) // threshold)", "drop = d * (base - lo) // threshold"),
+    ("adaptive_chunk", "return hi", "return base"),
+    ("adaptive_chunk", "return base - drop", "return lo + drop"),
 ]
 
 
@@ -139,3 +151,26 @@ def test_pins_catch_planted_scheduler_mistake(monkeypatch, name, old, new):
         except Exception:
             caught.append(check.__name__)
     assert caught, f"no pin caught the mutant Scheduler.{name}: {old!r} -> {new!r}"
+
+
+@pytest.mark.parametrize("fn_name,old,new", SHARE_MUTANTS,
+                         ids=[f"{m[0]}:{m[1][:24]}" for m in SHARE_MUTANTS])
+def test_pins_catch_planted_share_mistake(monkeypatch, fn_name, old, new):
+    monkeypatch.setattr(OS, fn_name, _mutant(fn_name, old, new, OS))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception:
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the mutant {fn_name}: {old!r} -> {new!r}"
+
+
+@pytest.mark.parametrize("fn_name,old,new", [m for m in MUTANTS if m[0] == "kv_slot_addresses"],
+                         ids=lambda v: str(v)[:24])
+def test_literal_slot_pin_catches_shifted_mapping(monkeypatch, fn_name, old, new):
+    """A shifted slot mapping fails the hand-worked literal slots, a pin whose expected values
+    do not come from the oracle's own slot function."""
+    monkeypatch.setattr(OL, fn_name, _mutant(fn_name, old, new))
+    with pytest.raises(Exception):
+        oracle_pins.check_cfg1_kv_slots_literal()

@@ -1,7 +1,9 @@
 """The token-budget scheduler: the oracle against a hand-worked trace and the invariants the
 chunked-prefill page states, then the native scheduler (hl_sched_*) against the oracle batch by
 batch on random arrivals (integer work: bit-exact). CPU only."""
+import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -77,11 +79,16 @@ def test_oracle_invariants(params):
         running = [r.rid for r in s.running]
         b = s.next()
         if params.get("adaptive"):
+            # the prompt share, computed exactly with rationals, plus one token per decode
             d = len(running)
-            chunk = params["max_chunk"] if d == 0 else max(params["min_chunk"], min(
-                int(params["base_chunk"] - d / params["pressure_threshold"] *
-                    (params["base_chunk"] - params["min_chunk"])), params["base_chunk"]))
-            cap = (params["min_chunk"] if d >= params["pressure_threshold"] else chunk) + d
+            lo, base, thr = params["min_chunk"], params["base_chunk"], params["pressure_threshold"]
+            if d == 0:
+                chunk = params["max_chunk"]
+            elif d >= thr:
+                chunk = lo
+            else:
+                chunk = math.floor(base - Fraction(d, thr) * (base - lo))
+            cap = chunk + d
         else:
             cap = params["budget"]
         assert sum(e["q_len"] for e in b) <= cap
@@ -152,3 +159,32 @@ def test_native_scheduler_rejects():
         s.submit(1, 30, 4)   # 33 tokens need 3 blocks > 2
     with pytest.raises(B.HLError):
         s.submit(2, 0, 4)
+    # more blocks than the whole pool holds: refused at submission (it could never be admitted,
+    # and arrival-order admission would hold every later request behind it)
+    small = B.Scheduler(budget=8, max_seqs=2, num_blocks=3, max_blocks_per_seq=8)
+    with pytest.raises(B.HLError):
+        small.submit(1, 60, 4)   # 63 tokens: 4 blocks > 3
+    small.submit(2, 40, 4)       # 43 tokens: 3 blocks
+    with pytest.raises(ValueError):
+        OS.Scheduler(budget=8, max_seqs=2, num_blocks=3).submit(1, 60, 4)
+
+
+def test_native_adaptive_two_prompt_trace():
+    """The native scheduler on the hand-worked adaptive trace of tests/golden."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "scheduler_adaptive_trace.txt")
+    want = [l.split(":", 1)[1].strip() for l in open(path) if l[0].isdigit()]
+    s = B.Scheduler(adaptive=True, max_seqs=4, num_blocks=40, min_chunk=4, base_chunk=8,
+                    max_chunk=12, pressure_threshold=4, max_blocks_per_seq=8)
+    names = {0: "C", 1: "A", 2: "B"}
+    for rid, p, o in [(0, 3, 4), (1, 20, 2), (2, 20, 2)]:
+        s.submit(rid, p, o)
+    got = []
+    for it in range(len(want)):
+        n = s.next()
+        qlen = np.diff(n["q_start"]).tolist()
+        got.append(" ".join(f"{names[r]}:{c}+{q}{'*' if e else ''}" for r, c, q, e in
+                            zip(n["request_ids"].tolist(), n["num_cached"].tolist(), qlen,
+                                n["emits"].tolist())))
+        s.complete([100 + it] * len(qlen))
+    assert got == want, got
+    assert s.counts() == (0, 0, 0, 40)
