@@ -70,6 +70,11 @@ class DeviceCase:
         B.hybrid_layer_step(self.cfg, self.batch, self.x, self.w, self.kp, self.vp, self.out,
                             self.ws, taps=self.taps if taps else None)
 
+    def cached_host(self, si):
+        """fp64 host copies of sequence si's cached K and V [c, Hkv, d]."""
+        k, v = workloads.cached_kv(self.spec, si, self.x.device)
+        return f64(k), f64(v)
+
     def oracle_host(self, seqs=None):
         """fp64 host copies for the oracle: x, weights, cached K/V of `seqs` (default all)."""
         idx = range(self.spec.num_seqs) if seqs is None else seqs

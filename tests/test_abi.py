@@ -24,7 +24,7 @@ HEADER = os.path.join(ROOT, "include", "hybrid_layer.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hl_[a-z_0-9]+|hybrid_layer_step)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hl_[a-z_0-9]+|hybrid_layer_step[a-z_0-9]*)\s*\(",
                        src, flags=re.M)
     return sorted(set(names))
 

@@ -437,6 +437,54 @@ def test_attention_paths_vs_oracle(case, attention):
         assert np.array_equal(g3[pre], got[pre])
 
 
+@pytest.mark.parametrize("attention", [B.HL_ATTN_AUTO, B.HL_ATTN_FUSED, B.HL_ATTN_SEPARATE],
+                         ids=["auto", "fused", "separate"])
+@pytest.mark.parametrize("case", sorted(ATTN_CASES))
+def test_attention_two_part_query_vs_oracle(case, attention):
+    """The decode path the layer step runs: the query in two bf16 halves (q_hi = bf16(q),
+    q_lo = bf16(q - q_hi)), work lists built by their own call, then the kernels (fused or
+    separate). Decode rows are checked against the oracle on q_hi + q_lo (exact in fp64), prompt
+    rows on q_hi alone; each path run alone gives the same rows bit for bit."""
+    shape, seqs = ATTN_CASES[case]
+    spec = workloads.custom_spec(shape, seqs, 77) if seqs is not None else workloads.make_spec(1)
+    say(f"attention two-part query {case} mode={attention}: seqs={spec.seqs[:6]}")
+    table, pool, full, kp, vp, _ = _attention_inputs(spec, 5)
+    s = spec.shape
+    g = torch.Generator(device=DEV)
+    g.manual_seed(606)
+    q32 = torch.randn(spec.num_tokens, s.n_q_heads * s.head_dim, generator=g, device=DEV)
+    q_hi = q32.to(torch.bfloat16)
+    q_lo = (q32 - q_hi.float()).to(torch.bfloat16)
+    cfg = B.layer_cfg(s)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV, attention=attention)
+    ws = B.alloc_workspace(cfg, b, DEV)
+    out = torch.full_like(q_hi, float("nan"))
+    B.attention_build_lists(cfg, b, kp, vp, ws)
+    B.attention_run(cfg, b, q_hi, kp, vp, out, ws, q_lo=q_lo, paths=B.ATTN_BOTH)
+    torch.cuda.synchronize()
+    pre = np.concatenate([np.arange(spec.q_start[i], spec.q_start[i + 1])
+                          for i, (c, n) in enumerate(spec.seqs) if n > 1] or [np.zeros(0, int)])
+    dec = np.array([spec.q_start[i] for i, (c, n) in enumerate(spec.seqs) if n == 1], dtype=int)
+    got = f64(out)
+    if pre.size:
+        ref_pre = _oracle_attention(spec, full, q_hi)
+        assert_close(got[pre], ref_pre[pre], "prefill rows (q_hi)")
+    if dec.size:
+        q_two = torch.from_numpy(f64(q_hi) + f64(q_lo))
+        ref_dec = _oracle_attention(spec, full, q_two)
+        assert_close(got[dec], ref_dec[dec], "decode rows (q_hi + q_lo)")
+    for paths, rows, other in ((B.ATTN_DECODE, dec, pre), (B.ATTN_PREFILL, pre, dec)):
+        o2 = torch.full_like(q_hi, float("nan"))
+        B.attention_build_lists(cfg, b, kp, vp, ws)
+        B.attention_run(cfg, b, q_hi, kp, vp, o2, ws, q_lo=q_lo, paths=paths)
+        torch.cuda.synchronize()
+        g2 = f64(o2)
+        if rows.size:
+            assert np.array_equal(g2[rows], got[rows]), f"paths={paths} rows differ"
+        if other.size:
+            assert np.isnan(g2[other]).all(), f"paths={paths} wrote other rows"
+
+
 def test_rope_kv_append_vs_oracle():
     spec = workloads.custom_spec(workloads.SHAPES["tiny"], [(64, 64), (32, 1), (57, 1), (0, 3),
                                                             (4095, 1), (100000, 1)], 5, pool_slack=1.0)
@@ -554,46 +602,114 @@ def test_step_deterministic_and_block_permutation_invariant():
 
 # ------------------------------------------------------------------------------- full sizes
 
-def _sampled_check(case, label, n_dec_samples=4, pre_rows=(0, 1, 63, 64, 127, 128, 129)):
-    """Full-size step on the GPU; the oracle recomputes sampled rows one request at a time."""
+def _decode_sample(spec, want, seed):
+    """Decode sequences to finish through the oracle: all of them when there are at most `want`,
+    otherwise the longest, the shortest, up to four whose new token opens a fresh page (c mod 16
+    == 0) and four that fill a page's last slot (c mod 16 == 15), and seeded random ones."""
+    dec = [i for i, (c, n) in enumerate(spec.seqs) if n == 1]
+    if len(dec) <= want:
+        return dec
+    ctx = {i: spec.seqs[i][0] for i in dec}
+    picks = {max(dec, key=ctx.get), min(dec, key=ctx.get)}
+    for r in (0, 15):
+        picks.update([i for i in dec if ctx[i] % 16 == r][:4])
+    rng = np.random.default_rng(seed)
+    rest = [i for i in dec if i not in picks]
+    picks.update(int(i) for i in rng.choice(rest, size=want - len(picks), replace=False))
+    return sorted(picks)
+
+
+def _full_size_check(case, label, n_dec=64, pre_rows=(0, 1, 63, 64, 127, 128, 129)):
+    """Full-size step on the GPU against the oracle:
+      * placement, bit-exact: the set of (block, head, slot) whose bytes changed in either pool
+        equals the oracle's addresses of the batch's new tokens (so every other byte of both
+        pools is unchanged);
+      * q_rot and the new K and V rows of every token (the oracle's norm, QKV projection and
+        rotation over the whole token matrix), K/V read back from the slots they were written to;
+      * out, attention output and h2 on sampled rows: every decode when there are at most n_dec,
+        else n_dec of them (longest, shortest, page-edge contexts, seeded random), and spread rows
+        of each prompt chunk, each request finished by the oracle on its own."""
     spec = case.spec
     s = spec.shape
+    T = spec.num_tokens
+    hq, hkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+    kp0, vp0 = case.kp.clone(), case.vp.clone()
     case.step()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(spec.seed)
-    dec_ids = [i for i, (c, n) in enumerate(spec.seqs) if n == 1]
+    say(f"  step done; checking placement over {case.kp.shape[0]} blocks")
+    pos_all, blk_all, slot_all = [], [], []
+    for si, (c, n) in enumerate(spec.seqs):
+        pos = c + np.arange(n)
+        blk, slot = OL.kv_slot_addresses(case.table[si], pos, 16)
+        pos_all.append(pos)
+        blk_all.append(blk)
+        slot_all.append(slot)
+    pos_all, blk_all, slot_all = map(np.concatenate, (pos_all, blk_all, slot_all))
+    expect = {(int(b), h, int(sl)) for b, sl in zip(blk_all, slot_all) for h in range(hkv)}
+    got = changed_slots(kp0, case.kp, vp0, case.vp)
+    assert got == expect, (f"{label}: {len(got - expect)} unexpected slots changed, "
+                           f"{len(expect - got)} expected slots untouched")
+    say(f"  placement bit-exact: {len(expect)} (block, head, slot) triples")
+    del kp0, vp0
+    torch.cuda.empty_cache()
+
+    x, w, _ = case.oracle_host([])
+    h1 = OL.rmsnorm(x, w["attn_norm"], s.rms_eps)
+    qkv = OL.linear(h1, w["w_qkv"])
+    q_ref = OL.rope(qkv[:, :hq * d].reshape(T, hq, d), pos_all, s.rope_theta)
+    k_ref = OL.rope(qkv[:, hq * d:(hq + hkv) * d].reshape(T, hkv, d), pos_all, s.rope_theta)
+    v_ref = qkv[:, (hq + hkv) * d:].reshape(T, hkv, d)
+    assert_close(f64(case.taps["q_rot"]).reshape(T, hq, d), q_ref, f"{label} q_rot (all rows)")
+    tb = torch.from_numpy(blk_all).to(DEV)
+    ts = torch.from_numpy(slot_all).to(DEV)
+    assert_close(f64(case.kp[tb, :, ts, :]), k_ref, f"{label} new K rows (all tokens)")
+    assert_close(f64(case.vp[tb, :, :, ts]), v_ref, f"{label} new V rows (all tokens)")
+    del qkv, q_ref, k_ref, v_ref
+
+    dec_ids = _decode_sample(spec, n_dec, spec.seed)
     pre_ids = [i for i, (c, n) in enumerate(spec.seqs) if n > 1]
-    picks = []
     if dec_ids:
-        longest = max(dec_ids, key=lambda i: spec.seqs[i][0])
-        shortest = min(dec_ids, key=lambda i: spec.seqs[i][0])
-        extra = list(rng.choice(dec_ids, size=min(n_dec_samples, len(dec_ids)), replace=False))
-        picks = sorted(set([longest, shortest] + [int(e) for e in extra]))
-    x, w, cached = case.oracle_host(picks + pre_ids)
-    out = f64(case.out)
-    att = f64(case.taps["attn_out"])
+        ctx = sorted(spec.seqs[i][0] for i in dec_ids)
+        all_ctx = [c for c, n in spec.seqs if n == 1]
+        say(f"  {len(dec_ids)} decodes sampled, contexts {ctx[0]}..{ctx[-1]}")
+        assert ctx[0] == min(all_ctx) and ctx[-1] == max(all_ctx)
+        for r in (0, 15):
+            if any(c % 16 == r for c in all_ctx):
+                assert any(c % 16 == r for c in ctx), f"no sampled decode with c mod 16 == {r}"
+    out, att, h2 = f64(case.out), f64(case.taps["attn_out"]), f64(case.taps["h2"])
     for si in pre_ids:
         c, n = spec.seqs[si]
         rows = sorted(set(r for r in pre_rows if r < n) | {n - 1, n // 2})
         r0 = int(spec.q_start[si])
-        ref = OL.sequence_step(s, x[r0:r0 + n], w, c, *cached[si], rows=rows)
+        ref = OL.sequence_step(s, x[r0:r0 + n], w, c, *case.cached_host(si), rows=rows)
         g_rows = r0 + np.array(ref["rows"])
         assert_close(out[g_rows], ref["out"], f"{label} prefill seq {si} out rows {rows}")
         assert_close(att[g_rows], ref["attn_out"], f"{label} prefill seq {si} attn rows")
-    for si in picks:
-        c, n = spec.seqs[si]
-        r0 = int(spec.q_start[si])
-        ref = OL.sequence_step(s, x[r0:r0 + 1], w, c, *cached[si])
-        assert_close(out[r0:r0 + 1], ref["out"], f"{label} decode seq {si} (ctx {c}) out")
-        assert_close(att[r0:r0 + 1], ref["attn_out"], f"{label} decode seq {si} attn")
+        assert_close(h2[g_rows], ref["h2"], f"{label} prefill seq {si} h2 rows")
+    if dec_ids:
+        refs = {"out": [], "attn_out": [], "h2": []}
+        rows = []
+        for si in dec_ids:
+            c, _ = spec.seqs[si]
+            r0 = int(spec.q_start[si])
+            ref = OL.sequence_step(s, x[r0:r0 + 1], w, c, *case.cached_host(si))
+            for k in refs:
+                refs[k].append(ref[k][0])
+            rows.append(r0)
+        rows = np.array(rows)
+        assert_close(out[rows], np.stack(refs["out"]), f"{label} decode out ({len(rows)} rows)")
+        assert_close(att[rows], np.stack(refs["attn_out"]),
+                     f"{label} decode attn ({len(rows)} rows)")
+        assert_close(h2[rows], np.stack(refs["h2"]), f"{label} decode h2 ({len(rows)} rows)")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfgid,variant", [(2, "mixed"), (3, "mixed"), (4, "mixed"),
                                            (4, "prefill_only"), (4, "decode_only"), (5, "mixed")])
-def test_step_full_size_sampled(cfgid, variant):
+def test_step_full_size(cfgid, variant):
     spec = workloads.make_spec(cfgid, variant)
     say(f"step full size {spec.name}: T={spec.num_tokens} seqs={spec.num_seqs}")
     case = DeviceCase(spec, DEV)
-    _sampled_check(case, spec.name)
+    _full_size_check(case, spec.name)
     del case
     torch.cuda.empty_cache()
