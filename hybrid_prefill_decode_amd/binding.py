@@ -142,6 +142,9 @@ _SIGS = {
                               ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
     "hl_decode_attention": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.POINTER(KvPages),
                              ctypes.POINTER(BlockTable), ctypes.c_void_p], ctypes.c_int),
+    "hybrid_layer_step_noalloc": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(Weights),
+                                   ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable),
+                                   ctypes.c_void_p], ctypes.c_int),
     "hl_attention_build_lists": ([ctypes.POINTER(BatchDesc), ctypes.POINTER(KvPages),
                                   ctypes.POINTER(BlockTable)], ctypes.c_int),
     "hl_attention_run": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,

@@ -161,6 +161,20 @@ typedef struct {
 int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* weights, hl_kv_pages* kv,
                       const hl_block_table* block_table, hl_bf16* out);
 
+/* The layer step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Identical to hybrid_layer_step (same
+ * kernels, same results bit for bit), except that batch->workspace and batch->workspace_bytes
+ * are ignored: the workspace is a fixed array of HL_NOALLOC_SCRATCH_MIB MiB inside the library,
+ * one per device, held until the process ends. The call allocates nothing (no hipMalloc, no
+ * library allocation); its first call on a device looks that device's array up. Batches whose
+ * hl_workspace_bytes() exceeds the array return HL_ERR_WORKSPACE with nothing launched. All calls
+ * on one device share its array, so calls that overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller; a call reads nothing a previous call left.
+ * Errors as hybrid_layer_step, and HL_ERR_HIP if the array cannot be looked up. */
+#define HL_NOALLOC_SCRATCH_MIB 192
+int hybrid_layer_step_noalloc(const hl_batch_desc* batch, const hl_weights* weights,
+                              hl_kv_pages* kv, const hl_block_table* block_table, hl_bf16* out);
+
 /* Workspace the step (and the phase entries) need for this batch, from the host mirrors only.
  * Writes the byte count to *bytes. */
 int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes);

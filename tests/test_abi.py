@@ -370,3 +370,17 @@ def test_attention_run_argument_checks():
     d.workspace_bytes = need
     assert B.lib().hl_attention_build_lists(ctypes.byref(d), ctypes.byref(kv),
                                             ctypes.byref(bt)) == B.HL_ERR_BLOCK
+
+
+def test_noalloc_step_refuses_batches_beyond_its_array():
+    """hybrid_layer_step_noalloc checks the batch's workspace against its fixed array first: a
+    batch that needs more gets HL_ERR_WORKSPACE with nothing launched and no device touched."""
+    spec = workloads.make_spec(3)
+    table, _ = workloads.block_table(spec)
+    b = B.Batch(spec.q_start, spec.num_cached, table, "cpu")
+    cfg = B.layer_cfg(spec.shape)
+    assert B.workspace_bytes(cfg, b) > (192 << 20)
+    d = B._desc(cfg, b, with_stream=False)
+    assert B.lib().hybrid_layer_step_noalloc(ctypes.byref(d), None, None, None,
+                                             None) == B.HL_ERR_WORKSPACE
+    assert B.lib().hybrid_layer_step_noalloc(None, None, None, None, None) == B.HL_ERR_NULL
