@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+SPIN_CYCLES = 2_000_000     # GPU spin between a phase's set-up and its timed launch
 
 
 def log(msg):
@@ -352,26 +353,21 @@ def main():
             pre()
         fn()
         torch.cuda.synchronize()
-        if pre is None:
-            # back to back: one event pair around all reps
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.phase_reps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            total_ms = a.elapsed_time(b)
-        else:
-            # each timed launch bracketed by its own events; its set-up runs outside them
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.phase_reps)]
-            for a, b in evs:
+        # each timed launch bracketed by its own events, its set-up (if any) outside them; a GPU
+        # spin before each one keeps the GPU busy while the host validates and enqueues it (the
+        # block-table checks of the 70B-shaped batch take about 0.2 ms of host time), so the
+        # events bracket the launch's kernels and no idle gap
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.phase_reps)]
+        for a, b in evs:
+            if pre is not None:
                 pre()
-                a.record(stream)
-                fn()
-                b.record(stream)
-            torch.cuda.synchronize()
-            total_ms = sum(a.elapsed_time(b) for a, b in evs)
+            torch.cuda._sleep(SPIN_CYCLES)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(a.elapsed_time(b) for a, b in evs)
         phase_us[pname] = 1000.0 * total_ms / args.phase_reps
         log(f"phase {pname}: {phase_us[pname]:.2f} us")
     if args.only_phase is not None:
