@@ -112,8 +112,8 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
   // the page by kThreads / kChunksPerPage and every LDS destination by 4096 bytes.
   constexpr int kPagesPerI = kThreads / SM::kChunksPerPage;
   const int pg0 = tid / SM::kChunksPerPage, w = tid % SM::kChunksPerPage;
-  // K: page pg, token row w / (D / 8), chunk w % (D / 8)
-  const int k_dst = k_off<D>(pg0 * 16 + w / (D / 8), w % (D / 8));
+  // K: chunk w of a chunk-major page is token w % 16, chunk w / 16
+  const int k_dst = k_off<D>(pg0 * 16 + w % 16, w / 16);
   // V^T: dim row w / 2 of page pg, token quads 2 (w & 1) and 2 (w & 1) + 1, which sit at
   // quad positions (w & 1) and 2 + (w & 1) (8-byte pieces)
   const int v_dst0 = v_off<D>(pg0, w >> 1, 0) + 8 * (w & 1);

@@ -15,6 +15,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define HL_DEV __device__ __forceinline__
 
+// Element offset, inside one (block, KV head) K page, of elements 8c .. 8c+7 of the page's token
+// t. K pages are chunk-major, [head_dim / 8][16 tokens][8]: the same 16-byte chunk of the 16
+// tokens is one contiguous 256-byte run, so a wave's K fragment load for a matrix-core step
+// (16 tokens x 4 chunks) reads 1 KB contiguously instead of sixteen 64-byte pieces 256 bytes apart.
+__host__ __device__ constexpr int kpage_off(int t, int c) { return (c * 16 + t) * 8; }
+
 // bf16 <-> fp32. bf16 is the top half of an fp32. Narrowing uses the CDNA4 packed conversion
 // (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN), one instruction for two values.
 typedef float f32x2 __attribute__((ext_vector_type(2)));

@@ -481,9 +481,9 @@ HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot
   }
   if (blk < 0) return;
   if (gh < Hq + Hkv) {
-    hl_bf16* dst = ep.kpool + (((size_t)blk * Hkv + (gh - Hq)) * HL_BLOCK_SIZE + slot) * HD + 8 * c;
-    *reinterpret_cast<u32x4*>(dst) = pack8(a);
-    *reinterpret_cast<u32x4*>(dst + half) = pack8(b);
+    hl_bf16* page = ep.kpool + ((size_t)blk * Hkv + (gh - Hq)) * HL_BLOCK_SIZE * HD;
+    *reinterpret_cast<u32x4*>(page + kpage_off(slot, c)) = pack8(a);
+    *reinterpret_cast<u32x4*>(page + kpage_off(slot, c + HD / 16)) = pack8(b);
   } else {
     hl_bf16* dst = ep.vpool + ((size_t)blk * Hkv + (gh - Hq - Hkv)) * HD * HL_BLOCK_SIZE + slot;
 #pragma unroll

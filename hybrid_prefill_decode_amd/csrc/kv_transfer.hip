@@ -9,8 +9,9 @@
 // gathers the request's pages into the contiguous slice (what a peer copy or an RDMA write then
 // moves in one piece), import scatters a received slice into pages of another block table.
 //
-// One workgroup per (page of the span, KV head), 2 d threads. K pages are token-major like the
-// slice, so each thread moves one 16-byte chunk of one token row. V pages are dim-major (each
+// One workgroup per (page of the span, KV head), 2 d threads. Each thread moves one 16-byte chunk
+// of one token's K row between the slice and the page (chunk-major: chunk c of token t sits at
+// (c * 16 + t) * 8 elements into the page). V pages are dim-major (each
 // (block, head) page is one contiguous run, as "Gescheiden Prefill en Decode" asks for sharded
 // transfers), so V goes through an LDS transpose: the page is read (or written) in 16-byte
 // pieces of a dim row, the slice in 16-byte pieces of a token row. Slots outside the span are
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(2 * D) void kv_span_kernel(SpanArgs<D> a) {
   const size_t srow = ((size_t)(p - a.start) * a.Hkv + h) * D + 8 * ch;
   // dim-row view of the V page: dim r, tokens 8 half .. 8 half + 7
   const int r = tid >> 1, half = tid & 1;
-  u32x4* kp = reinterpret_cast<u32x4*>(a.kpool + page + (size_t)tok * D + 8 * ch);
+  u32x4* kp = reinterpret_cast<u32x4*>(a.kpool + page + kpage_off(tok, ch));
   u32x4* vp = reinterpret_cast<u32x4*>(a.vpool + page + (size_t)r * HL_BLOCK_SIZE + 8 * half);
   const int p0 = lp * HL_BLOCK_SIZE;
   const bool whole = p0 >= a.start && p0 + HL_BLOCK_SIZE <= a.start + a.count;

@@ -60,9 +60,9 @@ __global__ __launch_bounds__(kThreads) void rope_append_kernel(
       q_rot[(size_t)t * Hq * D + h * D + j + half] = (hl_bf16)rb;
     } else if (blk_ok) {
       const int kh = h - Hq;
-      hl_bf16* dst = kpool + (((size_t)blk * Hkv + kh) * HL_BLOCK_SIZE + slot) * D;
-      dst[j] = (hl_bf16)ra;
-      dst[j + half] = (hl_bf16)rb;
+      hl_bf16* page = kpool + ((size_t)blk * Hkv + kh) * HL_BLOCK_SIZE * D;
+      page[kpage_off(slot, j / 8) + j % 8] = (hl_bf16)ra;
+      page[kpage_off(slot, (j + half) / 8) + (j + half) % 8] = (hl_bf16)rb;
     }
   }
   // values: copied unrotated into the dim-major V page

@@ -133,8 +133,9 @@ typedef struct {
 /* Paged KV cache of this layer. Each (block, kv head) page is one contiguous 4 KB run (for
  * d = 128), as the head-before-token layout of "Gescheiden Prefill en Decode" (section on
  * sharded KV cache transfers) keeps a head's page contiguous:
- *   k: [num_blocks][n_kv_heads][16 tokens][head_dim]   (token-major page: K rows)
- *   v: [num_blocks][n_kv_heads][head_dim][16 tokens]   (dim-major page: V columns)
+ *   k: [num_blocks][n_kv_heads][head_dim / 8][16 tokens][8]   (chunk-major page: elements
+ *      8c .. 8c+7 of token t at ((c * 16) + t) * 8 within the page)
+ *   v: [num_blocks][n_kv_heads][head_dim][16 tokens]          (dim-major page: V columns)
  * Keys are stored after the rotary embedding. The step writes only the slots of its new tokens;
  * every other byte is left as it was. Pages written by one step must not be shared between
  * sequences. */

@@ -8,6 +8,7 @@ import torch
 
 import workloads
 from hybrid_prefill_decode_amd import binding as B
+from hybrid_prefill_decode_amd import kvcache as KC
 from tests._util import f64
 
 SENTINEL = 0x7FC0  # bf16 quiet NaN: every slot that holds no valid K/V
@@ -23,23 +24,21 @@ def bits(t: torch.Tensor) -> torch.Tensor:
 
 
 def make_pools(spec, table, pool, device="cuda"):
-    """K pool [pool][Hkv][16][d] and V pool [pool][Hkv][d][16], NaN everywhere except the cached
-    positions 0..c-1 of every sequence, which get that sequence's seeded K/V."""
+    """K pool [pool][Hkv][d/8][16][8] and V pool [pool][Hkv][d][16], NaN everywhere except the
+    cached positions 0..c-1 of every sequence, which get that sequence's seeded K/V."""
     s = spec.shape
-    kp = torch.full((pool, s.n_kv_heads, 16, s.head_dim), float("nan"), dtype=torch.bfloat16,
-                    device=device)
-    vp = torch.full((pool, s.n_kv_heads, s.head_dim, 16), float("nan"), dtype=torch.bfloat16,
-                    device=device)
+    kp, vp = KC.alloc_pools(pool, s.n_kv_heads, s.head_dim, device)
     for si, (c, _) in enumerate(spec.seqs):
         if c == 0:
             continue
         k, v = workloads.cached_kv(spec, si, device)
-        pos = torch.arange(c, device=device)
-        blk = torch.from_numpy(table[si]).to(device)[pos // 16].long()
-        slot = pos % 16
-        kp[blk, :, slot, :] = k
-        vp[blk, :, :, slot] = v
+        KC.write_positions(kp, vp, table[si], range(c), k, v)
     return kp, vp
+
+
+def k_rows(kp, blk, slot):
+    """K rows [n, Hkv, d] at (block, slot) pairs given as device index tensors."""
+    return KC.k_rows_of(kp, blk, slot)
 
 
 class DeviceCase:
@@ -104,7 +103,7 @@ def assert_close(got, ref, what, tol=TOL):
 
 def changed_slots(before_k, after_k, before_v, after_v):
     """(block, head, slot) triples whose K or V bytes differ between two pool snapshots."""
-    dk = (bits(before_k) != bits(after_k)).any(dim=-1)            # [pool, Hkv, 16]
+    dk = (bits(before_k) != bits(after_k)).any(dim=-1).any(dim=2)  # [pool, Hkv, 16]
     dv = (bits(before_v) != bits(after_v)).any(dim=-2)            # [pool, Hkv, 16]
     idx = torch.nonzero(dk | dv).cpu().numpy()
     return set(map(tuple, idx.tolist()))

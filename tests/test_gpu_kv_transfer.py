@@ -8,6 +8,7 @@ import torch
 
 import oracle.kv_transfer as OKV
 from hybrid_prefill_decode_amd import binding as B
+from hybrid_prefill_decode_amd import kvcache as KC
 from tests._gpu import say
 
 pytestmark = pytest.mark.gpu
@@ -16,6 +17,12 @@ DEV = "cuda"
 
 def _bits(t):
     return t.view(torch.int16).cpu().numpy()
+
+
+def _kbits(k_pool):
+    """Raw bits of a K pool in the logical page layout [blocks, Hkv, 16 tokens, d] the oracle
+    uses (the device pages are chunk-major; the permutation moves bits, no arithmetic)."""
+    return KC.k_token_major(k_pool.view(torch.int16)).cpu().numpy()
 
 
 def _rand_bits(shape, seed):
@@ -40,27 +47,27 @@ def test_kv_export_import_bit_exact(hkv, d, nblk, start, count):
     npages = (start + count + 15) // 16 + 2
     rng = np.random.default_rng(count + d)
     row_a = rng.permutation(nblk)[:npages].astype(np.int32)
-    kA, vA = _rand_bits((nblk, hkv, 16, d), 1), _rand_bits((nblk, hkv, d, 16), 2)
+    kA, vA = _rand_bits(KC.k_pool_shape(nblk, hkv, d), 1), _rand_bits((nblk, hkv, d, 16), 2)
     dst = _rand_bits((L, 2, count, hkv, d), 3)  # other layers must keep these bits
     dst0 = _bits(dst)
     ta = torch.from_numpy(row_a).to(DEV)
     B.kv_export(kA, vA, ta, row_a, start, count, layer, dst)
     torch.cuda.synchronize()
     want = dst0.copy()
-    OKV.export_layer(_bits(kA), _bits(vA), row_a, start, count, layer, want)
+    OKV.export_layer(_kbits(kA), _bits(vA), row_a, start, count, layer, want)
     got = _bits(dst)
     assert np.array_equal(got, want), "export differs from the oracle gather"
 
     # import into another pool under another table: every byte equals the oracle scatter
     nblk_b = nblk + 11
     row_b = rng.permutation(nblk_b)[:npages].astype(np.int32)
-    kB, vB = _rand_bits((nblk_b, hkv, 16, d), 4), _rand_bits((nblk_b, hkv, d, 16), 5)
-    kB_ref, vB_ref = _bits(kB), _bits(vB)
+    kB, vB = _rand_bits(KC.k_pool_shape(nblk_b, hkv, d), 4), _rand_bits((nblk_b, hkv, d, 16), 5)
+    kB_ref, vB_ref = _kbits(kB), _bits(vB)
     OKV.import_layer(got, row_b, start, count, layer, kB_ref, vB_ref)
     tb = torch.from_numpy(row_b).to(DEV)
     B.kv_import(dst, tb, row_b, start, count, layer, kB, vB)
     torch.cuda.synchronize()
-    assert np.array_equal(_bits(kB), kB_ref), "import K pool differs from the oracle scatter"
+    assert np.array_equal(_kbits(kB), kB_ref), "import K pool differs from the oracle scatter"
     assert np.array_equal(_bits(vB), vB_ref), "import V pool differs from the oracle scatter"
 
     # round trip: exporting the imported span gives the same slice

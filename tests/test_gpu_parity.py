@@ -13,8 +13,9 @@ import torch
 import oracle.layer as OL
 import workloads
 from hybrid_prefill_decode_amd import binding as B
-from tests._gpu import (DeviceCase, assert_close, bits, changed_slots, make_pools, rel_err, say,
-                        SENTINEL)
+from hybrid_prefill_decode_amd import kvcache as KC
+from tests._gpu import (DeviceCase, assert_close, bits, changed_slots, k_rows, make_pools,
+                        rel_err, say, SENTINEL)
 from tests._util import f64
 
 pytestmark = pytest.mark.gpu
@@ -319,8 +320,7 @@ def test_qkv_rope_append_vs_oracle(case):
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
     x = workloads.hidden_states(spec, DEV)
     w = workloads.weights(spec, DEV, gain_jitter=0.1)
-    kp = torch.full((pool, s.n_kv_heads, 16, s.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
-    vp = torch.full((pool, s.n_kv_heads, s.head_dim, 16), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp, vp = KC.alloc_pools(pool, s.n_kv_heads, s.head_dim, DEV)
     kp0, vp0 = kp.clone(), vp.clone()
     q_rot = torch.empty(spec.num_tokens, s.n_q_heads * s.head_dim, dtype=torch.bfloat16, device=DEV)
     ws = B.alloc_workspace(cfg, b, DEV)
@@ -340,7 +340,7 @@ def test_qkv_rope_append_vs_oracle(case):
         assert_close(f64(q_rot[r0:r0 + n]).reshape(n, hq, d), qr, f"q_rot seq {si}")
         blk, slot = OL.kv_slot_addresses(table[si], pos, 16)
         tb, ts = torch.from_numpy(blk).to(DEV), torch.from_numpy(slot).to(DEV)
-        assert_close(f64(kp[tb, :, ts, :]), kr, f"K rows seq {si}")
+        assert_close(f64(k_rows(kp, tb, ts)), kr, f"K rows seq {si}")
         assert_close(f64(vp[tb, :, :, ts]), vv, f"V rows seq {si}")
         expect |= {(int(bb), h, int(ss)) for bb, ss in zip(blk, slot) for h in range(hkv)}
     assert changed_slots(kp0, kp, vp0, vp) == expect
@@ -493,8 +493,7 @@ def test_rope_kv_append_vs_oracle():
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
-    kp = torch.full((pool, s.n_kv_heads, 16, s.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
-    vp = torch.full((pool, s.n_kv_heads, s.head_dim, 16), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp, vp = KC.alloc_pools(pool, s.n_kv_heads, s.head_dim, DEV)
     kp0, vp0 = kp.clone(), vp.clone()
     qkv = _randn((spec.num_tokens, s.qkv_cols), 9)
     q_rot = torch.empty(spec.num_tokens, s.n_q_heads * s.head_dim, dtype=torch.bfloat16, device=DEV)
@@ -512,7 +511,7 @@ def test_rope_kv_append_vs_oracle():
         vv = rows[:, (hq + hkv) * d:].reshape(n, hkv, d)
         assert_close(f64(q_rot[r0:r0 + n]).reshape(n, hq, d), qr, f"q_rot seq {si}")
         blk, slot = OL.kv_slot_addresses(table[si], pos, 16)
-        gk = f64(kp[torch.from_numpy(blk).to(DEV), :, torch.from_numpy(slot).to(DEV), :])
+        gk = f64(k_rows(kp, torch.from_numpy(blk).to(DEV), torch.from_numpy(slot).to(DEV)))
         gv = f64(vp[torch.from_numpy(blk).to(DEV), :, :, torch.from_numpy(slot).to(DEV)])
         assert_close(gk, kr, f"k rows seq {si}")
         # V is copied, not recomputed: bit-exact with the input bf16
@@ -526,7 +525,7 @@ def test_rope_kv_append_vs_oracle():
     mask_k = torch.ones(pool, hkv, 16, dtype=torch.bool, device=DEV)
     for (bb, h, ss) in expect_slots:
         mask_k[bb, h, ss] = False
-    assert bool((bits(kp)[mask_k] == SENTINEL).all())
+    assert bool((bits(KC.k_token_major(kp))[mask_k] == SENTINEL).all())
     assert bool((bits(vp).permute(0, 1, 3, 2)[mask_k] == SENTINEL).all())
 
 
@@ -558,7 +557,7 @@ def _check_full_step(case, label):
     assert changed_slots(kp0, case.kp, vp0, case.vp) == expect
     bt = torch.from_numpy(a[:, 2]).to(DEV)
     sl = torch.from_numpy(a[:, 3]).to(DEV)
-    assert_close(f64(case.kp[bt, :, sl, :]), ref["k_new"], f"{label} new K rows")
+    assert_close(f64(k_rows(case.kp, bt, sl)), ref["k_new"], f"{label} new K rows")
     assert_close(f64(case.vp[bt, :, :, sl]), ref["v_new"], f"{label} new V rows")
     return ref
 
@@ -662,7 +661,7 @@ def _full_size_check(case, label, n_dec=64, pre_rows=(0, 1, 63, 64, 127, 128, 12
     assert_close(f64(case.taps["q_rot"]).reshape(T, hq, d), q_ref, f"{label} q_rot (all rows)")
     tb = torch.from_numpy(blk_all).to(DEV)
     ts = torch.from_numpy(slot_all).to(DEV)
-    assert_close(f64(case.kp[tb, :, ts, :]), k_ref, f"{label} new K rows (all tokens)")
+    assert_close(f64(k_rows(case.kp, tb, ts)), k_ref, f"{label} new K rows (all tokens)")
     assert_close(f64(case.vp[tb, :, :, ts]), v_ref, f"{label} new V rows (all tokens)")
     del qkv, q_ref, k_ref, v_ref
 

@@ -290,8 +290,9 @@ def engine_model(shape: LayerShape, layers: int, vocab: int, num_blocks: int, de
     layer_w = [weights(layer_spec(base, l), device) for l in range(layers)]
     pools = []
     for _ in range(layers):
-        k = torch.full((num_blocks, shape.n_kv_heads, BLOCK_SIZE, shape.head_dim), pool_fill,
-                       dtype=torch.bfloat16, device=device)
+        # K pages chunk-major [d/8][16][8], V pages dim-major [d][16] (the library's page layout)
+        k = torch.full((num_blocks, shape.n_kv_heads, shape.head_dim // 8, BLOCK_SIZE, 8),
+                       pool_fill, dtype=torch.bfloat16, device=device)
         v = torch.full((num_blocks, shape.n_kv_heads, shape.head_dim, BLOCK_SIZE), pool_fill,
                        dtype=torch.bfloat16, device=device)
         pools.append((k, v))
