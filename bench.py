@@ -376,6 +376,26 @@ def main():
               flush=True)
         return
 
+    # one traced fused launch: how the two paths shared the GPU (decode rate while prefill ran)
+    trace_metrics = None
+    if plan["fused"] and has_pre and has_dec:
+        items = plan["prefill_parts"] * s.n_q_heads + plan["decode_units"] * s.n_kv_heads
+        trace = torch.zeros(3 * items, dtype=torch.int64, device=dev)
+        lists()
+        torch.cuda._sleep(SPIN_CYCLES)
+        B.attention_run_traced(cfg, batch, q_rot, kp, vp, attn, ws, trace, q_lo=q_lo,
+                               paths=B.ATTN_BOTH, stream=stream)
+        torch.cuda.synchronize()
+        trace_metrics = fused_trace_metrics(spec, plan, trace.view(items, 3).cpu().numpy(),
+                                            B.trace_clock_khz())
+        if dec_gbps_alone := (algorithmic_counts(spec)["decode_kv_bytes"] /
+                              (phase_us["decode_attention"] * 1e-6) / 1e9):
+            trace_metrics["decode_alone_gbps"] = round(dec_gbps_alone, 1)
+            trace_metrics["decode_in_prefill_window_over_alone"] = (
+                round(trace_metrics["decode_gbps_in_prefill_window"] / dec_gbps_alone, 4)
+                if trace_metrics["decode_gbps_in_prefill_window"] else None)
+        log(f"fused trace: {trace_metrics}")
+
     cnt = algorithmic_counts(spec)
     # the QKV projection phase also holds its prep pass and the RoPE / append epilogue
     gemm_us = sum(phase_us[k] for k in ("qkv_rope_append", "gemm_o", "gemm_gate_up", "gemm_down"))
@@ -438,6 +458,7 @@ def main():
         "roofline": roofline,
         "attention_plan": plan,
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
+        "fused_attention_trace": trace_metrics,
         "gemm_mfma_util": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": round(gemm_tflops, 1),
         "gate_up_tflops": round(gu_tflops, 1),
@@ -462,6 +483,67 @@ def main():
         del kp2, vp2, xfer
         result["cpu_baseline"] = cpu_baseline(spec, x, w, dev, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _union_us(iv):
+    """Total length of the union of [start, end) intervals (sorted merge)."""
+    total, cur_s, cur_e = 0.0, None, None
+    for a, b in sorted(iv):
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                total += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    if cur_e is not None:
+        total += cur_e - cur_s
+    return total
+
+
+def fused_trace_metrics(spec, plan, rec, khz):
+    """How prefill and decode shared one fused attention launch, from its work-item trace
+    (rec [items, 3] int64: start, end, workgroup; prefill items first). Decode bytes per item:
+    the K and V of its pages' tokens for one KV head."""
+    import numpy as np
+    s = spec.shape
+    n_pre = plan["prefill_parts"] * s.n_q_heads
+    sp = plan["split_pages"]
+    dec_bytes = []
+    for c, n in spec.seqs:
+        if n != 1:
+            continue
+        kv = c + 1
+        pages = (kv + 15) // 16
+        for u in range((pages + sp - 1) // sp):
+            toks = min((u + 1) * sp * 16, kv) - u * sp * 16
+            dec_bytes += [toks * s.head_dim * 2 * 2] * s.n_kv_heads
+    dec_bytes = np.array(dec_bytes, dtype=np.float64)
+    us = (rec[:, :2].astype(np.float64) - float(rec[:, 0].min())) * 1000.0 / khz
+    pre, dec = us[:n_pre], us[n_pre:]
+    assert dec.shape[0] == dec_bytes.shape[0], (dec.shape, dec_bytes.shape)
+    span = float(us[:, 1].max())
+    dec_active = _union_us(map(tuple, dec))
+    pre_active = _union_us(map(tuple, pre)) if n_pre else 0.0
+    win = float(pre[:, 1].max()) if n_pre else 0.0
+    # decode bytes moved while prefill items still ran: each item's bytes prorated by the part of
+    # its interval inside [0, win)
+    frac = np.clip((np.minimum(dec[:, 1], win) - dec[:, 0]) / np.maximum(dec[:, 1] - dec[:, 0], 1e-9),
+                   0.0, 1.0)
+    in_win = float((dec_bytes * frac).sum())
+    workers_pre = len(set(rec[:n_pre, 2].tolist())) if n_pre else 0
+    return {
+        "span_us": round(span, 1),
+        "prefill_active_us": round(pre_active, 1),
+        "decode_active_us": round(dec_active, 1),
+        "decode_gbps_over_decode_active": round(dec_bytes.sum() / (dec_active * 1e-6) / 1e9, 1),
+        "prefill_window_us": round(win, 1),
+        "decode_gbps_in_prefill_window": round(in_win / (win * 1e-6) / 1e9, 1) if win > 0 else None,
+        "decode_gbps_after_prefill": round((dec_bytes.sum() - in_win) / ((span - win) * 1e-6) / 1e9, 1)
+                                     if span > win else None,
+        "workgroups_running_prefill": workers_pre,
+        "items": [n_pre, int(dec.shape[0])],
+        "clock_khz": khz,
+    }
 
 
 def model_bench(args, spec, dev):

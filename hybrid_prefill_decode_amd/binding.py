@@ -150,6 +150,11 @@ _SIGS = {
     "hl_attention_run": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
                           ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable), ctypes.c_void_p,
                           ctypes.c_int32], ctypes.c_int),
+    "hl_attention_run_traced": ([ctypes.POINTER(BatchDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.POINTER(KvPages), ctypes.POINTER(BlockTable),
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_size_t], ctypes.c_int),
+    "hl_trace_clock_khz": ([_c_i32p], ctypes.c_int),
 }
 
 
@@ -528,3 +533,22 @@ def attention_run(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, q_lo=None,
     _check(lib().hl_attention_run(ctypes.byref(d), _ptr(q_rot), _ptr(q_lo), ctypes.byref(kv),
                                   ctypes.byref(bt), _ptr(attn_out), int(paths)),
            "hl_attention_run")
+
+
+def attention_run_traced(cfg, b, q_rot, k_pool, v_pool, attn_out, workspace, trace, q_lo=None,
+                         paths: int = ATTN_BOTH, stream=None) -> None:
+    """hl_attention_run_traced: trace is a device int64 tensor of 3 * items entries ((start, end,
+    workgroup) per work item, prefill items first; see the header)."""
+    d = _desc(cfg, b, None, workspace, stream)
+    kv = _pages(k_pool, v_pool)
+    bt = _table(b)
+    _check(lib().hl_attention_run_traced(ctypes.byref(d), _ptr(q_rot), _ptr(q_lo), ctypes.byref(kv),
+                                         ctypes.byref(bt), _ptr(attn_out), int(paths), _ptr(trace),
+                                         trace.numel()),
+           "hl_attention_run_traced")
+
+
+def trace_clock_khz() -> int:
+    v = ctypes.c_int32(0)
+    _check(lib().hl_trace_clock_khz(ctypes.byref(v)), "hl_trace_clock_khz")
+    return int(v.value)

@@ -28,6 +28,7 @@ struct HostPlan {
   int32_t n_dec_units = 0, n_dec_seqs = 0, n_pre_tiles = 0, split_pages = 32;
   int32_t n_pre_merge = 0, n_pre_slots = 0, pre_split = 1 << 30;
   bool fused = false;  // prefill and decode attention in one launch
+  bool fused_prefetch = false;  // ... whose decode units prefetch their successors
   // workspace byte offsets
   size_t o_dec_units = 0, o_dec_seqs = 0, o_pre_tiles = 0, o_pre_merge = 0, o_pre_po = 0,
          o_pre_ml = 0, o_counters = 0, o_h1 = 0, o_rs = 0, o_pos = 0,
@@ -113,16 +114,20 @@ int device_cus() {
   return cus;
 }
 
-// Pages per decode work unit. A unit of n pages costs about n + kUnitOverhead page-times (query
-// load, state merge, partial write and merge read), and two workgroups run per compute unit (the
-// kernel's register budget), so `slots` units run at once. With equal-length decodes the units
-// run in whole rounds: cost = rounds * (largest unit + overhead). Otherwise the grid drains as a
-// list schedule: cost = total work / slots + the largest unit (its worst-case tail). Candidates
-// are a fixed ladder plus ceil(P_max / u) for small u (which tiles equal lengths exactly); the
-// cheapest wins, ties to the larger unit (fewer partials). No sequence may need more than
+// Pages per decode work unit. A unit of n pages costs about n + kUnitOverhead page-times (its
+// record, query and table reads before the first K/V bytes arrive, the state merge, the partial
+// write and its merge read), and two workgroups run per compute unit (the kernel's register
+// budget), so `slots` units run at once. With equal-length decodes the units run in whole rounds:
+// cost = rounds * (largest unit + overhead). Otherwise the grid drains as a list schedule: cost =
+// total work / slots + a quarter of the largest unit (the tail of thousands of dispatched units
+// is far shorter than a whole unit). The constants come from timing every unit size on the 70B
+// (512 decodes log-uniform in 1K..32K) and 14B (96 decodes uniform in 2K..8K) batches: the
+// overhead is ~14 page-times, and this cost tracks those timings within 2 %. Candidates are a
+// fixed ladder plus ceil(P_max / u) for small u (which tiles equal lengths exactly); the cheapest
+// wins, ties to the larger unit (fewer partials). No sequence may need more than
 // kMaxUnitsPerSeq units (its merge weights live in LDS).
 int pick_split(const hl_batch_desc* b) {
-  constexpr int64_t kUnitOverhead = 6;
+  constexpr int64_t kUnitOverhead = 14;
   const int64_t slots = 2 * (int64_t)device_cus();
   const int64_t hkv = b->cfg->n_kv_heads;
   std::vector<int64_t> pages;
@@ -155,7 +160,7 @@ int pick_split(const hl_batch_desc* b) {
     } else {
       double work = 0.0;
       for (int64_t p : pages) work += (double)(p + kUnitOverhead * ((p + sp - 1) / sp));
-      cost = work * (double)hkv / (double)slots + (double)job;
+      cost = work * (double)hkv / (double)slots + 0.25 * (double)job;
     }
     if (best_cost < 0.0 || cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && sp > best_sp)) {
       best_cost = cost;
@@ -239,6 +244,11 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
               (dec_us >= 1000.0 && pre_us >= 0.02 * dec_us));
   if (b->attention == HL_ATTN_FUSED) p->fused = pre_flops > 0 && dec_bytes > 0;
   if (b->attention == HL_ATTN_SEPARATE) p->fused = false;
+  // In a fused launch the decode units can start their successor's loads while they drain, which
+  // hides most of a unit's start-up but costs the kernel registers that its prefill items then
+  // spill: worth it when decode work dominates (measured: the 70B-shaped batch with 512 decodes
+  // gains 4 %, prefill-heavy batches lose 5-10 %).
+  p->fused_prefetch = p->fused && dec_us >= 4.0 * pre_us;
   p->split_pages = p->fused ? pick_split_fused(b) : pick_split(b);
   p->pre_split = pick_pre_split(b);
   for (int s = 0; s < b->num_seqs; ++s) {
@@ -271,7 +281,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
     return o;
   };
   p->o_counters = take(sizeof(int32_t) * hl::kPlanCounters * hl::kCounterStride);
-  p->o_dec_units = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_units);
+  p->o_dec_units = take(sizeof(int32_t) * hl::kDecUnitInts * (size_t)p->n_dec_units);
   p->o_dec_seqs = take(sizeof(int32_t) * 3 * (size_t)p->n_dec_seqs);
   p->o_pre_tiles = take(sizeof(int32_t) * hl::kPreEntry * (size_t)p->n_pre_tiles);
   p->o_pre_merge = take(sizeof(int32_t) * 4 * (size_t)p->n_pre_merge);
@@ -311,6 +321,7 @@ hl::Plan device_plan(const HostPlan& hp, void* ws) {
   p.n_pre_merge = hp.n_pre_merge;
   p.split_pages = hp.split_pages;
   p.pre_split = hp.pre_split;
+  p.fused_prefetch = hp.fused_prefetch;
   return p;
 }
 
@@ -399,11 +410,14 @@ int run_qkv(const hl_batch_desc* b, const hl_weights* w, hl_bf16* q_rot, const h
 // plan_built: the work lists are already in the workspace (built by the step's prep pass).
 int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q_lo,
                   const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
-                  const HostPlan& hp, bool do_prefill, bool do_decode, bool plan_built = false) {
+                  const HostPlan& hp, bool do_prefill, bool do_decode, bool plan_built = false,
+                  uint64_t* trace = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(b->stream);
-  const hl::Plan dp = device_plan(hp, b->workspace);
+  hl::Plan dp = device_plan(hp, b->workspace);
+  dp.trace = trace;
   int rc = plan_built ? HL_OK
-                      : hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, dp, st));
+                      : hip_rc(hl::launch_plan(b->q_start, b->num_cached, b->num_seqs, bt->table,
+                                          bt->max_blocks_per_seq, dp, st));
   if (rc) return rc;
   if (do_prefill && do_decode && hp.fused) {
     // both paths in one fused launch: prefill and decode overlap on every compute unit
@@ -421,7 +435,8 @@ int run_attention(const hl_batch_desc* b, const hl_bf16* q_rot, const hl_bf16* q
   if (do_decode) {
     rc = hip_rc(hl::launch_decode_attention(*b->cfg, b->q_start, b->num_cached, q_rot, q_lo, kv->k,
                                             kv->v, kv->num_blocks, bt->table,
-                                            bt->max_blocks_per_seq, dp, attn_out, st));
+                                            bt->max_blocks_per_seq, dp, device_cus(), attn_out,
+                                            st));
   }
   return rc;
 }
@@ -514,7 +529,7 @@ int hl_attention_plan(const hl_batch_desc* batch, int32_t* fused, int32_t* split
   if (rc) return rc;
   HostPlan hp;
   if (batch->num_seqs > 0) make_plan(batch, &hp);
-  *fused = hp.fused ? 1 : 0;
+  *fused = hp.fused ? (hp.fused_prefetch ? 2 : 1) : 0;
   *split_pages = hp.split_pages;
   *decode_units = hp.n_dec_units;
   *prefill_parts = hp.n_pre_tiles;
@@ -718,21 +733,50 @@ int hl_attention_build_lists(const hl_batch_desc* batch, const hl_kv_pages* kv,
   int rc = prepare(batch, kv, bt, &hp);
   if (rc || batch->num_seqs == 0) return rc;
   const hl::Plan dp = device_plan(hp, batch->workspace);
-  return hip_rc(hl::launch_plan(batch->q_start, batch->num_cached, batch->num_seqs, dp,
-                                static_cast<hipStream_t>(batch->stream)));
+  return hip_rc(hl::launch_plan(batch->q_start, batch->num_cached, batch->num_seqs, bt->table,
+                                bt->max_blocks_per_seq, dp, static_cast<hipStream_t>(batch->stream)));
 }
 
-int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
-                     const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
-                     int32_t paths) {
+static int attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                         const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                         int32_t paths, uint64_t* trace, size_t trace_entries, bool traced) {
   if (paths < 1 || paths > 3) return HL_ERR_ARG;
   HostPlan hp;
   int rc = prepare(batch, kv, bt, &hp);
   if (rc || batch->num_seqs == 0) return rc;
   if (!q_rot || !attn_out) return HL_ERR_NULL;
   if (!aligned16(q_rot) || !aligned16(attn_out) || (q_lo && !aligned16(q_lo))) return HL_ERR_ALIGN;
+  if (traced) {
+    const size_t items = (size_t)hp.n_pre_tiles * batch->cfg->n_q_heads +
+                         (size_t)hp.n_dec_units * batch->cfg->n_kv_heads;
+    if (!trace) return HL_ERR_NULL;
+    if (!aligned16(trace)) return HL_ERR_ALIGN;
+    if (trace_entries < 3 * items) return HL_ERR_ARG;
+  }
   return run_attention(batch, q_rot, q_lo, kv, bt, attn_out, hp, (paths & 1) != 0,
-                       (paths & 2) != 0, true);
+                       (paths & 2) != 0, true, traced ? trace : nullptr);
+}
+
+int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                     const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                     int32_t paths) {
+  return attention_run(batch, q_rot, q_lo, kv, bt, attn_out, paths, nullptr, 0, false);
+}
+
+int hl_attention_run_traced(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                            const hl_kv_pages* kv, const hl_block_table* bt, hl_bf16* attn_out,
+                            int32_t paths, uint64_t* trace, size_t trace_entries) {
+  return attention_run(batch, q_rot, q_lo, kv, bt, attn_out, paths, trace, trace_entries, true);
+}
+
+int hl_trace_clock_khz(int32_t* khz) {
+  if (!khz) return HL_ERR_NULL;
+  int dev = 0, rate = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return HL_ERR_HIP;
+  *khz = rate;
+  return HL_OK;
 }
 
 int hybrid_layer_step(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,

@@ -32,11 +32,23 @@ namespace {
 using hl::decode::kThreads;
 
 // One workgroup per (unit, KV head); KV head fastest in dispatch order, so the Hkv workgroups of a
-// unit read the Hkv adjacent 4 KB pieces of each block at about the same time.
+// unit read the Hkv adjacent pieces of each block at about the same time. (Persistent workers that
+// prefetch each next unit, as the fused launch can, were measured slower for this launch alone:
+// the hardware's dispatch of one short-lived workgroup per unit already overlaps a unit's start
+// with the streaming of the others on its compute unit.)
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(hl::decode::DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(hl::decode::DecodeArgs a,
+                                                                  uint64_t* __restrict__ trace) {
   __shared__ hl::decode::DecodeLds<D> L;
-  hl::decode::decode_unit<D>(a, blockIdx.x / a.Hkv, blockIdx.x % a.Hkv, L);
+  hl::decode::Carry<D> cy;
+  cy.item = -1;
+  cy.has_pair = false;
+  const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
+  hl::decode::decode_item<D, false>(a, blockIdx.x, L, cy);
+  if (trace) {
+    __syncthreads();
+    hl::record_item(trace, blockIdx.x, t0);
+  }
 }
 
 // Merge the split partials of each multi-unit decode sequence and write its attention row.
@@ -108,23 +120,27 @@ hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, 
 
 hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_start,
                                    const int32_t* num_cached, const hl_bf16* q_rot,
-                                   const hl_bf16* q_lo,
-                                   const hl_bf16* kpool, const hl_bf16* vpool,
-                                   int64_t num_blocks, const int32_t* table, int32_t max_blocks,
-                                   const Plan& plan, hl_bf16* attn_out, hipStream_t st) {
+                                   const hl_bf16* q_lo, const hl_bf16* kpool,
+                                   const hl_bf16* vpool, int64_t num_blocks, const int32_t* table,
+                                   int32_t max_blocks, const Plan& plan, int32_t cus,
+                                   hl_bf16* attn_out, hipStream_t st) {
+  (void)cus;
   if (plan.n_dec_units <= 0) return hipSuccess;
-  const float scale = cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
-  const float scale_log2 = scale * 1.4426950408889634f;
+  const float scale =
+      cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
   const dim3 grid(cfg.n_kv_heads * plan.n_dec_units), block(kThreads);
   const decode::DecodeArgs args{q_start,          num_cached,  q_rot,      q_lo,
                                 kpool,            vpool,       (long long)num_blocks, table,
                                 max_blocks,       plan.dec_units, plan.dec_seqs, plan.split_pages,
-                                cfg.n_q_heads,    cfg.n_kv_heads, scale_log2, plan.dec_part,
-                                attn_out};
+                                cfg.n_q_heads,    cfg.n_kv_heads, scale * 1.4426950408889634f,
+                                plan.dec_part,    attn_out,    plan.n_dec_units * cfg.n_kv_heads};
+  // decode records follow the batch's prefill records in the trace
+  uint64_t* trace =
+      plan.trace ? plan.trace + 3 * (size_t)plan.n_pre_tiles * cfg.n_q_heads : nullptr;
   if (cfg.head_dim == 128)
-    hipLaunchKernelGGL(decode_attn_kernel<128>, grid, block, 0, st, args);
+    hipLaunchKernelGGL(decode_attn_kernel<128>, grid, block, 0, st, args, trace);
   else
-    hipLaunchKernelGGL(decode_attn_kernel<64>, grid, block, 0, st, args);
+    hipLaunchKernelGGL(decode_attn_kernel<64>, grid, block, 0, st, args, trace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_merge(cfg, q_start, plan, attn_out, st);

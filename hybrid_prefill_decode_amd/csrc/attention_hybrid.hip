@@ -23,11 +23,14 @@
 // memory location: with a few hundred workers that cost tens of microseconds per launch.)
 // Each item runs the same code as in the separate kernels (and the same merges follow), so the
 // results are bit-identical to theirs.
+#include <type_traits>
+
 #include "attn_decode_core.h"
 #include "attn_prefill_core.h"
 
 namespace {
 
+using hl::decode::Carry;
 using hl::decode::DecodeArgs;
 using hl::decode::DecodeLds;
 using hl::prefill::PrefillArgs;
@@ -118,10 +121,12 @@ HL_DEV int wg_claim(const Queues& qs, int& stage, int* s_tick) {
   return -1;
 }
 
-template <int D>
+// PF: decode units prefetch the next unit of their worker (attn_decode_core.h). Worth it when
+// decode units dominate the launch; it costs registers, which the prefill items then spill.
+template <int D, bool PF>
 __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
     PrefillArgs pa, DecodeArgs da, int32_t* __restrict__ counters, int n_pre_items,
-    int n_dec_items, int n_pre_workers) {
+    int n_dec_items, int n_pre_workers, uint64_t* __restrict__ trace) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_tick;
   const Queues qs{counters, n_pre_items, n_dec_items, n_pre_workers, (int)gridDim.x,
@@ -130,54 +135,99 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
   int cur = qs.first_item(blockIdx.x);
   if (cur < 0) cur = wg_claim(qs, stage, &s_tick);
   while (cur >= 0) {
-    // Decode units are short: thread 0 takes the next decode ticket now and publishes it after
-    // the unit. Prefill items are long and few, so their next claim waits for the item's end
-    // (a ticket taken early would reserve an item that an idle worker could have run).
-    const int q = qs.queue_at(stage);
-    const bool ahead = q >= 8;
-    int t = 0;
-    if (threadIdx.x == 0 && ahead) t = atomicAdd(qs.counter(q), 1);
     if (cur < n_pre_items) {
+      // prefill items are long and few: the next claim waits for the item's end (a ticket taken
+      // early would reserve an item that an idle worker could have run)
+      const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
       hl::prefill::prefill_item<D>(pa, cur / pa.Hq, cur % pa.Hq, smem);
-    } else {
-      const int u = cur - n_pre_items;
-      hl::decode::decode_unit<D>(da, u / da.Hkv, u % da.Hkv,
-                                 *reinterpret_cast<DecodeLds<D>*>(smem));
+      __syncthreads();  // the item's LDS reads are done before the next item writes
+      if (trace) hl::record_item(trace, cur, t0);
+      cur = wg_claim(qs, stage, &s_tick);
+      continue;
     }
-    int next;
-    if (ahead) {
-      if (threadIdx.x == 0) s_tick = t;
-      __syncthreads();  // also: the item's LDS reads are done before the next item writes
-      next = qs.resolve(q, __builtin_amdgcn_readfirstlane(s_tick));
+    // A run of decode units. Thread 0 claims the next unit as the current one starts. With PF it
+    // publishes the claim in LDS right away, where each wave reads it near the end of its pages
+    // to start the next unit's loads (decode_item); without, the claim is published after the
+    // unit, so its atomic's latency hides behind the unit.
+    DecodeLds<D>& L = *reinterpret_cast<DecodeLds<D>*>(smem);
+    if (PF) {
+      if (threadIdx.x == 0) L.tick = hl::decode::kTickPending;
       __syncthreads();
+    }
+    Carry<D> cy;
+    cy.item = -1;
+    cy.has_pair = false;
+    while (cur >= n_pre_items) {
+      const int q = qs.queue_at(stage);
+      int t = -1;
+      if (threadIdx.x == 0 && q >= 8) {
+        t = atomicAdd(qs.counter(q), 1);
+        if (PF) {
+          const int nx = qs.resolve(q, t);
+          __hip_atomic_store(&L.tick, nx >= n_pre_items ? nx - n_pre_items : -1,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+      const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
+      hl::decode::decode_item<D, PF>(da, cur - n_pre_items, L, cy);
+      if (!PF && threadIdx.x == 0) s_tick = t;
+      __syncthreads();  // the unit's LDS reads are done and thread 0's claim is visible
+      int next;
+      if (PF) {
+        const int nd = __builtin_amdgcn_readfirstlane(L.tick);
+        next = nd >= 0 ? nd + n_pre_items : -1;
+      } else {
+        next = q >= 8 ? qs.resolve(q, __builtin_amdgcn_readfirstlane(s_tick)) : -1;
+      }
+      if (trace) hl::record_item(trace, cur, t0);
+      __syncthreads();  // every wave has read the claim before thread 0 overwrites it
+      if (PF && threadIdx.x == 0) L.tick = hl::decode::kTickPending;
       if (next < 0) {
         ++stage;
         next = wg_claim(qs, stage, &s_tick);
       }
-    } else {
-      __syncthreads();  // the item's LDS reads are done before the next item writes
-      next = wg_claim(qs, stage, &s_tick);
+      cur = next;
+      if (cur < 0) break;
     }
-    cur = next;
   }
 }
 
-template <int D>
+template <int D, bool PF>
 hipError_t launch(const PrefillArgs& pa, const DecodeArgs& da, int32_t* counters, int n_pre_items,
-                  int n_dec_items, int cus, hipStream_t st) {
+                  int n_dec_items, int cus, uint64_t* trace, hipStream_t st) {
+  constexpr int lds = kHybridLds<D>;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(hybrid_attn_kernel<D>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kHybridLds<D>);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(hybrid_attn_kernel<D, PF>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipGetLastError();
     attr = true;
   }
   const int total = n_pre_items + n_dec_items;
   const int n_pre_workers = n_pre_items > 0 ? std::min(cus, n_pre_items) : 0;
   const int workers = std::min(2 * cus, total);
-  hipLaunchKernelGGL(hybrid_attn_kernel<D>, dim3(workers), dim3(kThreads), kHybridLds<D>, st, pa,
-                     da, counters, n_pre_items, n_dec_items, std::min(n_pre_workers, workers));
+  hipLaunchKernelGGL((hybrid_attn_kernel<D, PF>), dim3(workers), dim3(kThreads), lds, st,
+                     pa, da, counters, n_pre_items, n_dec_items,
+                     std::min(n_pre_workers, workers), trace);
   return hipGetLastError();
+}
+
+DecodeArgs decode_args(const hl_layer_cfg& cfg, const int32_t* q_start,
+                               const int32_t* num_cached, const hl_bf16* q_rot,
+                               const hl_bf16* q_lo, const hl_bf16* kpool, const hl_bf16* vpool,
+                               int64_t num_blocks, const int32_t* table, int32_t max_blocks,
+                               const hl::Plan& plan, float scale_log2, hl_bf16* attn_out) {
+  return DecodeArgs{q_start,        num_cached,     q_rot,          q_lo,
+                            kpool,          vpool,          (long long)num_blocks, table,
+                            max_blocks,     plan.dec_units, plan.dec_seqs,  plan.split_pages,
+                            cfg.n_q_heads,  cfg.n_kv_heads, scale_log2,     plan.dec_part,
+                            attn_out,       plan.n_dec_units * cfg.n_kv_heads};
+}
+
+float scale_log2_of(const hl_layer_cfg& cfg) {
+  const float scale =
+      cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
+  return scale * 1.4426950408889634f;
 }
 
 }  // namespace
@@ -193,19 +243,22 @@ hipError_t launch_hybrid_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
   const int n_pre_items = plan.n_pre_tiles * cfg.n_q_heads;
   const int n_dec_items = plan.n_dec_units * cfg.n_kv_heads;
   if (n_pre_items + n_dec_items <= 0) return hipSuccess;
-  const float scale = cfg.softmax_scale > 0.f ? cfg.softmax_scale : 1.f / sqrtf((float)cfg.head_dim);
-  const float scale_log2 = scale * 1.4426950408889634f;
+  const float sl2 = scale_log2_of(cfg);
   const PrefillArgs pa{q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
-                       max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                       attn_out, plan.pre_part_o, plan.pre_part_ml};
-  const decode::DecodeArgs da{q_start,        num_cached,     q_rot,          q_lo,
-                              kpool,          vpool,          (long long)num_blocks, table,
-                              max_blocks,     plan.dec_units, plan.dec_seqs,  plan.split_pages,
-                              cfg.n_q_heads,  cfg.n_kv_heads, scale_log2,     plan.dec_part,
-                              attn_out};
-  hipError_t e = cfg.head_dim == 128
-                     ? launch<128>(pa, da, plan.counters, n_pre_items, n_dec_items, cus, st)
-                     : launch<64>(pa, da, plan.counters, n_pre_items, n_dec_items, cus, st);
+                       max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, sl2,
+                       attn_out, plan.pre_part_o, plan.pre_part_ml, nullptr};
+  const DecodeArgs da = decode_args(cfg, q_start, num_cached, q_rot, q_lo, kpool, vpool,
+                                            num_blocks, table, max_blocks, plan, sl2, attn_out);
+  auto go = [&](auto d, auto pf) {
+    return launch<decltype(d)::value, decltype(pf)::value>(pa, da, plan.counters, n_pre_items,
+                                                           n_dec_items, cus, plan.trace, st);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  using On = std::true_type;
+  using Off = std::false_type;
+  hipError_t e = cfg.head_dim == 128 ? (plan.fused_prefetch ? go(D128{}, On{}) : go(D128{}, Off{}))
+                                     : (plan.fused_prefetch ? go(D64{}, On{}) : go(D64{}, Off{}));
   if (e == hipSuccess && n_dec_items > 0) e = launch_decode_merge(cfg, q_start, plan, attn_out, st);
   if (e == hipSuccess && n_pre_items > 0) e = launch_prefill_merge(cfg, q_start, plan, attn_out, st);
   return e;

@@ -48,7 +48,12 @@ template <int D>
 __global__ __launch_bounds__(hl::prefill::kThreads, 2) void prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int item = xcd_item(blockIdx.x, gridDim.x);
+  const uint64_t t0 = a.trace ? (uint64_t)wall_clock64() : 0;
   hl::prefill::prefill_item<D>(a, item / a.Hq, item % a.Hq, smem);
+  if (a.trace) {
+    __syncthreads();
+    hl::record_item(a.trace, item, t0);
+  }
 }
 
 // Combine the parts of each split tile. One workgroup per (split tile, query head, block of
@@ -133,7 +138,7 @@ hipError_t launch_prefill_attention(const hl_layer_cfg& cfg, const int32_t* q_st
   const dim3 grid(plan.n_pre_tiles * cfg.n_q_heads), block(kThreads);
   const PrefillArgs args{q_start, num_cached, q_rot, kpool, vpool, (long long)num_blocks, table,
                          max_blocks, plan.pre_tiles, cfg.n_q_heads, cfg.n_kv_heads, scale_log2,
-                         attn_out, plan.pre_part_o, plan.pre_part_ml};
+                         attn_out, plan.pre_part_o, plan.pre_part_ml, plan.trace};
   if (cfg.head_dim == 128) {
     static bool attr = false;
     if (!attr) {

@@ -56,6 +56,7 @@ struct PrefillArgs {
   hl_bf16* attn_out;
   float* part_o;         // [slot][Hq][128][D]: unnormalised o of a part
   float2* part_ml;       // [slot][Hq][128]: (m, l) of a part, m in the exp2 domain
+  uint64_t* trace;       // optional: work-item trace records (Plan::trace), prefill items first
 };
 
 // Work item (entry, query head h): the entry's query rows against its key tiles [kt0, kt1). An

@@ -72,9 +72,14 @@ __host__ __device__ inline int prefill_parts(int key_tiles, int split) {
   return (key_tiles + split - 1) / split;
 }
 
+constexpr int kDecUnitInts = 16;
+
 struct Plan {
   // device work lists inside the workspace
-  int32_t* dec_units;      // [n_dec_units][3]: (seq, first page, decode index)
+  int32_t* dec_units;      // [n_dec_units][kDecUnitInts]: (seq, first page, decode index, units
+                           // of the sequence, its query row, its KV length, 0, 0, then the block
+                           // ids of its pages first .. first + 7, clamped to its last page):
+                           // everything a unit's first page pairs need, in one 64-byte record
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
   int32_t* pre_tiles;      // [n_pre_tiles][kPreEntry]: (seq, first query row within the sequence,
                            // first key tile, end key tile, partial slot or -1 if unsplit)
@@ -87,7 +92,21 @@ struct Plan {
   int32_t n_dec_units, n_dec_seqs, n_pre_tiles, n_pre_merge;
   int32_t split_pages;     // pages per decode work unit
   int32_t pre_split;       // key tiles per prefill work part
+  bool fused_prefetch = false;  // fused launch: decode units prefetch the next (decode-heavy)
+  uint64_t* trace = nullptr;  // optional [items][3]: (start, end, worker) of every work item,
+                              // prefill items first, then decode units (see record_item)
 };
+
+// Trace record of one work item: its start and end on the device's constant-rate clock and the
+// workgroup that ran it. Thread 0 writes it once the whole workgroup has finished the item.
+HL_DEV void record_item(uint64_t* trace, int item, uint64_t t0) {
+  if (threadIdx.x == 0) {
+    uint64_t* r = trace + 3 * (size_t)item;
+    r[0] = t0;
+    r[1] = (uint64_t)wall_clock64();
+    r[2] = blockIdx.x;
+  }
+}
 
 // Per-token data of one step (filled by the first prep pass, read by the QKV GEMM epilogue).
 constexpr int32_t kDecodeBit = 1 << 30;  // positions are below 2^30 (checked on the host)
@@ -127,7 +146,8 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
                        int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
                        hipStream_t st, const Plan* plan = nullptr);
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
-                       const Plan& plan, hipStream_t st);
+                       const int32_t* table, int32_t max_blocks, const Plan& plan,
+                       hipStream_t st);
 constexpr int kPlanCounters = 16;
 constexpr int kCounterStride = 64;  // int32 slots per counter: each on its own 256-byte line
 constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
@@ -172,7 +192,8 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
                                    const hl_bf16* q_lo,
                                    const hl_bf16* kpool, const hl_bf16* vpool,
                                    int64_t num_blocks, const int32_t* table, int32_t max_blocks,
-                                   const Plan& plan, hl_bf16* attn_out, hipStream_t st);
+                                   const Plan& plan, int32_t cus, hl_bf16* attn_out,
+                                   hipStream_t st);
 
 hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, const Plan& plan,
                                hl_bf16* attn_out, hipStream_t st);

@@ -8,19 +8,22 @@ constexpr int kThreads = 1024;
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restrict__ q_start,
                                                         const int32_t* __restrict__ num_cached,
-                                                        int num_seqs, hl::Plan p) {
+                                                        int num_seqs,
+                                                        const int32_t* __restrict__ table,
+                                                        int max_blocks, hl::Plan p) {
   __shared__ int wt[5][kThreads / 64];
-  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, p, wt);
+  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, p, wt);
 }
 
 }  // namespace
 
 namespace hl {
 hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_t num_seqs,
-                       const Plan& plan, hipStream_t st) {
+                       const int32_t* table, int32_t max_blocks, const Plan& plan,
+                       hipStream_t st) {
   if (num_seqs <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, st, q_start, num_cached, num_seqs,
-                     plan);
+                     table, max_blocks, plan);
   return hipGetLastError();
 }
 }  // namespace hl

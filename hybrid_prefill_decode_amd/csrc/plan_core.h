@@ -55,7 +55,8 @@ HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[
 // `wt` is NT / 64 ints x 5 of LDS.
 template <int NT>
 HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict__ num_cached,
-                  int num_seqs, const hl::Plan& p, int (*wt)[NT / 64]) {
+                  int num_seqs, const int32_t* __restrict__ table, int max_blocks,
+                  const hl::Plan& p, int (*wt)[NT / 64]) {
   constexpr int QT = hl::kPrefillQTile;
   if (threadIdx.x < hl::kPlanCounters) p.counters[threadIdx.x * hl::kCounterStride] = 0;
   int base_u = 0, base_d = 0, base_e = 0, base_p = 0, base_m = 0;
@@ -88,10 +89,21 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
     const int off_u = base_u + off[0], off_d = base_d + off[1], off_e = base_e + off[2],
               off_p = base_p + off[3], off_m = base_m + off[4];
     if (is_dec) {
+      const int row = q_start[s];
+      const int pages = (c + qlen + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+      const int32_t* trow = table + (size_t)s * max_blocks;
       for (int u = 0; u < units; ++u) {
-        p.dec_units[3 * (off_u + u)] = s;
-        p.dec_units[3 * (off_u + u) + 1] = u * p.split_pages;
-        p.dec_units[3 * (off_u + u) + 2] = off_d;
+        int32_t* r = p.dec_units + (size_t)hl::kDecUnitInts * (off_u + u);
+        const int pg0 = u * p.split_pages, last = min(pg0 + p.split_pages, pages) - 1;
+        r[0] = s;
+        r[1] = pg0;
+        r[2] = off_d;
+        r[3] = units;
+        r[4] = row;
+        r[5] = c + qlen;
+        r[6] = 0;
+        r[7] = 0;
+        for (int j = 0; j < 8; ++j) r[8 + j] = trow[min(pg0 + j, last)];
       }
       p.dec_seqs[3 * off_d] = s;
       p.dec_seqs[3 * off_d + 1] = off_u;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   const int row = blockIdx.x;
   if (TOKEN_INFO && row == rows) {  // the extra workgroup: the attention work lists
     __shared__ int wt[5][kThreads / 64];
-    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, plan, wt);
+    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, plan, wt);
     return;
   }
   if (TOKEN_INFO) {

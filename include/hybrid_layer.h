@@ -184,7 +184,8 @@ int hl_workspace_bytes(const hl_batch_desc* batch, size_t* bytes);
  * for tuning and tests. Work splits follow from the batch alone ("Chunked prefill (stall-free
  * batching), explained", "How it works, step by step": a chunk attends to its cached prefix plus
  * itself; decode attention is split over the KV length). Outputs:
- *   fused          1 if prefill and decode attention run in one launch, else 0;
+ *   fused          0 for two launches; 1 if prefill and decode attention run in one launch, 2 if
+ *                  they do and its decode units also prefetch their successors (decode-heavy);
  *   split_pages    KV pages per decode work unit;
  *   decode_units   decode work units (each covers all KV heads);
  *   prefill_parts  prefill work entries: 128-query-row tiles, or parts of a tile's key range;
@@ -477,6 +478,26 @@ int hl_attention_build_lists(const hl_batch_desc* batch, const hl_kv_pages* kv,
 int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
                      const hl_kv_pages* kv, const hl_block_table* block_table, hl_bf16* attn_out,
                      int32_t paths);
+
+/* hl_attention_run that also records every work item it runs, for measuring how the two paths
+ * share the GPU when they run in one launch (the overlap the ConfluxServe summary asks of them,
+ * "Why can linear layers be batched but attention cannot?": decode keeping most of its standalone
+ * bandwidth while prefill runs). trace (device, trace_entries uint64 values, 16-byte aligned)
+ * receives three values per item: start and end time on the device's constant-rate clock
+ * (hl_trace_clock_khz), and the workgroup that ran it. Items are numbered prefill items first
+ * (entry * n_q_heads + query head, entries as hl_attention_plan's prefill_parts), then decode work
+ * (unit * n_kv_heads + kv head, units as its decode_units); a path that does not run leaves its
+ * records untouched. Results equal hl_attention_run's bit for bit. Errors: those of
+ * hl_attention_run; HL_ERR_NULL for a NULL trace, HL_ERR_ALIGN, HL_ERR_ARG if trace_entries is
+ * less than 3 * (prefill_parts * n_q_heads + decode_units * n_kv_heads). */
+int hl_attention_run_traced(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_bf16* q_lo,
+                            const hl_kv_pages* kv, const hl_block_table* block_table,
+                            hl_bf16* attn_out, int32_t paths, uint64_t* trace,
+                            size_t trace_entries);
+
+/* Ticks per millisecond of the clock hl_attention_run_traced records (the current device's
+ * constant-rate wall clock). Errors: HL_ERR_NULL, HL_ERR_HIP. */
+int hl_trace_clock_khz(int32_t* khz);
 
 #ifdef __cplusplus
 }

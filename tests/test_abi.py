@@ -384,3 +384,30 @@ def test_noalloc_step_refuses_batches_beyond_its_array():
     assert B.lib().hybrid_layer_step_noalloc(ctypes.byref(d), None, None, None,
                                              None) == B.HL_ERR_WORKSPACE
     assert B.lib().hybrid_layer_step_noalloc(None, None, None, None, None) == B.HL_ERR_NULL
+
+
+def test_attention_run_traced_argument_checks():
+    """The traced run refuses a missing, misaligned or short trace buffer on the host."""
+    spec, b, pool = _fake_batch([(20, 4), (7, 1)])
+    cfg = B.layer_cfg(spec.shape)
+    s = spec.shape
+    need = B.workspace_bytes(cfg, b)
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    off = (-ws.data_ptr()) % 256
+    d = B._desc(cfg, b, None, None, None, with_stream=False)
+    d.workspace = ws.data_ptr() + off
+    d.workspace_bytes = need
+    q = torch.zeros(spec.num_tokens * s.n_q_heads * s.head_dim + 64, dtype=torch.bfloat16)
+    kp = torch.zeros(pool * s.n_kv_heads * 16 * s.head_dim, dtype=torch.bfloat16)
+    kv = B.KvPages(kp.data_ptr(), kp.data_ptr(), pool)
+    bt = B.BlockTable(b.table.data_ptr(), b.h_table.ctypes.data_as(B._c_i32p), b.max_blocks)
+    plan = B.attention_plan(cfg, b)
+    items = plan["prefill_parts"] * s.n_q_heads + plan["decode_units"] * s.n_kv_heads
+    tr = torch.zeros(3 * items + 8, dtype=torch.int64)
+    run = lambda t, n: B.lib().hl_attention_run_traced(
+        ctypes.byref(d), q.data_ptr(), None, ctypes.byref(kv), ctypes.byref(bt), q.data_ptr(), 3,
+        t, n)
+    assert run(None, 3 * items) == B.HL_ERR_NULL
+    assert run(tr.data_ptr() + 8, 3 * items) == B.HL_ERR_ALIGN
+    assert run(tr.data_ptr(), 3 * items - 1) == B.HL_ERR_ARG
+    assert B.lib().hl_trace_clock_khz(None) == B.HL_ERR_NULL

@@ -29,7 +29,7 @@ def test_layer_step_graph_replays(attention):
                                 True, shape.head_dim)
     say(f"graph replay ({attention}): T={spec.num_tokens}, plan {plan}, QKV choice {choice}")
     assert choice[2] == 3 and plan["prefill_merges"] > 0 and plan["decode_units"] > 0
-    assert plan["fused"] == (attention == B.HL_ATTN_FUSED)
+    assert (plan["fused"] >= 1) == (attention == B.HL_ATTN_FUSED)
     x = workloads.hidden_states(spec, DEV)
     w = workloads.weights(spec, DEV)
     kp, vp = make_pools(spec, table, pool, DEV)

@@ -385,6 +385,10 @@ ATTN_CASES = {
     "split_long_prefix": (workloads.SHAPES["tiny"], [(3000, 100), (2500, 1), (40, 1)]),
     "split_d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(5000, 200), (70, 1)]),
     "split_causal": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 1000)]),
+    # decode-heavy at d = 128: fused, each worker runs several decode units in a row and prefetches
+    # the next one (contexts 0 mod 16, 15 mod 16 and in between)
+    "decode_heavy_d128": (workloads.LayerShape(1024, 8, 2, 128, 512),
+                          [(37, 70)] + [(2000 + 97 * i + (i % 3) * 7, 1) for i in range(200)]),
 }
 
 
@@ -400,7 +404,7 @@ def test_attention_paths_vs_oracle(case, attention):
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV, attention=attention)
     if attention == B.HL_ATTN_FUSED and spec.num_tokens > len(spec.seqs) and \
             any(n == 1 for _, n in spec.seqs):
-        assert B.attention_plan(cfg, b)["fused"] == 1
+        assert B.attention_plan(cfg, b)["fused"] >= 1
     if case.startswith("split"):
         plan = B.attention_plan(cfg, b)
         say(f"  plan {plan}")
@@ -483,6 +487,42 @@ def test_attention_two_part_query_vs_oracle(case, attention):
             assert np.array_equal(g2[rows], got[rows]), f"paths={paths} rows differ"
         if other.size:
             assert np.isnan(g2[other]).all(), f"paths={paths} wrote other rows"
+
+
+@pytest.mark.parametrize("attention", [B.HL_ATTN_FUSED, B.HL_ATTN_SEPARATE],
+                         ids=["fused", "separate"])
+@pytest.mark.parametrize("case", ["ragged", "many_decodes", "split_long_prefix", "g5_d128"])
+def test_attention_traced_run(case, attention):
+    """hl_attention_run_traced: rows bit-identical to hl_attention_run, and one record per work
+    item (start <= end on the constant-rate clock, a valid workgroup), prefill items first."""
+    shape, seqs = ATTN_CASES[case]
+    spec = workloads.custom_spec(shape, seqs, 77)
+    say(f"attention traced {case} mode={attention}")
+    table, pool, full, kp, vp, q = _attention_inputs(spec, 5)
+    s = spec.shape
+    cfg = B.layer_cfg(s)
+    b = B.Batch(spec.q_start, spec.num_cached, table, DEV, attention=attention)
+    plan = B.attention_plan(cfg, b)
+    items = plan["prefill_parts"] * s.n_q_heads + plan["decode_units"] * s.n_kv_heads
+    ws = B.alloc_workspace(cfg, b, DEV)
+    ref = torch.full_like(q, float("nan"))
+    B.attention_build_lists(cfg, b, kp, vp, ws)
+    B.attention_run(cfg, b, q, kp, vp, ref, ws)
+    out = torch.full_like(q, float("nan"))
+    trace = torch.zeros(3 * items + 6, dtype=torch.int64, device=DEV)
+    B.attention_build_lists(cfg, b, kp, vp, ws)
+    B.attention_run_traced(cfg, b, q, kp, vp, out, ws, trace)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(ref))
+    rec = trace.cpu().numpy()
+    assert (rec[3 * items:] == 0).all(), "records past the items"
+    rec = rec[:3 * items].reshape(items, 3)
+    assert (rec[:, 0] > 0).all() and (rec[:, 1] >= rec[:, 0]).all(), "an item without a record"
+    assert (rec[:, 2] >= 0).all() and (rec[:, 2] < max(items, 2 * 256 * 8)).all()
+    khz = B.trace_clock_khz()
+    span_us = (rec[:, 1].max() - rec[:, 0].min()) * 1000.0 / khz
+    say(f"  {items} items over {span_us:.1f} us (clock {khz} kHz)")
+    assert 0 < span_us < 1e6
 
 
 def test_rope_kv_append_vs_oracle():
