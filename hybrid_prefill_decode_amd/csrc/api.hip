@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <vector>
 
 #include "common.h"
@@ -189,31 +190,89 @@ int pick_split_fused(const hl_batch_desc* b) {
 }
 
 // Key tiles per prefill work part. Items are (tile or part, query head), two resident per compute
-// unit; an item's time is a start-up (query load, pipeline fill) plus one step per key tile.
-// Whole tiles are kept whenever the batch has at least one item per compute unit: equalising
-// uneven tiles by splitting them was measured slower there (the start-up, the partial write and
-// the merge outweigh the shorter tail). With fewer items — a short chunk after a long cached
-// prefix has only Hq — most compute units would idle, so tiles are cut into near-equal parts
-// sized to give every slot about one part, never below kMinPart key tiles. The choice depends on
-// the batch only, so the fused and the separate launches run the same parts and stay
+// unit, dealt to the 8 XCDs in (entry, KV head) units (prefill_item_at) and dispatched longest
+// first. An item costs a start-up plus one step per key tile; a part of a split tile costs more:
+// its fp32 partial rows are written and read back by the merge. A few near-equal items just above
+// a multiple of the resident slots leave most slots idle through a last round, and a short chunk
+// after a long cached prefix has only Hq items, so the rule compares splits of every tile into
+// near-equal parts: for each candidate count of parts of the longest tile it replays the greedy
+// longest-first dispatch of one XCD's items over that XCD's slots and keeps the shortest
+// makespan (fewer parts on a tie within 2 %), parts never below kMinPart key tiles. The choice
+// depends on the batch only, so the fused and the separate launches run the same parts and stay
 // bit-identical.
+namespace {
+constexpr double kItemStart = 2.0;  // start-up of an item, in key-tile steps
+constexpr double kPartCost = 6.0;   // partial write + merge read of a split part, in steps
+constexpr double kMergeLaunch = 3.0;  // the merge launch that any split adds, in steps
+
+// greedy dispatch of `cost` (in order) over `slots` slots: the makespan
+double replay(const std::vector<double>& cost, int slots, std::vector<double>& heap) {
+  heap.assign((size_t)slots, 0.0);
+  double end = 0.0;
+  for (const double c : cost) {
+    std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+    heap.back() += c;
+    end = std::max(end, heap.back());
+    std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+  }
+  return end;
+}
+}  // namespace
+
 int pick_pre_split(const hl_batch_desc* b) {
-  constexpr int64_t kMinPart = 8;
-  int64_t work = 0, longest = 0, tiles = 0;
+  constexpr int kMinPart = 8;
+  std::vector<int> tiles;  // key tiles of each prefill tile, in entry order (last tile first)
+  int longest = 0;
   for (int s = 0; s < b->num_seqs; ++s) {
     const int n = b->h_q_start[s + 1] - b->h_q_start[s], c = b->h_num_cached[s];
     if (n < 2) continue;
-    for (int r0 = 0; r0 < n; r0 += hl::kPrefillQTile) {
-      const int64_t k = hl::prefill_key_tiles(c, r0, std::min(hl::kPrefillQTile, n - r0));
-      work += k;
-      longest = std::max(longest, k);
-      ++tiles;
+    for (int r0 = ((n - 1) / hl::kPrefillQTile) * hl::kPrefillQTile; r0 >= 0;
+         r0 -= hl::kPrefillQTile) {
+      tiles.push_back(hl::prefill_key_tiles(c, r0, std::min(hl::kPrefillQTile, n - r0)));
+      longest = std::max(longest, tiles.back());
     }
   }
-  const int64_t hq = b->cfg->n_q_heads, cus = device_cus();
-  if (tiles * hq >= cus) return 1 << 30;
-  const int64_t split = std::max<int64_t>(kMinPart, (work * hq + 2 * cus - 1) / (2 * cus));
-  return split >= longest ? 1 << 30 : (int)split;
+  const int64_t hq = b->cfg->n_q_heads, hkv = b->cfg->n_kv_heads, g = hq / hkv;
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t items = (int64_t)tiles.size() * hq;
+  if (tiles.empty() || longest < 2 * kMinPart || items >= 8 * slots) return 1 << 30;
+  const int xslots = (int)std::max<int64_t>(1, slots / 8);
+  // candidate part counts of the longest tile: 1..8, the counts that fill the slots one to three
+  // times over, and the finest split allowed
+  std::vector<int> cand = {1, 2, 3, 4, 5, 6, 8, longest / kMinPart};
+  for (int64_t k = 1; k <= 3; ++k) cand.push_back((int)((k * slots + items - 1) / items));
+  std::vector<double> cost, heap;
+  double best = 0.0;
+  int best_split = 1 << 30;
+  int64_t best_parts = 0;
+  for (const int pc : cand) {
+    if (pc < 1) continue;
+    const int split = (longest + pc - 1) / pc;
+    if (split < kMinPart && pc > 1) continue;
+    int64_t parts_total = 0;
+    for (const int nkt : tiles) parts_total += hl::prefill_parts(nkt, split);
+    if (parts_total * hq > 8 * slots && pc > 1) continue;  // the tail is already short
+    // section 0 of the dealing: units u = entry * Hkv + k with u % 8 == 0, g items each
+    cost.clear();
+    int64_t e = 0;
+    for (const int nkt : tiles) {
+      const int parts = hl::prefill_parts(nkt, split);
+      for (int j = 0; j < parts; ++j, ++e) {
+        const double steps = (double)((int64_t)(j + 1) * nkt / parts - (int64_t)j * nkt / parts);
+        const double c = steps + kItemStart + (parts > 1 ? kPartCost : 0.0);
+        for (int64_t k = 0; k < hkv; ++k)
+          if ((e * hkv + k) % 8 == 0)
+            for (int64_t i = 0; i < g; ++i) cost.push_back(c);
+      }
+    }
+    const double t = replay(cost, xslots, heap) + (parts_total > (int64_t)tiles.size() ? kMergeLaunch : 0.0);
+    if (best_parts == 0 || t < 0.98 * best || (t <= best && parts_total < best_parts)) {
+      best = t;
+      best_split = pc == 1 ? (1 << 30) : split;
+      best_parts = parts_total;
+    }
+  }
+  return best_split;
 }
 
 void make_plan(const hl_batch_desc* b, HostPlan* p) {

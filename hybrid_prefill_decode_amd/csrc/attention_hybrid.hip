@@ -12,8 +12,9 @@
 // every unit holds one worker of each kind: the split of the units between the paths happens
 // inside each unit, where the matrix cores and the memory pipeline are both kept busy.
 //
-// Queues. The items of each kind are dealt to 8 queues in contiguous runs, one per XCD (the query
-// heads of one KV head are consecutive prefill items, so their K/V tiles hit in that XCD's L2). A
+// Queues. The items of each kind are dealt to 8 queues in contiguous runs of positions, one per
+// XCD; prefill positions map to items through prefill_item_at (whole (entry, KV head) units per
+// XCD, longest first, so the XCDs get near-equal prefill work and share K/V tiles in L2). A
 // worker's first item needs no claim: the l-th worker of a kind on XCD x takes the l-th item of
 // that kind's queue x. Further items are claimed from per-queue device counters (zeroed by the
 // step's plan kernel, each on its own 256-byte line) that number the claims past those first
@@ -139,9 +140,10 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
       // prefill items are long and few: the next claim waits for the item's end (a ticket taken
       // early would reserve an item that an idle worker could have run)
       const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
-      hl::prefill::prefill_item<D>(pa, cur / pa.Hq, cur % pa.Hq, smem);
+      const int item = hl::prefill_item_at(cur, n_pre_items / pa.Hq, pa.Hq, pa.Hkv);
+      hl::prefill::prefill_item<D>(pa, item / pa.Hq, item % pa.Hq, smem);
       __syncthreads();  // the item's LDS reads are done before the next item writes
-      if (trace) hl::record_item(trace, cur, t0);
+      if (trace) hl::record_item(trace, item, t0);
       cur = wg_claim(qs, stage, &s_tick);
       continue;
     }

@@ -42,12 +42,13 @@ HL_DEV int xcd_item(int bid, int nblk) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-// One workgroup per work item; the items of one (tile, KV head) group are consecutive in work
-// order and so share an XCD (their K/V tiles hit in its L2).
+// One workgroup per work item. Positions map to items through prefill_item_at, so each XCD runs
+// whole (entry, KV head) units, longest key ranges first, and the XCDs get near-equal work.
 template <int D>
 __global__ __launch_bounds__(hl::prefill::kThreads, 2) void prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int item = hl::prefill_item_at(xcd_item(blockIdx.x, gridDim.x), gridDim.x / a.Hq, a.Hq,
+                                       a.Hkv);
   const uint64_t t0 = a.trace ? (uint64_t)wall_clock64() : 0;
   hl::prefill::prefill_item<D>(a, item / a.Hq, item % a.Hq, smem);
   if (a.trace) {

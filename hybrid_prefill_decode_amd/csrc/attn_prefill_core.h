@@ -115,15 +115,18 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
   const int pg0 = tid / SM::kChunksPerPage, w = tid % SM::kChunksPerPage;
   // K: chunk w of a chunk-major page is token w % 16, chunk w / 16
   const int k_dst = k_off<D>(pg0 * 16 + w % 16, w / 16);
-  // V^T: dim row w / 2 of page pg, token quads 2 (w & 1) and 2 (w & 1) + 1, which sit at
-  // quad positions (w & 1) and 2 + (w & 1) (8-byte pieces)
-  const int v_dst0 = v_off<D>(pg0, w >> 1, 0) + 8 * (w & 1);
-  const int v_dst1 = v_off<D>(pg0, w >> 1, 1) + 8 * (w & 1);
+  // V^T: this thread moves chunk wv of the page, w with bits 3 and 4 swapped, so that each
+  // 16 lanes store rows {0..3, 8..11} (+ 4 or 16 multiples) and their 8-byte pieces fall in
+  // distinct banks. Chunk wv is dim row wv / 2, token quads 2 (wv & 1) and 2 (wv & 1) + 1, which
+  // sit at quad positions (wv & 1) and 2 + (wv & 1).
+  const int wv = (w & ~24) | ((w & 8) << 1) | ((w & 16) >> 1);
+  const int v_dst0 = v_off<D>(pg0, wv >> 1, 0) + 8 * (wv & 1);
+  const int v_dst1 = v_off<D>(pg0, wv >> 1, 1) + 8 * (wv & 1);
   static_assert(kPagesPerI * 16 * D * 2 == 4096 && kPagesPerI * D * 32 == 4096, "tile slice");
   // byte addresses: page base + this thread's chunk; a block adds blk * block_bytes
   const uint32_t block_bytes = (uint32_t)(Hkv * page_elems * 2);
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kpool) + (size_t)kvh * page_elems * 2 + 16 * w;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vpool) + (size_t)kvh * page_elems * 2 + 16 * w;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vpool) + (size_t)kvh * page_elems * 2 + 16 * wv;
   const uint32_t nb = (uint32_t)min(num_blocks, (long long)INT32_MAX);
 
   u32x4 rk[SM::kPer], rv[SM::kPer];
@@ -157,7 +160,7 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     for (int i = 0; i < SM::kPer; ++i) {
       u32x4 vv = rv[i];
       if constexpr (decltype(zero)::value) {
-        const int tok0 = (4 * kt + pg0 + kPagesPerI * i) * HL_BLOCK_SIZE + 8 * (w & 1);
+        const int tok0 = (4 * kt + pg0 + kPagesPerI * i) * HL_BLOCK_SIZE + 8 * (wv & 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t lo_ok = (tok0 + 2 * e < kv_len) ? 0x0000ffffu : 0u;

@@ -72,6 +72,25 @@ __host__ __device__ inline int prefill_parts(int key_tiles, int split) {
   return (key_tiles + split - 1) / split;
 }
 
+// Prefill work item (entry * Hq + query head) at position p of the dispatch order. The launches
+// hand each of the 8 XCDs a contiguous run of positions; the order deals the items to 8 sections
+// in units of one entry and one KV head (its Hq / Hkv query heads, which read the same K/V
+// tiles): unit u = entry * Hkv + kv head goes to section u % 8, each section keeping the entries'
+// order (longest key range first). With 8 KV heads every section is one KV head over all entries,
+// so the XCDs get equal work and each streams one head's keys and values through its own L2.
+__host__ __device__ inline int prefill_item_at(int p, int n_ent, int Hq, int Hkv) {
+  const int g = Hq / Hkv, n_units = n_ent * Hkv;
+  for (int x = 0; x < 8; ++x) {
+    const int here = (x < n_units ? (n_units - x + 7) / 8 : 0) * g;
+    if (p < here) {
+      const int u = x + 8 * (p / g);
+      return (u / Hkv) * Hq + (u % Hkv) * g + p % g;
+    }
+    p -= here;
+  }
+  return -1;  // p out of range
+}
+
 constexpr int kDecUnitInts = 16;
 
 struct Plan {

@@ -381,10 +381,11 @@ ATTN_CASES = {
     "many_prefill": (workloads.LayerShape(1280, 10, 2, 128, 512),
                      [(64 * i, 257 + 31 * i) for i in range(6)] + [(900, 1), (3, 1)]),
     # prefill tiles cut into key-range parts and merged: a short chunk after a long prefix, a
-    # d = 128 chunk with a ragged last tile, a causal chunk alone (its last tiles are the longest)
+    # d = 128 chunk with a ragged last tile, a causal chunk alone (its last tiles are the longest,
+    # split where they exceed 8 key tiles; 1500 rows leave a ragged last tile)
     "split_long_prefix": (workloads.SHAPES["tiny"], [(3000, 100), (2500, 1), (40, 1)]),
     "split_d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(5000, 200), (70, 1)]),
-    "split_causal": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 1000)]),
+    "split_causal": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 1500)]),
     # decode-heavy at d = 128: fused, each worker runs several decode units in a row and prefetches
     # the next one (contexts 0 mod 16, 15 mod 16 and in between)
     "decode_heavy_d128": (workloads.LayerShape(1024, 8, 2, 128, 512),
