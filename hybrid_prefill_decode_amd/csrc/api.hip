@@ -197,9 +197,11 @@ int pick_split_fused(const hl_batch_desc* b) {
 // after a long cached prefix has only Hq items, so the rule compares splits of every tile into
 // near-equal parts: for each candidate count of parts of the longest tile it replays the greedy
 // longest-first dispatch of one XCD's items over that XCD's slots and keeps the shortest
-// makespan (fewer parts on a tie within 2 %), parts never below kMinPart key tiles. The choice
-// depends on the batch only, so the fused and the separate launches run the same parts and stay
-// bit-identical.
+// makespan (fewer parts on a tie within 2 %), parts never below kMinPart key tiles. A fused
+// launch fills the prefill tail with decode units instead, so there tiles are split only when
+// the prefill items are fewer than the compute units (measured on the 70B-shaped batch: splitting
+// its 256 items costs 1.5 %). The choice depends on the batch's plan only, so every launch of one
+// batch (both paths, or either alone) runs the same parts and gives bit-identical rows.
 namespace {
 constexpr double kItemStart = 2.0;  // start-up of an item, in key-tile steps
 constexpr double kPartCost = 6.0;   // partial write + merge read of a split part, in steps
@@ -219,7 +221,7 @@ double replay(const std::vector<double>& cost, int slots, std::vector<double>& h
 }
 }  // namespace
 
-int pick_pre_split(const hl_batch_desc* b) {
+int pick_pre_split(const hl_batch_desc* b, bool fused) {
   constexpr int kMinPart = 8;
   std::vector<int> tiles;  // key tiles of each prefill tile, in entry order (last tile first)
   int longest = 0;
@@ -236,6 +238,16 @@ int pick_pre_split(const hl_batch_desc* b) {
   const int64_t slots = 2 * (int64_t)device_cus();
   const int64_t items = (int64_t)tiles.size() * hq;
   if (tiles.empty() || longest < 2 * kMinPart || items >= 8 * slots) return 1 << 30;
+  if (fused) {
+    // a fused launch fills the prefill tail with decode units: parts only when there are fewer
+    // prefill items than compute units, sized to give every compute unit about one
+    const int64_t cus = device_cus();
+    if (items >= cus) return 1 << 30;
+    int64_t work = 0;
+    for (const int nkt : tiles) work += nkt;
+    const int64_t split = std::max<int64_t>(kMinPart, (work * hq + cus - 1) / cus);
+    return split >= longest ? 1 << 30 : (int)split;
+  }
   const int xslots = (int)std::max<int64_t>(1, slots / 8);
   // candidate part counts of the longest tile: 1..8, the counts that fill the slots one to three
   // times over, and the finest split allowed
@@ -309,7 +321,7 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
   // gains 4 %, prefill-heavy batches lose 5-10 %).
   p->fused_prefetch = p->fused && dec_us >= 4.0 * pre_us;
   p->split_pages = p->fused ? pick_split_fused(b) : pick_split(b);
-  p->pre_split = pick_pre_split(b);
+  p->pre_split = pick_pre_split(b, p->fused);
   for (int s = 0; s < b->num_seqs; ++s) {
     const int qlen = b->h_q_start[s + 1] - b->h_q_start[s];
     if (qlen == 1) {

@@ -289,17 +289,23 @@ def _key_tiles(c, n):
     ("causal_1500_d128", "small_d128", [(0, 1500)], True),
     # config 2's 1024-token chunk: tiles of at most 16 key tiles, half the slots -> whole tiles
     ("cfg2", "qwen3_8b", [(0, 1024)] + [(8192, 1)] * 16, False),
-    # config 3's 2048-token chunk at 16K: 640 even items, just above the 512 resident slots,
-    # would leave a last round three-quarters idle -> split
-    ("cfg3", "qwen3_14b", [(16384, 2048)] + [(3000, 1)] * 96, True),
+    # config 3's 2048-token chunk at 16K alone: 640 even items, just above the 512 resident
+    # slots, would leave a last round three-quarters idle -> split
+    ("cfg3_prefill", "qwen3_14b", [(16384, 2048)], True),
+    # the same chunk with config 3's decodes runs fused: decode units fill the prefill tail, so
+    # tiles split only when there are fewer prefill items than compute units -> whole tiles
+    ("cfg3", "qwen3_14b", [(16384, 2048)] + [(3000, 1)] * 96, False),
+    # config 5's 512-token chunk at 8K with 512 decodes: fused, 256 items -> whole tiles
+    ("cfg5", "llama_70b", [(8192, 512)] + [(4000, 1)] * 512, False),
     # config 4's 4096-token causal chunk: 1024 uneven items, dispatched longest first -> whole
     ("cfg4", "qwen3_8b", [(0, 4096)] + [(1125, 1)] * 64, False),
     ("tiny_chunk", "tiny", [(64, 64), (32, 1)], False),
 ])
 def test_attention_plan_prefill_parts(name, shape, seqs, splits):
     """Prefill tiles are cut into parts where a few long tiles or a nearly empty last round would
-    idle the launch; the counts agree with the parts the split size implies (host-only, on a
-    host without a GPU the library assumes 256 compute units)."""
+    idle the launch (in a fused launch only below one item per compute unit); the counts agree
+    with the parts the split size implies (host-only, on a host without a GPU the library assumes
+    256 compute units)."""
     shape = workloads.LayerShape(1024, 8, 2, 128, 512) if shape == "small_d128" else \
         workloads.SHAPES[shape]
     p = _plan(shape, seqs)
