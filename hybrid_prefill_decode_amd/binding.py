@@ -427,7 +427,8 @@ def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: int = 0, res
                        epilogue: int = HL_EPI_NONE, workspace=None, stream=None,
                        row_scale=None) -> None:
     """stream_k: 0 one tile per workgroup, 1 stream-K (plain / residual), s >= 2 split-K into s
-    K ranges."""
+    K ranges, -s one tile per workgroup with the tiles past the last full round split into s K
+    ranges."""
     m, k = a.shape
     n = w.shape[0]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -452,7 +453,8 @@ def gemm_tile_choice(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE,
                      with_workspace: bool = True, qkv_head_dim: int = 0):
     """(tile_m, tile_n, schedule, splits) that hl_gemm_bf16_nt (or, with qkv_head_dim, the step's
     QKV projection) uses for this shape; schedule 0 = one tile per workgroup, 1 = stream-K, 2 =
-    the weight-streaming path of up to 64 token rows, 3 = split-K into `splits` K ranges.
+    the weight-streaming path of up to 64 token rows, 3 = split-K into `splits` K ranges, 4 = one
+    tile per workgroup with the tiles past the last full round split into `splits` K ranges.
     Host-only."""
     tm, tn, sk, sp = (ctypes.c_int32(0) for _ in range(4))
     _check(lib().hl_gemm_tile_choice(m, n, k, epilogue, int(bool(with_workspace)), qkv_head_dim,

@@ -654,11 +654,12 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
   }
   int sched = 0;
   if (with_workspace)
-    sched = (qkv_head_dim || epilogue == HL_EPI_SWIGLU) ? hl::kSchedSplitK : hl::kSchedStreamK;
+    sched = ((qkv_head_dim || epilogue == HL_EPI_SWIGLU) ? hl::kSchedSplitK : hl::kSchedStreamK) |
+            hl::kSchedTail;
   const hl::TileChoice tc = hl::choose_tiles(m, n, k, sched, qkv_head_dim ? qkv_head_dim : 1);
   *tile_m = tc.bm;
   *tile_n = tc.bn;
-  *stream_k = tc.sk ? 1 : (tc.splits >= 2 ? 3 : 0);
+  *stream_k = tc.sk ? 1 : (tc.splits >= 2 ? (tc.tail ? 4 : 3) : 0);
   *splits = tc.splits >= 2 ? tc.splits : 0;
   return HL_OK;
 }
@@ -702,15 +703,20 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
   const int rc = check_gemm_args(a, w, c, residual, m, n, k, epilogue);
   if (rc) return rc;
   if (!hl::gemm_tile_supported(tile_m, tile_n) || n % tile_n) return HL_ERR_ARG;
-  if (stream_k < 0) return HL_ERR_ARG;
+  if (stream_k == -1 || stream_k < -8) return HL_ERR_ARG;
   if (stream_k && (!workspace || workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
     return HL_ERR_ARG;
-  // 1: stream-K (plain / residual); s >= 2: split-K into s K ranges
+  // 1: stream-K (plain / residual); s >= 2: split-K into s K ranges; -s (2 <= s <= 8): one tile
+  // per workgroup, the tiles past the last full round split into s K ranges
   if (stream_k == 1 && epilogue == HL_EPI_SWIGLU) return HL_ERR_ARG;
   if (stream_k >= 2 && (stream_k > k / 64 || !hl::gemm_split_fits(m, n, tile_m, tile_n, stream_k)))
     return HL_ERR_ARG;
+  if (stream_k <= -2 && (-stream_k > k / 64 || !hl::gemm_tail_fits(m, n, tile_m, tile_n, -stream_k)))
+    return HL_ERR_ARG;
   if (m == 0) return HL_OK;
-  const hl::TileChoice tc{tile_m, tile_n, stream_k == 1, stream_k >= 2 ? stream_k : 0};
+  const hl::TileChoice tc{tile_m, tile_n, stream_k == 1,
+                          stream_k >= 2 ? stream_k : (stream_k <= -2 ? -stream_k : 0),
+                          stream_k <= -2};
   return hip_rc(hl::launch_gemm_tiles(a, w, c, m, n, k, plain_epi(epilogue, residual, row_scale),
                                       tc, workspace, static_cast<hipStream_t>(stream)));
 }

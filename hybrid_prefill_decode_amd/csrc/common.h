@@ -177,15 +177,18 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
 size_t gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epi);
 struct TileChoice {
   int bm, bn;
-  bool sk;         // stream-K (plain and residual epilogues with a workspace only)
-  int splits = 0;  // >= 2: split-K into that many K ranges (SwiGLU and RoPE epilogues)
+  bool sk;            // stream-K (plain and residual epilogues with a workspace only)
+  int splits = 0;     // >= 2: split-K into that many K ranges (SwiGLU and RoPE epilogues)
+  bool tail = false;  // with splits: one tile per workgroup, but the tiles past the last full
+                      // round over the compute units are split into `splits` K ranges
 };
 // Schedules a launch may use besides one tile per workgroup (each needs the workspace).
-constexpr int kSchedStreamK = 1, kSchedSplitK = 2;
+constexpr int kSchedStreamK = 1, kSchedSplitK = 2, kSchedTail = 4;
 // Tile shape and schedule of a GEMM launch (gemm.hip); col_align: N-tile widths a multiple of it.
 TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align);
 bool gemm_tile_supported(int bm, int bn);
 bool gemm_split_fits(int m, int n, int bm, int bn, int splits);  // pieces fit the workspace
+bool gemm_tail_fits(int m, int n, int bm, int bn, int splits);  // tail-split pieces fit it
 // few-token path (gemm_skinny.hip): split-K weight streaming with fp32 partials in the workspace
 constexpr int kSkinnyMaxM = 64;
 size_t skinny_workspace_bytes(int m, int n, int k);

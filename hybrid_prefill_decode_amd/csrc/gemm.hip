@@ -15,6 +15,10 @@
 //   stream-K: t = 1.39 * ceil(tiles * k_steps / 256) * c(BM, BN) + 0.05 us per MB of fp32 pieces
 //     (one piece per run end plus one per split tile, written and read back by the fix-up; a run
 //     that changes tiles loses cache locality, hence the 1.39);
+//   tail split (any epilogue): the full rounds as above, then the r tiles left over (r at most
+//     half the compute units) cut into S = min(256 / r, 4) K ranges: t = k_steps * c(BM, BN) *
+//     full rounds + 1.36 * ceil(k_steps / S) * c(BM, BN) * (0.84 + 0.16 r S / 256) + 0.05 us per MB
+//     of pieces + 11 us (split-K's constants: the fix-up pass and the pieces' round trip);
 //   split-K into S ranges (SwiGLU, RoPE; 128-wide tiles): t = 1.36 * ceil(k_steps / S) * c(BM, BN)
 //     * (rounds of tiles * S) + 0.05 us per MB of pieces (S per tile) + 11 us (the fix-up pass
 //     and the pieces' round trip). Fitted to every 128-wide tile x S in {2, 3, 4, 6, 8} on the
@@ -70,6 +74,26 @@ float split_cost(const TileCost& t, int m, int n, int nk, int s) {
          kPieceUsPerMB * mb + kSplitFixed;
 }
 
+// one tile per workgroup with the last partial round split along K; S = 0 if not applicable
+int tail_splits(const TileCost& t, int m, int n, int nk) {
+  const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
+  const long rem = tiles % kCUs;
+  if (tiles < kCUs || rem == 0 || 2 * rem > kCUs) return 0;
+  const int s = (int)std::min<long>(4, kCUs / rem);
+  if (nk < s * kMinSplitSteps || !tail_fits((int)rem, t.bm, t.bn, s)) return 0;
+  return s;
+}
+
+float tail_cost(const TileCost& t, int m, int n, int nk, int s) {
+  const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
+  const long rem = tiles % kCUs, full = tiles / kCUs;
+  const float mb = (float)s * rem * t.bm * t.bn * 8 / 1e6f;
+  return nk * t.kstep_us * (float)full +
+         (float)((nk + s - 1) / s) * t.kstep_us * kSplitStep *
+             (kPartialRound + (1.f - kPartialRound) * (float)(rem * s) / kCUs) +
+         kPieceUsPerMB * mb + kSplitFixed;
+}
+
 float streamk_cost(const TileCost& t, int m, int n, int nk) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
   const long per = (tiles * nk + kCUs - 1) / kCUs;
@@ -94,6 +118,11 @@ TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align) {
     if (n % t.bn || t.bn % col_align) continue;
     const float c1 = one_tile_cost(t, m, n, nk);
     if (c1 < best_t) best_t = c1, best = TileChoice{t.bm, t.bn, false};
+    if (schedules & kSchedTail)
+      if (const int s = tail_splits(t, m, n, nk)) {
+        const float c4 = tail_cost(t, m, n, nk, s);
+        if (c4 < best_t) best_t = c4, best = TileChoice{t.bm, t.bn, false, s, true};
+      }
     if ((schedules & kSchedStreamK) && t.streamk && nk >= 4) {
       const float c2 = streamk_cost(t, m, n, nk);
       if (c2 < best_t) best_t = c2, best = TileChoice{t.bm, t.bn, true};
@@ -114,6 +143,11 @@ bool use_skinny(int m, int n, int k, size_t ws_bytes) {
 
 bool gemm_split_fits(int m, int n, int bm, int bn, int splits) {
   return split_fits(m, n, bm, bn, splits);
+}
+
+bool gemm_tail_fits(int m, int n, int bm, int bn, int splits) {
+  const int tiles = ((m + bm - 1) / bm) * (n / bn);
+  return tail_fits(tiles - tail_full_tiles(tiles), bm, bn, splits);
 }
 
 bool gemm_tile_supported(int bm, int bn) {
@@ -145,17 +179,18 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
     return launch_gemm_skinny(a, w, c, m, n, k, epi, static_cast<float*>(ws), st);
   switch (epi.kind) {
     case HL_EPI_NONE:
-      return launch_gemm_plain(choose_tiles(m, n, k, part ? kSchedStreamK : 0, 1), a, w, c, m, n,
-                               k, epi, part, st);
+      return launch_gemm_plain(choose_tiles(m, n, k, part ? kSchedStreamK | kSchedTail : 0, 1), a,
+                               w, c, m, n, k, epi, part, st);
     case HL_EPI_RESIDUAL:
-      return launch_gemm_residual(choose_tiles(m, n, k, part ? kSchedStreamK : 0, 1), a, w, c, m,
-                                  n, k, epi, part, st);
+      return launch_gemm_residual(choose_tiles(m, n, k, part ? kSchedStreamK | kSchedTail : 0, 1),
+                                  a, w, c, m, n, k, epi, part, st);
     case HL_EPI_SWIGLU:
-      return launch_gemm_swiglu(choose_tiles(m, n, k, part ? kSchedSplitK : 0, 1), a, w, c, m, n,
-                                k, epi, part, st);
+      return launch_gemm_swiglu(choose_tiles(m, n, k, part ? kSchedSplitK | kSchedTail : 0, 1), a,
+                                w, c, m, n, k, epi, part, st);
     default:
-      return launch_gemm_rope(choose_tiles(m, n, k, part ? kSchedSplitK : 0, epi.head_dim), a, w,
-                              c, m, n, k, epi, part, st);
+      return launch_gemm_rope(
+          choose_tiles(m, n, k, part ? kSchedSplitK | kSchedTail : 0, epi.head_dim), a, w, c, m,
+          n, k, epi, part, st);
   }
 }
 

@@ -721,16 +721,17 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
 template <int EPI, int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
     const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N, int K,
-    int splits, int mtiles, int tiles, float* __restrict__ part) {
+    int splits, int mtiles, int tiles, float* __restrict__ part, int tile0) {
   using CF = Cfg<BM, BN>;
   constexpr int MT = CF::MT, NT = CF::NT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // `tiles` tiles from tile tile0 of the GEMM on; pieces are numbered from 0
   const int u = xcd_tile(blockIdx.x, gridDim.x);
-  const int tile = u % tiles, s = u / tiles;
+  const int tile = u % tiles, s = u / tiles, gt = tile0 + tile;
   const int nk = K / BK;
   const int kb = (int)((long)s * nk / splits), ke = (int)((long)(s + 1) * nk / splits);
   f32x4 acc[MT][NT];
-  mainloop<EPI, BM, BN, 2, true>(A, W, M, N, K, tile % mtiles, tile / mtiles, kb, ke, smem, acc);
+  mainloop<EPI, BM, BN, 2, true>(A, W, M, N, K, gt % mtiles, gt / mtiles, kb, ke, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* dst = part + ((size_t)s * tiles + tile) * BM * BN + lane * 4;
 #pragma unroll
@@ -745,10 +746,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_split_kernel(
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_split_fixup(hl_bf16* __restrict__ C, int M, int N,
                                                         GemmEpi ep, int splits, int mtiles,
-                                                        int tiles, const float* __restrict__ part) {
+                                                        int tiles, const float* __restrict__ part,
+                                                        int tile0) {
   using CF = Cfg<BM, BN>;
   constexpr int MT = CF::MT, NT = CF::NT;
-  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  // pieces of `tiles` split tiles, the first of which is tile tile0 of the GEMM
+  const int tile = blockIdx.x, mt = (tile0 + tile) % mtiles, nt = (tile0 + tile) / mtiles;
   const int g = blockIdx.y * 256 + threadIdx.x;
   const int q = g & 15, blk = g >> 4;  // lane quad, block (w MT + i) NT + t
   if (blk >= 4 * MT * NT) return;
@@ -788,10 +791,11 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_split_swiglu_fixup(hl_bf16* __restrict__ C, int M,
                                                                int N, GemmEpi ep, int splits,
                                                                int mtiles, int tiles,
-                                                               const float* __restrict__ part) {
+                                                               const float* __restrict__ part,
+                                                               int tile0) {
   using CF = Cfg<BM, BN>;
   constexpr int MT = CF::MT, NT = CF::NT, NH = NT / 2;
-  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  const int tile = blockIdx.x, mt = (tile0 + tile) % mtiles, nt = (tile0 + tile) / mtiles;
   const int g = blockIdx.y * 256 + threadIdx.x;
   const int q = g & 15, hb = g >> 4;  // lane quad, gate block (w, i, t < NH)
   if (hb >= 4 * MT * NH) return;
@@ -831,12 +835,13 @@ __global__ __launch_bounds__(256) void gemm_split_swiglu_fixup(hl_bf16* __restri
 template <int BM, int BN, int HD>
 __global__ __launch_bounds__(256) void gemm_split_rope_fixup(int M, GemmEpi ep, int splits,
                                                              int mtiles, int tiles,
-                                                             const float* __restrict__ part) {
+                                                             const float* __restrict__ part,
+                                                             int tile0) {
   using CF = Cfg<BM, BN>;
   constexpr int MT = CF::MT, NT = CF::NT, SROW = kStageRow<BN>, ROWS = 32;
   constexpr int CB = BN / 16;  // 16-column blocks of the tile
   __shared__ float st[ROWS * SROW];
-  const int tile = blockIdx.x, mt = tile % mtiles, nt = tile / mtiles;
+  const int tile = blockIdx.x, mt = (tile0 + tile) % mtiles, nt = (tile0 + tile) / mtiles;
   const int r0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x;
   for (int e = tid; e < (ROWS / 16) * CB * 16; e += 256) {
@@ -876,10 +881,39 @@ inline bool split_fits(int m, int n, int bm, int bn, int splits) {
   const size_t tiles = (size_t)((m + bm - 1) / bm) * (n / bn);
   return (size_t)splits * tiles * bm * bn * 4 <= kStreamKWorkspace;
 }
+// Tail split: the tiles that run whole (the full rounds over the compute units), and whether
+// the pieces of the rest fit the workspace.
+inline int tail_full_tiles(int tiles) { return (tiles / kStreamKGrid) * kStreamKGrid; }
+inline bool tail_fits(int tail, int bm, int bn, int splits) {
+  return (size_t)splits * tail * bm * bn * 4 <= kStreamKWorkspace;
+}
 
+// The fix-up of `tiles` split tiles (the first is tile tile0 of the GEMM), `splits` pieces each.
+template <int EPI, int BM, int BN, int HD>
+hipError_t launch_split_fixup(hl_bf16* c, int m, int n, const GemmEpi& epi, const float* part,
+                              int splits, int mtiles, int tiles, int tile0, hipStream_t st) {
+  using CF = Cfg<BM, BN>;
+  if constexpr (EPI == HL_EPI_SWIGLU) {
+    constexpr int quads = 4 * CF::MT * (CF::NT / 2) * 16;
+    hipLaunchKernelGGL((gemm_split_swiglu_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256),
+                       dim3(256), 0, st, c, m, n, epi, splits, mtiles, tiles, part, tile0);
+  } else if constexpr (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL) {
+    constexpr int quads = 4 * CF::MT * CF::NT * 16;
+    hipLaunchKernelGGL((gemm_split_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256), dim3(256), 0,
+                       st, c, m, n, epi, splits, mtiles, tiles, part, tile0);
+  } else {
+    hipLaunchKernelGGL((gemm_split_rope_fixup<BM, BN, HD>), dim3(tiles, BM / 32), dim3(256), 0,
+                       st, m, epi, splits, mtiles, tiles, part, tile0);
+  }
+  return hipGetLastError();
+}
+
+// Split-K over all tiles, or (tail) over the tiles past the last full round only: those the
+// one-tile launch before it left out.
 template <int EPI, int BM, int BN, int HD>
 hipError_t launch_split(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
-                        const GemmEpi& epi, float* part, int splits, hipStream_t st) {
+                        const GemmEpi& epi, float* part, int splits, hipStream_t st,
+                        bool tail = false) {
   using CF = Cfg<BM, BN>;
 
   auto kern = gemm_split_kernel<EPI, BM, BN>;
@@ -891,28 +925,19 @@ hipError_t launch_split(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
     attr = true;
   }
   const int mtiles = (m + BM - 1) / BM, tiles = mtiles * (n / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles * splits), dim3(kThreads), CF::MAIN_LDS, st, a, w, m, n, k,
-                     splits, mtiles, tiles, part);
+  const int t0 = tail ? tail_full_tiles(tiles) : 0;
+  hipLaunchKernelGGL(kern, dim3((tiles - t0) * splits), dim3(kThreads), CF::MAIN_LDS, st, a, w, m,
+                     n, k, splits, mtiles, tiles - t0, part, t0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (EPI == HL_EPI_SWIGLU) {
-    constexpr int quads = 4 * CF::MT * (CF::NT / 2) * 16;
-    hipLaunchKernelGGL((gemm_split_swiglu_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256),
-                       dim3(256), 0, st, c, m, n, epi, splits, mtiles, tiles, part);
-  } else if constexpr (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL) {
-    constexpr int quads = 4 * CF::MT * CF::NT * 16;
-    hipLaunchKernelGGL((gemm_split_fixup<BM, BN>), dim3(tiles, (quads + 255) / 256), dim3(256), 0,
-                       st, c, m, n, epi, splits, mtiles, tiles, part);
-  } else {
-    hipLaunchKernelGGL((gemm_split_rope_fixup<BM, BN, HD>), dim3(tiles, BM / 32), dim3(256), 0,
-                       st, m, epi, splits, mtiles, tiles, part);
-  }
-  return hipGetLastError();
+  return launch_split_fixup<EPI, BM, BN, HD>(c, m, n, epi, part, splits, mtiles, tiles - t0, t0,
+                                             st);
 }
 
 template <int EPI, int BM, int BN, int HD = 0>
 hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, int n, int k,
-                        const GemmEpi& epi, float* part, bool streamk, hipStream_t st) {
+                        const GemmEpi& epi, float* part, bool streamk, hipStream_t st,
+                        int tail_splits = 0) {
   using CF = Cfg<BM, BN>;
   constexpr bool kCanSplit = (EPI == HL_EPI_NONE || EPI == HL_EPI_RESIDUAL);
   auto kern = gemm_bf16_nt_kernel<EPI, BM, BN, HD, false>;
@@ -937,6 +962,15 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
   const int tiles = sc.mtiles * sc.ntiles;
   int grid = tiles;
   streamk = streamk && kCanSplit && part;
+  // Tail split: the full rounds of tiles here, then the tiles left over (whose round would leave
+  // most compute units idle) as split-K pieces in a launch of their own, which starts as the
+  // equal-length tiles of the last full round drain together.
+  bool tail = false;
+  if (!streamk && part && tail_splits >= 2) {
+    const int full = tail_full_tiles(tiles);
+    tail = full < tiles && tail_fits(tiles - full, BM, BN, tail_splits) && tail_splits <= sc.nk;
+    if (tail) grid = full;
+  }
   if (streamk) {
     const int total = tiles * sc.nk;
     sc.ipw = (total + kStreamKGrid - 1) / kStreamKGrid;
@@ -951,10 +985,12 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
   }
   if (streamk)
     hipLaunchKernelGGL(kern_sk, dim3(grid), dim3(kThreads), lds, st, a, w, c, m, n, k, epi, sc);
-  else
+  else if (grid > 0)
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a, w, c, m, n, k, epi, sc);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !streamk) return e;
+  if (e != hipSuccess) return e;
+  if (tail) return launch_split<EPI, BM, BN, HD>(a, w, c, m, n, k, epi, part, tail_splits, st, true);
+  if (!streamk) return e;
   hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN>), dim3(tiles, BM * BN / 4096), dim3(256), 0, st,
                      c, m, n, epi, sc);
   return hipGetLastError();
@@ -965,8 +1001,9 @@ template <int EPI, int HD = 0>
 hipError_t launch_choice(const hl::TileChoice& tc, const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                          int m, int n, int k, const GemmEpi& epi, float* part, hipStream_t st) {
   const bool sk = tc.sk && part != nullptr;
+  const int ts = tc.tail ? tc.splits : 0;
   {
-    if (tc.splits >= 2) {
+    if (tc.splits >= 2 && !tc.tail) {
       if (!part || !split_fits(m, n, tc.bm, tc.bn, tc.splits) || tc.splits > k / BK)
         return hipErrorInvalidValue;
       switch (tc.bm * 1000 + tc.bn) {
@@ -984,15 +1021,15 @@ hipError_t launch_choice(const hl::TileChoice& tc, const hl_bf16* a, const hl_bf
     }
   }
   switch (tc.bm * 1000 + tc.bn) {
-    case 256256: return launch_tiles<EPI, 256, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 224256: return launch_tiles<EPI, 224, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 192256: return launch_tiles<EPI, 192, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 160256: return launch_tiles<EPI, 160, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 128256: return launch_tiles<EPI, 128, 256, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 256128: return launch_tiles<EPI, 256, 128, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 224128: return launch_tiles<EPI, 224, 128, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 160128: return launch_tiles<EPI, 160, 128, HD>(a, w, c, m, n, k, epi, part, sk, st);
-    case 128128: return launch_tiles<EPI, 128, 128, HD>(a, w, c, m, n, k, epi, part, sk, st);
+    case 256256: return launch_tiles<EPI, 256, 256, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 224256: return launch_tiles<EPI, 224, 256, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 192256: return launch_tiles<EPI, 192, 256, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 160256: return launch_tiles<EPI, 160, 256, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 128256: return launch_tiles<EPI, 128, 256, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 256128: return launch_tiles<EPI, 256, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 224128: return launch_tiles<EPI, 224, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 160128: return launch_tiles<EPI, 160, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 128128: return launch_tiles<EPI, 128, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
     default: return hipErrorInvalidValue;
   }
 }

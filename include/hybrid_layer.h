@@ -386,8 +386,10 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
  * tuning and tests). tile_m x tile_n must be one of 256x256, 224x256, 192x256, 160x256, 128x256,
  * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0. stream_k: 0 one tile per workgroup;
  * 1 a stream-K schedule (HL_EPI_NONE / HL_EPI_RESIDUAL); s >= 2 split-K into s equal K ranges
- * (any epilogue; s <= k / 64, and the s fp32 pieces per tile must fit the workspace). Any
- * schedule but 0 needs `workspace` of hl_gemm_workspace_bytes(). Results agree with
+ * (any epilogue; s <= k / 64, and the s fp32 pieces per tile must fit the workspace); -s with
+ * 2 <= s <= 8 one tile per workgroup for the full rounds of tiles over the compute units and the
+ * tiles left over split into s K ranges (any epilogue; same limits; with no tile left over it is
+ * schedule 0). Any schedule but 0 needs `workspace` of hl_gemm_workspace_bytes(). Results agree with
  * hl_gemm_bf16_nt to fp32 summation order. Errors as hl_gemm_bf16_nt, and HL_ERR_ARG for an
  * unsupported tile or schedule. */
 int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
@@ -398,8 +400,9 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
 /* The tile shape (*tile_m x *tile_n outputs per workgroup) and schedule (*stream_k: 1 for a
  * stream-K run with a fix-up pass, 0 for one tile per workgroup, 2 for the weight-streaming path of
  * up to 64 token rows, whose workgroups each cover 64 columns of all rows over a K range, 3 for
- * split-K into *splits equal K ranges summed by a fix-up pass that applies the epilogue; *splits
- * is 0 otherwise) that hl_gemm_bf16_nt uses for
+ * split-K into *splits equal K ranges summed by a fix-up pass that applies the epilogue, 4 for one
+ * tile per workgroup with the tiles past the last full round over the compute units split into
+ * *splits K ranges; *splits is 0 otherwise) that hl_gemm_bf16_nt uses for
  * these arguments (with_workspace != 0: a stream-K workspace is passed). qkv_head_dim 64 or 128
  * asks instead for the QKV projection of the layer step (RoPE + KV-append epilogue: whole heads
  * per tile); 0 otherwise. Host-only: no device work, no GPU needed. The choice minimises a cost

@@ -203,6 +203,9 @@ def test_gemm_tiled_argument_checks():
     assert g(p, p, p, None, None, 8, 256, 64, 2, 128, 256, 2, p, big, None) == B.HL_ERR_ARG  # 2 ranges > 1 k-step
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, 2, None, 0, None) == B.HL_ERR_ARG  # no workspace
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -1, p, big, None) == B.HL_ERR_ARG  # negative
+    assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -9, p, big, None) == B.HL_ERR_ARG  # tail > 8
+    assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -5, p, big, None) == B.HL_ERR_ARG  # 5 > 4 k-steps
+    assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -2, None, 0, None) == B.HL_ERR_ARG  # no workspace
 
 
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
@@ -222,13 +225,18 @@ def test_gemm_tile_choice_is_valid(epi):
             assert ws and 0 < m <= 64 and bn == 64 and bm == 16 * ((m + 15) // 16), (m, n, k)
             continue
         assert (bm, bn) in tiles and n % bn == 0, (m, n, k, bm, bn)
-        assert (sp >= 2) == (sk == 3), (sk, sp)
+        assert (sp >= 2) == (sk in (3, 4)), (sk, sp)
         if sk == 1:
             assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)
         if sk == 3:  # split-K: SwiGLU or the QKV projection, at least 4 k-steps per range
             assert ws and (hd or epi == B.HL_EPI_SWIGLU) and k // 64 >= 4 * sp, (m, n, k, sp)
             tiles_n = -(-m // bm) * (n // bn)
             assert sp * tiles_n * bm * bn * 4 <= 256 * 2 * 256 * 256 * 4, (m, n, bm, bn, sp)
+        if sk == 4:  # tail split: full rounds of whole tiles, at most half a round left over
+            tiles_n = -(-m // bm) * (n // bn)
+            rem = tiles_n % 256
+            assert ws and tiles_n > 256 and 0 < 2 * rem <= 256 and k // 64 >= 4 * sp, (m, n, k, sp)
+            assert sp * rem * bm * bn * 4 <= 256 * 2 * 256 * 256 * 4, (m, n, bm, bn, sp)
         if hd:
             assert bn % hd == 0
     with pytest.raises(RuntimeError):

@@ -127,6 +127,41 @@ def test_gemm_every_tile_shape(tile, epi, stream_k):
         assert_close(f64(c), ref, f"gemm {bm}x{bn} sk={stream_k}")
 
 
+@pytest.mark.parametrize("tile", B.GEMM_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("epi,splits", [(B.HL_EPI_NONE, 2), (B.HL_EPI_RESIDUAL, 3),
+                                        (B.HL_EPI_SWIGLU, 2), (B.HL_EPI_SWIGLU, 3)],
+                         ids=["plain-2", "residual-3", "swiglu-2", "swiglu-3"])
+def test_gemm_tail_split(tile, epi, splits):
+    """Tail split: one full round of 256 whole tiles, then the 8..16 tiles left over cut into 2 or
+    3 K ranges (the 5 k-steps of K = 320 as 2 + 3 or 1 + 2 + 2) in the same launch, finished by the
+    split-K fix-up from the right tile on. 300 rows leave a ragged last M tile; a row scale is
+    applied."""
+    bm, bn = tile
+    m, k = 300, 320
+    mtiles = -(-m // bm)
+    n = bn * -(-264 // mtiles)
+    tiles = mtiles * (n // bn)
+    assert 256 < tiles <= 256 + 16
+    say(f"gemm tail split {bm}x{bn} s={splits} epi={epi} m={m} n={n} k={k} tiles={tiles}")
+    a = _randn((m, k), 81 + bm)
+    w = _randn((n, k), 82 + bn, 0.05)
+    out_n = n // 2 if epi == B.HL_EPI_SWIGLU else n
+    res = _randn((m, out_n), 83) if epi == B.HL_EPI_RESIDUAL else None
+    rs = 0.5 + torch.rand(m, generator=torch.Generator(device=DEV).manual_seed(9), device=DEV)
+    ws = torch.empty(B.gemm_workspace_bytes(m, n, k, epi), dtype=torch.uint8, device=DEV)
+    c = torch.full((m, out_n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.gemm_bf16_nt_tiled(a, w, c, bm, bn, -splits, res, epi, workspace=ws, row_scale=rs)
+    torch.cuda.synchronize()
+    A, W = f64(a) * f64(rs)[:, None], f64(w)
+    if epi == B.HL_EPI_SWIGLU:
+        ref = OL.swiglu(A, W, n // 2)
+    else:
+        ref = OL.linear(A, W)
+        if epi == B.HL_EPI_RESIDUAL:
+            ref = ref + f64(res)
+    assert_close(f64(c), ref, f"gemm tail split {bm}x{bn} s={splits}")
+
+
 @pytest.mark.parametrize("tile", [(128, 128), (160, 256), (256, 256)], ids=lambda t: f"{t[0]}x{t[1]}")
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
 def test_gemm_tall_one_tile(tile, epi):
@@ -301,6 +336,9 @@ _QKV_SPLIT = {"split160x128_d128": ((4096, 8, 2, 128), 150),
 for _name, (_dims, _rows) in _QKV_SPLIT.items():
     QKV_CASES[_name] = (workloads.LayerShape(*_dims, 512),
                         [(0, _rows - 69), (777, 40), (5000, 1), (33, 1), (15, 26), (4096, 1)])
+# 10884 rows at hidden 4096: 49 x 6 = 294 tiles of 224 x 256, one full round of 256 whole tiles and
+# 38 tiles cut into 4 K ranges, whose fix-up rotates and appends from tile 256 on
+QKV_CASES["tail224x256_d128"] = (workloads.LayerShape(4096, 8, 2, 128, 512), _qkv_rows_case(10884))
 
 
 @pytest.mark.parametrize("case", sorted(QKV_CASES))
@@ -309,12 +347,13 @@ def test_qkv_rope_append_vs_oracle(case):
     spec = workloads.make_spec(1) if seqs is None else workloads.custom_spec(shape, seqs, 3)
     say(f"qkv+rope+append {case}: {spec.seqs}")
     s = spec.shape
-    if case.startswith("tile") or case.startswith("split"):
-        want = tuple(int(v) for v in case[5 if case[0] == "s" else 4:].split("_")[0].split("x"))
+    if case.startswith(("tile", "split", "tail")):
+        want = tuple(int(v) for v in case[4 + case.startswith("split"):].split("_")[0].split("x"))
         qkv_cols = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
         got = B.gemm_tile_choice(spec.num_tokens, qkv_cols, s.hidden, B.HL_EPI_NONE, True,
                                  s.head_dim)
         assert got[:2] == want and (got[2] == 3) == case.startswith("split"), (case, got)
+        assert (got[2] == 4) == case.startswith("tail"), (case, got)
     table, pool = workloads.block_table(spec)
     cfg = B.layer_cfg(s)
     b = B.Batch(spec.q_start, spec.num_cached, table, DEV)
