@@ -654,7 +654,9 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
   }
   int sched = 0;
   if (with_workspace)
-    sched = ((qkv_head_dim || epilogue == HL_EPI_SWIGLU) ? hl::kSchedSplitK : hl::kSchedStreamK) |
+    sched = ((qkv_head_dim || epilogue == HL_EPI_SWIGLU)
+                 ? hl::kSchedSplitK
+                 : hl::kSchedStreamK | hl::kSchedSplitK | hl::kSchedWideSplit) |
             hl::kSchedTail;
   const hl::TileChoice tc = hl::choose_tiles(m, n, k, sched, qkv_head_dim ? qkv_head_dim : 1);
   *tile_m = tc.bm;

@@ -184,6 +184,9 @@ struct TileChoice {
 };
 // Schedules a launch may use besides one tile per workgroup (each needs the workspace).
 constexpr int kSchedStreamK = 1, kSchedSplitK = 2, kSchedTail = 4;
+// split-K on the 256-wide tiles too, priced at the k-step cost of a one-tile run (plain and
+// residual epilogues: measured faster there, slower for SwiGLU and RoPE)
+constexpr int kSchedWideSplit = 8;
 // Tile shape and schedule of a GEMM launch (gemm.hip); col_align: N-tile widths a multiple of it.
 TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align);
 bool gemm_tile_supported(int bm, int bn);

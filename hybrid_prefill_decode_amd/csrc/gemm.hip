@@ -19,17 +19,19 @@
 //     half the compute units) cut into S = min(256 / r, 4) K ranges: t = k_steps * c(BM, BN) *
 //     full rounds + 1.36 * ceil(k_steps / S) * c(BM, BN) * (0.84 + 0.16 r S / 256) + 0.05 us per MB
 //     of pieces + 11 us (split-K's constants: the fix-up pass and the pieces' round trip);
-//   split-K into S ranges (SwiGLU, RoPE; 128-wide tiles): t = 1.36 * ceil(k_steps / S) * c(BM, BN)
-//     * (rounds of tiles * S) + 0.05 us per MB of pieces (S per tile) + 11 us (the fix-up pass
-//     and the pieces' round trip). Fitted to every 128-wide tile x S in {2, 3, 4, 6, 8} on the
+//   split-K into S ranges: t = f * ceil(k_steps / S) * c(BM, BN) * (rounds of tiles * S) + 0.05 us
+//     per MB of pieces (S per tile) + 11 us (the fix-up pass and the pieces' round trip), with
+//     f = 1.36 for the 128-wide tiles, fitted to every 128-wide tile x S in {2, 3, 4, 6, 8} on the
 //     SwiGLU and QKV projections of the 8B and 70B shapes at 65..1040 rows (relative rms error
-//     12 %; the model's picks take 0.8 % longer than the measured best); wider split tiles were
-//     never the best and fit badly, so they are not candidates.
+//     12 %). Plain and residual GEMMs may also split the 256-wide tiles, at f = 1.0 (their long
+//     split runs go at the one-tile k-step rate: 0.95-1.06 measured on the 70B and 14B O and down
+//     projections); against the previous picks that made the 17 changed layer GEMMs of a sweep
+//     (8B / 14B / 70B, 128..4160 rows) 14 % faster in total, none more than 1 % slower. For SwiGLU
+//     and the QKV projection the wide splits were slower (up to 22 %), so there only the
+//     128-wide tiles split.
 // Over a sweep of every tile x schedule on the QKV, O, gate/up and down projections of the 8B, 14B
 // and 70B shapes at 128..4160 rows (2954 timings), the model's picks take 1.2 % longer in total
-// than the best measured pick of each GEMM. Plain / residual GEMMs can also run split-K (through
-// hl_gemm_bf16_nt_tiled), but offering it to the model did not improve its picks, so they use
-// stream-K.
+// than the best measured pick of each GEMM.
 //
 // c(BM, BN) is the time of one 64-deep k-step of a BM x BN tile with every compute unit busy,
 // fitted, together with the other constants, to times of all shapes below on the layer GEMMs of
@@ -54,6 +56,8 @@ constexpr TileCost kTiles[] = {
 constexpr int kCUs = kStreamKGrid;
 constexpr float kPartialRound = 0.84f, kStreamKStep = 1.39f, kPieceUsPerMB = 0.05f;
 constexpr float kSplitStep = 1.36f, kSplitFixed = 11.0f;
+// the k-step factor of split runs of the 256-wide tiles (long runs: measured 0.95-1.06)
+constexpr float kSplitStepWide = 1.0f;
 constexpr int kSplitCandidates[] = {2, 3, 4, 6, 8, 12, 16};
 constexpr int kMinSplitSteps = 4;  // k-steps of 64 per split at least
 
@@ -67,10 +71,14 @@ float one_tile_cost(const TileCost& t, int m, int n, int nk) {
   return nk * t.kstep_us * rounds(tiles);
 }
 
-float split_cost(const TileCost& t, int m, int n, int nk, int s) {
+float split_step(const TileCost& t, bool wide) {
+  return (t.bn == 128 || !wide) ? kSplitStep : kSplitStepWide;
+}
+
+float split_cost(const TileCost& t, int m, int n, int nk, int s, bool wide) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
   const float mb = (float)s * tiles * t.bm * t.bn * 8 / 1e6f;
-  return (float)((nk + s - 1) / s) * t.kstep_us * rounds(tiles * s) * kSplitStep +
+  return (float)((nk + s - 1) / s) * t.kstep_us * rounds(tiles * s) * split_step(t, wide) +
          kPieceUsPerMB * mb + kSplitFixed;
 }
 
@@ -84,12 +92,12 @@ int tail_splits(const TileCost& t, int m, int n, int nk) {
   return s;
 }
 
-float tail_cost(const TileCost& t, int m, int n, int nk, int s) {
+float tail_cost(const TileCost& t, int m, int n, int nk, int s, bool wide) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
   const long rem = tiles % kCUs, full = tiles / kCUs;
   const float mb = (float)s * rem * t.bm * t.bn * 8 / 1e6f;
   return nk * t.kstep_us * (float)full +
-         (float)((nk + s - 1) / s) * t.kstep_us * kSplitStep *
+         (float)((nk + s - 1) / s) * t.kstep_us * split_step(t, wide) *
              (kPartialRound + (1.f - kPartialRound) * (float)(rem * s) / kCUs) +
          kPieceUsPerMB * mb + kSplitFixed;
 }
@@ -114,23 +122,24 @@ TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align) {
   const int nk = k / BK;
   TileChoice best{128, 128, false};
   float best_t = 3.4e38f;
+  const bool wide = (schedules & kSchedWideSplit) != 0;
   for (const TileCost& t : kTiles) {
     if (n % t.bn || t.bn % col_align) continue;
     const float c1 = one_tile_cost(t, m, n, nk);
     if (c1 < best_t) best_t = c1, best = TileChoice{t.bm, t.bn, false};
     if (schedules & kSchedTail)
       if (const int s = tail_splits(t, m, n, nk)) {
-        const float c4 = tail_cost(t, m, n, nk, s);
+        const float c4 = tail_cost(t, m, n, nk, s, wide);
         if (c4 < best_t) best_t = c4, best = TileChoice{t.bm, t.bn, false, s, true};
       }
     if ((schedules & kSchedStreamK) && t.streamk && nk >= 4) {
       const float c2 = streamk_cost(t, m, n, nk);
       if (c2 < best_t) best_t = c2, best = TileChoice{t.bm, t.bn, true};
     }
-    if ((schedules & kSchedSplitK) && t.bn == 128)
+    if ((schedules & kSchedSplitK) && (t.bn == 128 || wide))
       for (int s : kSplitCandidates) {
         if (nk < s * kMinSplitSteps || !split_fits(m, n, t.bm, t.bn, s)) continue;
-        const float c3 = split_cost(t, m, n, nk, s);
+        const float c3 = split_cost(t, m, n, nk, s, wide);
         if (c3 < best_t) best_t = c3, best = TileChoice{t.bm, t.bn, false, s};
       }
   }
@@ -179,11 +188,15 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
     return launch_gemm_skinny(a, w, c, m, n, k, epi, static_cast<float*>(ws), st);
   switch (epi.kind) {
     case HL_EPI_NONE:
-      return launch_gemm_plain(choose_tiles(m, n, k, part ? kSchedStreamK | kSchedTail : 0, 1), a,
-                               w, c, m, n, k, epi, part, st);
+      return launch_gemm_plain(
+          choose_tiles(m, n, k, part ? kSchedStreamK | kSchedSplitK | kSchedWideSplit | kSchedTail : 0,
+                       1),
+          a, w, c, m, n, k, epi, part, st);
     case HL_EPI_RESIDUAL:
-      return launch_gemm_residual(choose_tiles(m, n, k, part ? kSchedStreamK | kSchedTail : 0, 1),
-                                  a, w, c, m, n, k, epi, part, st);
+      return launch_gemm_residual(
+          choose_tiles(m, n, k, part ? kSchedStreamK | kSchedSplitK | kSchedWideSplit | kSchedTail : 0,
+                       1),
+          a, w, c, m, n, k, epi, part, st);
     case HL_EPI_SWIGLU:
       return launch_gemm_swiglu(choose_tiles(m, n, k, part ? kSchedSplitK | kSchedTail : 0, 1), a,
                                 w, c, m, n, k, epi, part, st);

@@ -228,8 +228,10 @@ def test_gemm_tile_choice_is_valid(epi):
         assert (sp >= 2) == (sk in (3, 4)), (sk, sp)
         if sk == 1:
             assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)
-        if sk == 3:  # split-K: SwiGLU or the QKV projection, at least 4 k-steps per range
-            assert ws and (hd or epi == B.HL_EPI_SWIGLU) and k // 64 >= 4 * sp, (m, n, k, sp)
+        if sk == 3:  # split-K with a workspace, at least 4 k-steps per range; SwiGLU and the
+            # QKV projection split the 128-wide tiles only
+            assert ws and k // 64 >= 4 * sp, (m, n, k, sp)
+            assert bn == 128 or not (hd or epi == B.HL_EPI_SWIGLU), (m, n, k, bm, bn)
             tiles_n = -(-m // bm) * (n // bn)
             assert sp * tiles_n * bm * bn * 4 <= 256 * 2 * 256 * 256 * 4, (m, n, bm, bn, sp)
         if sk == 4:  # tail split: full rounds of whole tiles, at most half a round left over
