@@ -54,12 +54,23 @@ constexpr TileCost kTiles[] = {
     {224, 128, 0.853f, false}, {160, 128, 0.631f, false}, {128, 128, 0.547f, false},
 };
 constexpr int kCUs = kStreamKGrid;
-constexpr float kPartialRound = 0.84f, kStreamKStep = 1.39f, kPieceUsPerMB = 0.05f;
-constexpr float kSplitStep = 1.36f, kSplitFixed = 11.0f;
-// the k-step factor of split runs of the 256-wide tiles (long runs: measured 0.95-1.06)
-constexpr float kSplitStepWide = 1.0f;
+constexpr float kPartialRound = 0.84f;
+// Split and stream-K prices. SwiGLU and the QKV projection (whose fix-ups also rotate and route
+// rows) keep the constants fitted on the 128-wide split tiles; plain and residual GEMMs use a set
+// fitted to every tile x schedule (one tile, stream-K, split-K into 2..8, tail split into 2..4)
+// of the 8B / 14B / 70B O and down projections at 128..4160 rows: their picks take 0.66 % longer
+// in total than the best measured schedule of each of those 51 GEMMs (mean 1.1 %, worst 11 %),
+// against ~2 % for the constants fitted before, which under-priced stream-K's short runs at a few
+// hundred rows and over-priced the long split runs of the 256-wide tiles.
+struct SchedCost {
+  float split_step, split_step_wide, split_fixed, piece_us_per_mb, streamk_step, streamk_fixed;
+};
+constexpr SchedCost kCostEpilogue = {1.36f, 1.36f, 11.0f, 0.05f, 1.39f, 0.0f};
+constexpr SchedCost kCostPlain = {0.9f, 0.92f, 3.0f, 0.08f, 1.1f, 5.0f};
 constexpr int kSplitCandidates[] = {2, 3, 4, 6, 8, 12, 16};
 constexpr int kMinSplitSteps = 4;  // k-steps of 64 per split at least
+
+const SchedCost& sched_cost(bool plain) { return plain ? kCostPlain : kCostEpilogue; }
 
 float rounds(long items) {
   const long full = items / kCUs, rem = items % kCUs;
@@ -71,15 +82,16 @@ float one_tile_cost(const TileCost& t, int m, int n, int nk) {
   return nk * t.kstep_us * rounds(tiles);
 }
 
-float split_step(const TileCost& t, bool wide) {
-  return (t.bn == 128 || !wide) ? kSplitStep : kSplitStepWide;
+float split_step(const TileCost& t, bool plain) {
+  const SchedCost& c = sched_cost(plain);
+  return t.bn == 128 ? c.split_step : c.split_step_wide;
 }
 
-float split_cost(const TileCost& t, int m, int n, int nk, int s, bool wide) {
+float split_cost(const TileCost& t, int m, int n, int nk, int s, bool plain) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
   const float mb = (float)s * tiles * t.bm * t.bn * 8 / 1e6f;
-  return (float)((nk + s - 1) / s) * t.kstep_us * rounds(tiles * s) * split_step(t, wide) +
-         kPieceUsPerMB * mb + kSplitFixed;
+  return (float)((nk + s - 1) / s) * t.kstep_us * rounds(tiles * s) * split_step(t, plain) +
+         sched_cost(plain).piece_us_per_mb * mb + sched_cost(plain).split_fixed;
 }
 
 // one tile per workgroup with the last partial round split along K; S = 0 if not applicable
@@ -92,14 +104,14 @@ int tail_splits(const TileCost& t, int m, int n, int nk) {
   return s;
 }
 
-float tail_cost(const TileCost& t, int m, int n, int nk, int s, bool wide) {
+float tail_cost(const TileCost& t, int m, int n, int nk, int s, bool plain) {
   const long tiles = (long)((m + t.bm - 1) / t.bm) * (n / t.bn);
   const long rem = tiles % kCUs, full = tiles / kCUs;
   const float mb = (float)s * rem * t.bm * t.bn * 8 / 1e6f;
   return nk * t.kstep_us * (float)full +
-         (float)((nk + s - 1) / s) * t.kstep_us * split_step(t, wide) *
+         (float)((nk + s - 1) / s) * t.kstep_us * split_step(t, plain) *
              (kPartialRound + (1.f - kPartialRound) * (float)(rem * s) / kCUs) +
-         kPieceUsPerMB * mb + kSplitFixed;
+         sched_cost(plain).piece_us_per_mb * mb + sched_cost(plain).split_fixed;
 }
 
 float streamk_cost(const TileCost& t, int m, int n, int nk) {
@@ -108,7 +120,8 @@ float streamk_cost(const TileCost& t, int m, int n, int nk) {
   const long split = per < nk ? tiles : std::min<long>(tiles, kCUs);
   const long pieces = std::min<long>(2 * kCUs, kCUs + split);
   const float mb = (float)pieces * t.bm * t.bn * 8 / 1e6f;
-  return per * t.kstep_us * kStreamKStep + kPieceUsPerMB * mb;
+  return per * t.kstep_us * kCostPlain.streamk_step + kCostPlain.piece_us_per_mb * mb +
+         kCostPlain.streamk_fixed;
 }
 
 }  // namespace
