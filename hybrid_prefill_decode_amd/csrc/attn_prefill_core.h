@@ -132,32 +132,37 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
   u32x4 rk[SM::kPer], rv[SM::kPer];
   int blk[SM::kPer];
   const int npages = (kv_len + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
-  // Three-stage software pipeline over key tiles: step kt first stores tile kt + 1 to LDS, then
-  // issues the K/V loads of tile kt + 2 and the block-table reads of tile kt + 3, each from data
-  // that arrived during the previous step, so no step waits on a load it issued itself. Loads
-  // are unconditional: a page past the sequence repeats the last page, whose surplus rows are
-  // masked (K by the score mask, V by zeroing in sstore); invalid table entries read block 0.
+  // Three-stage software pipeline over key tiles: step kt stores tile kt + 1 to LDS, issues the
+  // K/V loads of tile kt + 2 and the block-table reads of tile kt + 3, each from data that
+  // arrived during the previous step, so no step waits on a load it issued itself. The stores
+  // and loads go in the second half of the step, one slice per page of the P V product, after
+  // that page's V fragment reads: the score products then wait only for their own K fragment
+  // reads (the LDS counter drains in issue order, so stores issued before them would hold the
+  // first product back), and the stores overlap the exponentials. Loads are unconditional: a
+  // page past the sequence repeats the last page, whose surplus rows are masked (K by the score
+  // mask, V by zeroing in sstore); invalid table entries read block 0.
   auto tload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < SM::kPer; ++i)
       blk[i] = trow[min(4 * kt + pg0 + kPagesPerI * i, npages - 1)];
   };
+  auto gload1 = [&](int i) {
+    const uint32_t b = ((uint32_t)blk[i] < nb) ? (uint32_t)blk[i] : 0u;
+    const size_t off = (size_t)b * block_bytes;
+    rk[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+    rv[i] = *reinterpret_cast<const u32x4*>(vbase + off);
+  };
   auto gload = [&]() {
 #pragma unroll
-    for (int i = 0; i < SM::kPer; ++i) {
-      const uint32_t b = ((uint32_t)blk[i] < nb) ? (uint32_t)blk[i] : 0u;
-      const size_t off = (size_t)b * block_bytes;
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + off);
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + off);
-    }
+    for (int i = 0; i < SM::kPer; ++i) gload1(i);
   };
   // ZERO: V rows past the sequence end are zeroed when stored (their weight is 0, the slot may
-  // hold anything, and 0 * NaN would poison the product); only the last tile has such rows
-  auto sstore = [&](int buf, int kt, auto zero) {
+  // hold anything, and 0 * NaN would poison the product); only the last tile has such rows.
+  // Slice i of the thread's part of the tile.
+  auto sstore1 = [&](int buf, int kt, int i, auto zero) {
     uint8_t* kb = smem + buf * SM::kStage;
     uint8_t* vb = kb + SM::kKBytes;
-#pragma unroll
-    for (int i = 0; i < SM::kPer; ++i) {
+    {
       u32x4 vv = rv[i];
       if constexpr (decltype(zero)::value) {
         const int tok0 = (4 * kt + pg0 + kPagesPerI * i) * HL_BLOCK_SIZE + 8 * (wv & 1);
@@ -173,6 +178,10 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
       *reinterpret_cast<u32x2*>(vb + v_dst1 + 4096 * i) = u32x2{vv[2], vv[3]};
     }
   };
+  auto sstore = [&](int buf, int kt, auto zero) {
+#pragma unroll
+    for (int i = 0; i < SM::kPer; ++i) sstore1(buf, kt, i, zero);
+  };
   const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
 
   // One key tile. MASKED: keys past a query's position are masked and the stored tile's V rows
@@ -182,11 +191,6 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     const int buf = kt & 1;
     const uint8_t* kb = smem + buf * SM::kStage;
     const uint8_t* vb = kb + SM::kKBytes;
-    // the next tile into the other buffer (last read one step ago, before the barrier), then
-    // the loads of the two tiles after it (past the end they repeat the last tile, unused)
-    sstore(buf ^ 1, min(kt + 1, kt1 - 1), masked);
-    gload();
-    tload(min(kt + 3, kt1 - 1));
     // S^T for the two 32-key halves of the tile; half hb holds keys
     // 32 hb + 8 (i / 4) + 4 hl32 + (i & 3) of query lane & 31
     f32x16 st[2] = {f32x16{}, f32x16{}};
@@ -214,14 +218,12 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(st[hb][i], st[hb][i + 1]));
-    // loads first, stores between the score MFMAs, K fragment reads running ahead of them
-    __builtin_amdgcn_sched_group_barrier(0x020, 3 * SM::kPer, 0);  // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             // LDS read
+    // K fragment reads running three ahead of the score products
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS read
 #pragma unroll
     for (int q = 0; q < D / 8; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (q < D / 8 - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      if (q < 3 * SM::kPer) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
     }
     tmax = wave_max_xor(tmax, 32) * scale_log2;
     // Lazy rescaling: the reference m_run moves only when a tile max exceeds it by more than 8,
@@ -250,13 +252,21 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
         pb[e] = pack_bf2(p0, p1);
         l_run = dot2_bf16(pb[e], ones, l_run);
       }
+      u32x4 va[D / 32];
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(vb + v_off<D>(t, 32 * mt + (lane & 31), hl32));
-        o[mt] = mfma32x32x16(va, pb, o[mt]);
+      for (int mt = 0; mt < D / 32; ++mt)
+        va[mt] = *reinterpret_cast<const u32x4*>(vb + v_off<D>(t, 32 * mt + (lane & 31), hl32));
+      // slice t of the next tile into the other buffer (last read one step ago, before the
+      // barrier), then the loads of the tile after it into the freed registers (past the end
+      // they repeat the last tile, unused)
+      if (t < SM::kPer) {
+        sstore1(buf ^ 1, min(kt + 1, kt1 - 1), t, masked);
+        gload1(t);
       }
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) o[mt] = mfma32x32x16(va[mt], pb, o[mt]);
     }
+    tload(min(kt + 3, kt1 - 1));
     __syncthreads();
   };
 
