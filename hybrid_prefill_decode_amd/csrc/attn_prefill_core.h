@@ -190,7 +190,6 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
     constexpr bool kMasked = decltype(masked)::value;
     const int buf = kt & 1;
     const uint8_t* kb = smem + buf * SM::kStage;
-    const uint8_t* vb = kb + SM::kKBytes;
     // S^T for the two 32-key halves of the tile; half hb holds keys
     // 32 hb + 8 (i / 4) + 4 hl32 + (i & 3) of query lane & 31
     f32x16 st[2] = {f32x16{}, f32x16{}};
@@ -211,6 +210,12 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
           st[hb][i] = (key <= qpos) ? st[hb][i] : -INFINITY;
         }
     }
+    // V fragments of page 0 (each page's are read one page ahead of its products)
+    const uint8_t* vb = kb + SM::kKBytes;
+    u32x4 va[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+      va[mt] = *reinterpret_cast<const u32x4*>(vb + v_off<D>(0, 32 * mt + (lane & 31), hl32));
     // Softmax in the exp2 domain with the scale folded in: the max is taken on raw scores and
     // p = 2^(s * scale_log2 - m) costs one FMA and one exp2.
     float tmax = -INFINITY;
@@ -252,10 +257,13 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
         pb[e] = pack_bf2(p0, p1);
         l_run = dot2_bf16(pb[e], ones, l_run);
       }
-      u32x4 va[D / 32];
+      u32x4 vn[D / 32];
+      if (t < 3) {
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt)
-        va[mt] = *reinterpret_cast<const u32x4*>(vb + v_off<D>(t, 32 * mt + (lane & 31), hl32));
+        for (int mt = 0; mt < D / 32; ++mt)
+          vn[mt] =
+              *reinterpret_cast<const u32x4*>(vb + v_off<D>(t + 1, 32 * mt + (lane & 31), hl32));
+      }
       // slice t of the next tile into the other buffer (last read one step ago, before the
       // barrier), then the loads of the tile after it into the freed registers (past the end
       // they repeat the last tile, unused)
@@ -265,6 +273,10 @@ HL_DEV void prefill_item(const PrefillArgs& a, int tile, int h, uint8_t* smem) {
       }
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) o[mt] = mfma32x32x16(va[mt], pb, o[mt]);
+      if (t < 3) {
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) va[mt] = vn[mt];
+      }
     }
     tload(min(kt + 3, kt1 - 1));
     __syncthreads();
