@@ -11,8 +11,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
                                                         int num_seqs,
                                                         const int32_t* __restrict__ table,
                                                         int max_blocks, hl::Plan p) {
-  __shared__ int wt[5][kThreads / 64];
-  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, p, wt);
+  __shared__ hl::plan::Shared<kThreads> sh;
+  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, p, sh);
 }
 
 }  // namespace

@@ -51,92 +51,171 @@ HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[
   __syncthreads();  // wt may be rewritten by the next call
 }
 
-// The work lists of the batch, built by one workgroup of NT threads (every thread calls it);
-// `wt` is NT / 64 ints x 5 of LDS.
+// LDS of build() for a workgroup of NT threads.
+template <int NT>
+struct Shared {
+  int wt[3][NT / 64];   // wave totals of the scans
+  int off_u[NT + 1];    // per sequence of the current block: first decode unit (block-relative)
+  int off_t[NT + 1];    // first prefill query tile (block-relative)
+  int row[NT];          // first token row of the sequence
+  int cached[NT];       // cached prefix length
+  int kv[NT];           // KV length after the step
+  int dseq[NT];         // decode index (position in dec_seqs)
+  int e_off[NT + 1];    // per prefill query tile of the current pass: first entry (pass-relative)
+  int e_seq[NT];        // its sequence
+  int e_r0[NT];         // its first query row
+  int e_nkt[NT];        // its key tiles
+  int e_slot[NT];       // its first partial slot (or -1 when unsplit)
+};
+
+// Largest i < n with off[i] <= k (off non-decreasing, off[0] = 0 <= k): the sequence whose run
+// of items holds item k. Sequences with no items share the next one's offset and are skipped.
+HL_DEV int owner(const int* off, int n, int k) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= k) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The work lists of the batch, built by one workgroup of NT threads (every thread calls it).
+// Sequences are taken NT at a time: each thread classifies one and the workgroup scans the
+// counts; then the decode units and the prefill query tiles of those sequences are dealt over all
+// threads (a thread finds its item's sequence by binary search over the scanned offsets), so no
+// thread writes a long sequence's records alone. A thread gathers the block ids of up to kBatch
+// units before it stores any record: loads queued behind stores would wait for them.
 template <int NT>
 HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict__ num_cached,
                   int num_seqs, const int32_t* __restrict__ table, int max_blocks,
-                  const hl::Plan& p, int (*wt)[NT / 64]) {
+                  const hl::Plan& p, Shared<NT>& sh) {
   constexpr int QT = hl::kPrefillQTile;
+  constexpr int kBatch = NT >= 1024 ? 2 : 4;  // within the 128 registers of 1024 threads
   if (threadIdx.x < hl::kPlanCounters) p.counters[threadIdx.x * hl::kCounterStride] = 0;
   int base_u = 0, base_d = 0, base_e = 0, base_p = 0, base_m = 0;
   for (int s0 = 0; s0 < num_seqs; s0 += NT) {
-    const int s = s0 + threadIdx.x;
-    int units = 0, is_dec = 0, ents = 0, slots = 0, merges = 0, qlen = 0, c = 0;
+    const int t = threadIdx.x, s = s0 + t;
+    int units = 0, is_dec = 0, tiles = 0, row = 0, c = 0, qlen = 0;
     if (s < num_seqs) {
-      qlen = q_start[s + 1] - q_start[s];
+      row = q_start[s];
+      qlen = q_start[s + 1] - row;
       c = num_cached[s];
-      const int kv = c + qlen;
       if (qlen == 1) {
-        const int pages = (kv + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+        const int pages = (c + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
         units = (pages + p.split_pages - 1) / p.split_pages;
         is_dec = 1;
       } else if (qlen > 1) {
-        for (int r0 = 0; r0 < qlen; r0 += QT) {
-          const int parts = hl::prefill_parts(hl::prefill_key_tiles(c, r0, min(QT, qlen - r0)),
-                                              p.pre_split);
-          ents += parts;
-          if (parts > 1) {
-            slots += parts;
-            merges += 1;
-          }
-        }
+        tiles = (qlen + QT - 1) / QT;
       }
     }
-    const int cnt[5] = {units, is_dec, ents, slots, merges};
-    int off[5], tot[5];
-    block_exclusive_scan<NT, 5>(cnt, off, tot, wt);
-    const int off_u = base_u + off[0], off_d = base_d + off[1], off_e = base_e + off[2],
-              off_p = base_p + off[3], off_m = base_m + off[4];
+    const int cnt[3] = {units, is_dec, tiles};
+    int off[3], tot[3];
+    block_exclusive_scan<NT, 3>(cnt, off, tot, sh.wt);
+    sh.off_u[t] = off[0];
+    sh.off_t[t] = off[2];
+    sh.row[t] = row;
+    sh.cached[t] = c;
+    sh.kv[t] = c + qlen;
+    sh.dseq[t] = base_d + off[1];
     if (is_dec) {
-      const int row = q_start[s];
-      const int pages = (c + qlen + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
-      const int32_t* trow = table + (size_t)s * max_blocks;
-      for (int u = 0; u < units; ++u) {
-        int32_t* r = p.dec_units + (size_t)hl::kDecUnitInts * (off_u + u);
-        const int pg0 = u * p.split_pages, last = min(pg0 + p.split_pages, pages) - 1;
-        r[0] = s;
-        r[1] = pg0;
-        r[2] = off_d;
-        r[3] = units;
-        r[4] = row;
-        r[5] = c + qlen;
-        r[6] = 0;
-        r[7] = 0;
-        for (int j = 0; j < 8; ++j) r[8 + j] = trow[min(pg0 + j, last)];
-      }
-      p.dec_seqs[3 * off_d] = s;
-      p.dec_seqs[3 * off_d + 1] = off_u;
-      p.dec_seqs[3 * off_d + 2] = units;
+      p.dec_seqs[3 * (base_d + off[1])] = s;
+      p.dec_seqs[3 * (base_d + off[1]) + 1] = base_u + off[0];
+      p.dec_seqs[3 * (base_d + off[1]) + 2] = units;
     }
-    if (ents > 0) {
-      int e = off_e, slot = off_p, m = off_m;
-      for (int r0 = ((qlen - 1) / QT) * QT; r0 >= 0; r0 -= QT) {
-        const int nkt = hl::prefill_key_tiles(c, r0, min(QT, qlen - r0));
-        const int parts = hl::prefill_parts(nkt, p.pre_split);
-        for (int j = 0; j < parts; ++j, ++e) {
-          int32_t* t = p.pre_tiles + (size_t)hl::kPreEntry * e;
-          t[0] = s;
-          t[1] = r0;
-          t[2] = (int)((long long)j * nkt / parts);  // near-equal parts
-          t[3] = (int)((long long)(j + 1) * nkt / parts);
-          t[4] = parts > 1 ? slot + j : -1;
-        }
-        if (parts > 1) {
-          p.pre_merge[4 * m] = s;
-          p.pre_merge[4 * m + 1] = r0;
-          p.pre_merge[4 * m + 2] = slot;
-          p.pre_merge[4 * m + 3] = parts;
-          slot += parts;
-          ++m;
+    if (t == 0) {
+      sh.off_u[NT] = tot[0];
+      sh.off_t[NT] = tot[2];
+    }
+    __syncthreads();
+
+    // decode units: 64-byte records, kBatch per thread per round
+    for (int k0 = t; k0 < tot[0]; k0 += kBatch * NT) {
+      int ids[kBatch][8], own[kBatch], pg[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int k = k0 + b * NT;
+        if (k < tot[0]) {
+          const int i = owner(sh.off_u, NT, k);
+          const int pages = (sh.kv[i] + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
+          const int pg0 = (k - sh.off_u[i]) * p.split_pages;
+          const int last = min(pg0 + p.split_pages, pages) - 1;
+          const int32_t* trow = table + (size_t)(s0 + i) * max_blocks;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ids[b][j] = trow[min(pg0 + j, last)];
+          own[b] = i;
+          pg[b] = pg0;
         }
       }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int k = k0 + b * NT, i = own[b];
+        if (k < tot[0]) {
+          int4* r = reinterpret_cast<int4*>(p.dec_units + (size_t)hl::kDecUnitInts * (base_u + k));
+          r[0] = make_int4(s0 + i, pg[b], sh.dseq[i], sh.off_u[i + 1] - sh.off_u[i]);
+          r[1] = make_int4(sh.row[i], sh.kv[i], 0, 0);
+          r[2] = make_int4(ids[b][0], ids[b][1], ids[b][2], ids[b][3]);
+          r[3] = make_int4(ids[b][4], ids[b][5], ids[b][6], ids[b][7]);
+        }
+      }
+    }
+
+    // prefill query tiles, each sequence's last tile first (the longest key ranges are
+    // dispatched first); a tile whose key range exceeds pre_split key tiles becomes near-equal
+    // parts with partial slots and one merge record
+    for (int k0 = 0; k0 < tot[2]; k0 += NT) {
+      const int k = k0 + t;
+      int i = 0, r0 = 0, nkt = 0, parts = 0;
+      if (k < tot[2]) {
+        i = owner(sh.off_t, NT, k);
+        const int ql = sh.kv[i] - sh.cached[i];
+        r0 = ((ql - 1) / QT - (k - sh.off_t[i])) * QT;
+        nkt = hl::prefill_key_tiles(sh.cached[i], r0, min(QT, ql - r0));
+        parts = hl::prefill_parts(nkt, p.pre_split);
+      }
+      const int pc[3] = {parts, parts > 1 ? parts : 0, parts > 1 ? 1 : 0};
+      int po[3], pt[3];
+      block_exclusive_scan<NT, 3>(pc, po, pt, sh.wt);
+      sh.e_off[t] = po[0];
+      sh.e_seq[t] = s0 + i;
+      sh.e_r0[t] = r0;
+      sh.e_nkt[t] = nkt;
+      sh.e_slot[t] = parts > 1 ? base_p + po[1] : -1;
+      if (t == 0) sh.e_off[NT] = pt[0];
+      if (parts > 1) {
+        int32_t* m = p.pre_merge + 4 * (size_t)(base_m + po[2]);
+        m[0] = s0 + i;
+        m[1] = r0;
+        m[2] = base_p + po[1];
+        m[3] = parts;
+      }
+      __syncthreads();
+      // the entries of the pass, one per thread: part j of n covers key tiles
+      // [j * nkt / n, (j + 1) * nkt / n) (near-equal parts)
+      for (int e = t; e < pt[0]; e += NT) {
+        const int tl = owner(sh.e_off, NT, e);
+        const int j = e - sh.e_off[tl], n = sh.e_off[tl + 1] - sh.e_off[tl];
+        const int nk = sh.e_nkt[tl], slot = sh.e_slot[tl];
+        int first, end;
+        if (nk <= 46340) {  // (j + 1) * nk stays below 2^31
+          first = (int)((unsigned)(j * nk) / (unsigned)n);
+          end = (int)((unsigned)((j + 1) * nk) / (unsigned)n);
+        } else {
+          first = (int)((long long)j * nk / n);
+          end = (int)((long long)(j + 1) * nk / n);
+        }
+        int32_t* r = p.pre_tiles + (size_t)hl::kPreEntry * (base_e + e);
+        r[0] = sh.e_seq[tl];
+        r[1] = sh.e_r0[tl];
+        r[2] = first;
+        r[3] = end;
+        r[4] = slot >= 0 ? slot + j : -1;
+      }
+      base_e += pt[0];
+      base_p += pt[1];
+      base_m += pt[2];
     }
     base_u += tot[0];
     base_d += tot[1];
-    base_e += tot[2];
-    base_p += tot[3];
-    base_m += tot[4];
   }
 }
 

@@ -26,12 +26,15 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t* __restrict__ num_cached, int num_seqs, const int32_t* __restrict__ table,
     int max_blocks, long long num_blocks, int D, float theta, int32_t* __restrict__ tok_pos,
     int32_t* __restrict__ tok_blk, float2* __restrict__ rope_cs, hl::Plan plan, int rows) {
-  const int row = blockIdx.x;
-  if (TOKEN_INFO && row == rows) {  // the extra workgroup: the attention work lists
-    __shared__ int wt[5][kThreads / 64];
-    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, plan, wt);
+  // with the work lists asked for, workgroup 0 builds them (dispatched first: its serial chain
+  // of loads and scans is the longest of the launch) and the rows follow
+  const bool lists = TOKEN_INFO && (int)gridDim.x > rows;
+  if (lists && blockIdx.x == 0) {
+    __shared__ hl::plan::Shared<kThreads> sh;
+    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, plan, sh);
     return;
   }
+  const int row = blockIdx.x - (lists ? 1 : 0);
   if (TOKEN_INFO) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {

@@ -661,6 +661,18 @@ def test_step_ragged_small_layer():
     _check_full_step(DeviceCase(spec, DEV), "ragged")
 
 
+def test_step_many_sequences_work_lists():
+    """300 sequences, every other one a prompt chunk of 129..378 rows after a short prefix: the
+    step's work lists take several rounds of sequences, and the first round holds more query
+    tiles and prefill entries than the building workgroup has threads."""
+    seqs = [((i * 37) % 600, 129 + (i * 53) % 250) if i % 2 == 0 else ((i * 97) % 3000, 1)
+            for i in range(300)]
+    spec = workloads.custom_spec(workloads.SHAPES["tiny"], seqs, 5)
+    assert sum((n + 127) // 128 for _, n in seqs[:256] if n > 1) > 256
+    say(f"step many sequences: T={spec.num_tokens} seqs={spec.num_seqs}")
+    _check_full_step(DeviceCase(spec, DEV), "many-seqs")
+
+
 def test_step_deterministic_and_block_permutation_invariant():
     say("step determinism / permutation")
     spec = workloads.make_spec(1)
