@@ -31,8 +31,9 @@ namespace {
 
 using hl::decode::kThreads;
 
-// One workgroup per (unit, KV head); KV head fastest in dispatch order, so the Hkv workgroups of a
-// unit read the Hkv adjacent pieces of each block at about the same time. (Persistent workers that
+// One workgroup per (unit, KV head), dispatched largest unit first when the plan orders the units
+// so (Plan::dec_lpt, which shortens the launch's tail); KV head fastest, so the Hkv workgroups of a unit read the Hkv
+// adjacent pieces of each block at about the same time. (Persistent workers that
 // prefetch each next unit, as the fused launch can, were measured slower for this launch alone:
 // the hardware's dispatch of one short-lived workgroup per unit already overlaps a unit's start
 // with the streaming of the others on its compute unit.)
@@ -44,10 +45,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(hl::decode::De
   cy.item = -1;
   cy.has_pair = false;
   const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
-  hl::decode::decode_item<D, false>(a, blockIdx.x, L, cy);
+  // workgroups in rank order (largest unit first): rank r's unit sits at dec_position(r)
+  const int units = a.n_items / a.Hkv, r = blockIdx.x / a.Hkv;
+  const int item =
+      a.lpt ? hl::dec_position(r, units) * a.Hkv + (blockIdx.x - r * a.Hkv) : (int)blockIdx.x;
+  const int seq_item = hl::decode::decode_item<D, false>(a, item, L, cy);
   if (trace) {
     __syncthreads();
-    hl::record_item(trace, blockIdx.x, t0);
+    hl::record_item(trace, seq_item, t0);
   }
 }
 
@@ -133,7 +138,8 @@ hipError_t launch_decode_attention(const hl_layer_cfg& cfg, const int32_t* q_sta
                                 kpool,            vpool,       (long long)num_blocks, table,
                                 max_blocks,       plan.dec_units, plan.dec_seqs, plan.split_pages,
                                 cfg.n_q_heads,    cfg.n_kv_heads, scale * 1.4426950408889634f,
-                                plan.dec_part,    attn_out,    plan.n_dec_units * cfg.n_kv_heads};
+                                plan.dec_part,    attn_out,    plan.n_dec_units * cfg.n_kv_heads,
+                                plan.dec_lpt};
   // decode records follow the batch's prefill records in the trace
   uint64_t* trace =
       plan.trace ? plan.trace + 3 * (size_t)plan.n_pre_tiles * cfg.n_q_heads : nullptr;

@@ -19,7 +19,8 @@
 // that kind's queue x. Further items are claimed from per-queue device counters (zeroed by the
 // step's plan kernel, each on its own 256-byte line) that number the claims past those first
 // items: a worker drains its own queue, then the other XCDs' queues of its kind, then helps with
-// the other kind, and exits once every queue is empty. A queue is read before it is incremented,
+// the other kind (except prefill workers of a decode-heavy launch), and exits once every queue it
+// may take from is empty. A queue is read before it is incremented,
 // so drained queues cost no atomic. (One shared decode counter serialised every claim at one
 // memory location: with a few hundred workers that cost tens of microseconds per launch.)
 // Each item runs the same code as in the separate kernels (and the same merges follow), so the
@@ -113,9 +114,9 @@ HL_DEV int wg_claim_queue(const Queues& qs, int q, int* s_tick) {
 }
 
 // waiting claim from stage `stage` on (every thread; stage uniform); advances stage past drained
-// queues; -1 when all are drained
-HL_DEV int wg_claim(const Queues& qs, int& stage, int* s_tick) {
-  for (; stage < 16; ++stage) {
+// queues up to `stages`; -1 when all of those are drained
+HL_DEV int wg_claim(const Queues& qs, int& stage, int stages, int* s_tick) {
+  for (; stage < stages; ++stage) {
     const int c = wg_claim_queue(qs, qs.queue_at(stage), s_tick);
     if (c >= 0) return c;
   }
@@ -132,9 +133,15 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
   __shared__ int s_tick;
   const Queues qs{counters, n_pre_items, n_dec_items, n_pre_workers, (int)gridDim.x,
                   (int)(blockIdx.x & 7), (int)blockIdx.x < n_pre_workers};
+  // In a decode-heavy launch (PF) the prefill workers stop when the prefill queues are drained
+  // instead of joining the decode units: one decode worker per compute unit already keeps HBM
+  // busy, and the joining workers' start-up, the shorter units and the thinner tail of fewer
+  // concurrent streams measured ~1.5 % faster over the launch on the 70B-shaped batch. Decode
+  // workers still help with prefill items once the decode queues are drained.
+  const int stages = (PF && qs.pre_worker) ? 8 : 16;
   int stage = 0;
   int cur = qs.first_item(blockIdx.x);
-  if (cur < 0) cur = wg_claim(qs, stage, &s_tick);
+  if (cur < 0) cur = wg_claim(qs, stage, stages, &s_tick);
   while (cur >= 0) {
     if (cur < n_pre_items) {
       // prefill items are long and few: the next claim waits for the item's end (a ticket taken
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
       hl::prefill::prefill_item<D>(pa, item / pa.Hq, item % pa.Hq, smem);
       __syncthreads();  // the item's LDS reads are done before the next item writes
       if (trace) hl::record_item(trace, item, t0);
-      cur = wg_claim(qs, stage, &s_tick);
+      cur = wg_claim(qs, stage, stages, &s_tick);
       continue;
     }
     // A run of decode units. Thread 0 claims the next unit as the current one starts. With PF it
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
         }
       }
       const uint64_t t0 = trace ? (uint64_t)wall_clock64() : 0;
-      hl::decode::decode_item<D, PF>(da, cur - n_pre_items, L, cy);
+      const int seq_item = hl::decode::decode_item<D, PF>(da, cur - n_pre_items, L, cy);
       if (!PF && threadIdx.x == 0) s_tick = t;
       __syncthreads();  // the unit's LDS reads are done and thread 0's claim is visible
       int next;
@@ -181,12 +188,12 @@ __global__ __launch_bounds__(kThreads, 2) void hybrid_attn_kernel(
       } else {
         next = q >= 8 ? qs.resolve(q, __builtin_amdgcn_readfirstlane(s_tick)) : -1;
       }
-      if (trace) hl::record_item(trace, cur, t0);
+      if (trace) hl::record_item(trace, n_pre_items + seq_item, t0);
       __syncthreads();  // every wave has read the claim before thread 0 overwrites it
       if (PF && threadIdx.x == 0) L.tick = hl::decode::kTickPending;
       if (next < 0) {
         ++stage;
-        next = wg_claim(qs, stage, &s_tick);
+        next = wg_claim(qs, stage, stages, &s_tick);
       }
       cur = next;
       if (cur < 0) break;
@@ -223,7 +230,7 @@ DecodeArgs decode_args(const hl_layer_cfg& cfg, const int32_t* q_start,
                             kpool,          vpool,          (long long)num_blocks, table,
                             max_blocks,     plan.dec_units, plan.dec_seqs,  plan.split_pages,
                             cfg.n_q_heads,  cfg.n_kv_heads, scale_log2,     plan.dec_part,
-                            attn_out,       plan.n_dec_units * cfg.n_kv_heads};
+                            attn_out,       plan.n_dec_units * cfg.n_kv_heads, plan.dec_lpt};
 }
 
 float scale_log2_of(const hl_layer_cfg& cfg) {

@@ -37,6 +37,7 @@ struct DecodeArgs {
   float* part;
   hl_bf16* attn_out;
   int n_items;      // decode items (units x KV heads)
+  int lpt;          // unit records in largest-first dispatch order (Plan::dec_lpt)
 };
 
 // LDS of one work item: the waves' (o, m, l) states before they are combined, and the
@@ -58,7 +59,7 @@ struct Pair {
 
 // A unit's record (Plan::dec_units).
 struct UnitRec {
-  int s, pg0, nu, row, kv_len;
+  int s, pg0, nu, row, kv_len, slot;
 };
 HL_DEV UnitRec unit_rec(const int32_t* __restrict__ units, int unit) {
   const int32_t* r = units + (size_t)kDecUnitInts * unit;
@@ -67,7 +68,7 @@ HL_DEV UnitRec unit_rec(const int32_t* __restrict__ units, int unit) {
   // wave-uniform values: scalar registers
   return UnitRec{__builtin_amdgcn_readfirstlane((int)a[0]), __builtin_amdgcn_readfirstlane((int)a[1]),
                  __builtin_amdgcn_readfirstlane((int)a[3]), __builtin_amdgcn_readfirstlane((int)b[0]),
-                 __builtin_amdgcn_readfirstlane((int)b[1])};
+                 __builtin_amdgcn_readfirstlane((int)b[1]), __builtin_amdgcn_readfirstlane((int)b[2])};
 }
 // block ids of the unit's pages first + 2 wave and first + 2 wave + 1, from the record
 HL_DEV void unit_first_pair(const int32_t* __restrict__ units, int unit, int wave, int* blk) {
@@ -89,12 +90,13 @@ struct Carry {
   Pair<D> first;
 };
 
-// Decode item `item` (unit * Hkv + KV head). Every thread of a kThreads-thread workgroup calls it.
-// `cy` holds what the previous item prefetched (used when cy.item == item) and receives the
-// prefetch of the next item. Consecutive items of one workgroup must be separated by a barrier
-// (the LDS is reused).
+// Decode item `item` (unit position * Hkv + KV head). Every thread of a kThreads-thread workgroup
+// calls it. `cy` holds what the previous item prefetched (used when cy.item == item) and receives
+// the prefetch of the next item. Consecutive items of one workgroup must be separated by a barrier
+// (the LDS is reused). Returns the item's index in sequence order (partial slot * Hkv + KV head),
+// which the work-item trace records are indexed by.
 template <int D, bool PREFETCH>
-HL_DEV void decode_item(const DecodeArgs& a, int item, DecodeLds<D>& L, Carry<D>& cy) {
+HL_DEV int decode_item(const DecodeArgs& a, int item, DecodeLds<D>& L, Carry<D>& cy) {
   const hl_bf16* __restrict__ q_rot = a.q_rot;
   const hl_bf16* __restrict__ q_lo = a.q_lo;
   const hl_bf16* __restrict__ kpool = a.kpool;
@@ -361,7 +363,7 @@ HL_DEV void decode_item(const DecodeArgs& a, int item, DecodeLds<D>& L, Carry<D>
       attn_out[((size_t)row * Hq + kvh * g + hh) * D + d] = (hl_bf16)f2bf(acc / lsum);
     }
   } else {
-    float* dst = part + ((size_t)unit * Hkv + kvh) * g * (D + 2);
+    float* dst = part + ((size_t)rc.slot * Hkv + kvh) * g * (D + 2);
     for (int e = tid; e < g * D; e += kThreads) {
       const int hh = e / D, d = e - hh * D;
       float mx = -1e30f;
@@ -382,6 +384,7 @@ HL_DEV void decode_item(const DecodeArgs& a, int item, DecodeLds<D>& L, Carry<D>
     }
   }
   cy = nc;
+  return rc.slot * Hkv + kvh;
 }
 
 }  // namespace decode

@@ -93,12 +93,32 @@ __host__ __device__ inline int prefill_item_at(int p, int n_ent, int Hq, int Hkv
 
 constexpr int kDecUnitInts = 16;
 
+// Dispatch order of the decode units (when Plan::dec_lpt): largest first, so the last units of a
+// launch are short and the workers run out of work at nearly the same time
+// (longest-processing-time-first list scheduling). Full units (split_pages pages) take ranks 0..F-1 in sequence order; each sequence's
+// last unit, when shorter, goes into one of kDecBuckets size classes, the longer classes first.
+constexpr int kDecBuckets = 8;
+// size class of a last unit of `rem` pages, 0 < rem < split (larger class = longer unit)
+__host__ __device__ inline int dec_bucket(int rem, int split) {
+  return (rem * kDecBuckets - 1) / split;
+}
+// Position in the unit list of the unit of rank r among n: the ranks are dealt round-robin to 8
+// contiguous runs of positions (the fused launch's per-XCD queues), so each run holds every 8th
+// rank, largest first.
+__host__ __device__ inline int dec_position(int r, int n) {
+  const int x = r & 7, rem = n & 7;
+  return x * (n >> 3) + (x < rem ? x : rem) + (r >> 3);
+}
+
 struct Plan {
   // device work lists inside the workspace
-  int32_t* dec_units;      // [n_dec_units][kDecUnitInts]: (seq, first page, decode index, units
-                           // of the sequence, its query row, its KV length, 0, 0, then the block
-                           // ids of its pages first .. first + 7, clamped to its last page):
-                           // everything a unit's first page pairs need, in one 64-byte record
+  int32_t* dec_units;      // [n_dec_units][kDecUnitInts] in dispatch order (dec_position):
+                           // (seq, first page, decode index, units of the sequence, its query
+                           // row, its KV length, partial slot, 0, then the block ids of its pages
+                           // first .. first + 7, clamped to its last page): everything a unit's
+                           // first page pairs need, in one 64-byte record. The partial slot is
+                           // the unit's index in sequence order (dec_seqs and dec_part use it);
+                           // without dec_lpt the records are in that order too.
   int32_t* dec_seqs;       // [n_dec_seqs][3]: (seq, first unit, unit count)
   int32_t* pre_tiles;      // [n_pre_tiles][kPreEntry]: (seq, first query row within the sequence,
                            // first key tile, end key tile, partial slot or -1 if unsplit)
@@ -110,6 +130,8 @@ struct Plan {
                            // attention kernel (one per 256-byte line), zeroed by the plan kernel
   int32_t n_dec_units, n_dec_seqs, n_pre_tiles, n_pre_merge;
   int32_t split_pages;     // pages per decode work unit
+  int32_t dec_rank_base[kDecBuckets];  // first rank of each size class of last units
+  int32_t dec_lpt = 0;     // 1: dec_units in largest-first dispatch order, 0: in sequence order
   int32_t pre_split;       // key tiles per prefill work part
   bool fused_prefetch = false;  // fused launch: decode units prefetch the next (decode-heavy)
   uint64_t* trace = nullptr;  // optional [items][3]: (start, end, worker) of every work item,

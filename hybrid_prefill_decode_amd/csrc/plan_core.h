@@ -4,7 +4,10 @@
 // offset num_cached), the two kinds a chunked-prefill iteration mixes ("Chunked prefill
 // (stall-free batching), explained", "How it works, step by step"). One workgroup classifies
 // the sequences and scans their work counts:
-//   decode unit  = (sequence, first page, decode index) covering `split_pages` KV pages;
+//   decode unit  = (sequence, first page, decode index) covering `split_pages` KV pages, stored
+//                  in sequence order or (dec_lpt) in dispatch order (largest first, dealt
+//                  round-robin to 8 runs: dec_position), with its index in sequence order as
+//                  its partial slot;
 //   decode entry = (sequence, first unit, unit count) for the split merge;
 //   prefill entry = (sequence, first query row, key-tile range, partial slot): a tile of
 //                  `kPrefillQTile` query rows, or one part of it when its causal key range is
@@ -21,7 +24,8 @@ namespace hl {
 namespace plan {
 
 // Exclusive scan of N counts per thread across the workgroup, all N at once: a shuffle scan
-// inside each wave, then the wave totals through LDS (two barriers for all N).
+// inside each wave, then a shuffle scan of the wave totals passed through LDS (two barriers for
+// all N).
 template <int NT, int N>
 HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[N],
                                  int (*wt)[NT / 64]) {
@@ -38,15 +42,19 @@ HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[
     if (lane == 63) wt[i][wave] = inc[i];
   }
   __syncthreads();
+  // the wave totals scanned across the lanes of every wave alike: lane w holds wave w's total
+  constexpr int W = NT / 64;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    int before = 0, all = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      before += (w < wave) ? wt[i][w] : 0;
-      all += wt[i][w];
+    int x = lane < W ? wt[i][lane] : 0;
+#pragma unroll
+    for (int d = 1; d < W; d <<= 1) {
+      const int o = __shfl_up(x, d, 64);
+      if (lane >= d) x += o;
     }
+    const int before = wave > 0 ? __shfl(x, wave - 1, 64) : 0;
+    total[i] = __shfl(x, W - 1, 64);
     off[i] = before + inc[i] - v[i];
-    total[i] = all;
   }
   __syncthreads();  // wt may be rewritten by the next call
 }
@@ -54,13 +62,15 @@ HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[
 // LDS of build() for a workgroup of NT threads.
 template <int NT>
 struct Shared {
-  int wt[3][NT / 64];   // wave totals of the scans
+  int wt[4 + hl::kDecBuckets / 2][NT / 64];  // wave totals of the scans
   int off_u[NT + 1];    // per sequence of the current block: first decode unit (block-relative)
   int off_t[NT + 1];    // first prefill query tile (block-relative)
   int row[NT];          // first token row of the sequence
   int cached[NT];       // cached prefix length
   int kv[NT];           // KV length after the step
   int dseq[NT];         // decode index (position in dec_seqs)
+  int full_rank[NT];    // dispatch rank of the sequence's first full unit
+  int last_rank[NT];    // dispatch rank of its shorter last unit, or -1 if all units are full
   int e_off[NT + 1];    // per prefill query tile of the current pass: first entry (pass-relative)
   int e_seq[NT];        // its sequence
   int e_r0[NT];         // its first query row
@@ -92,10 +102,11 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
   constexpr int QT = hl::kPrefillQTile;
   constexpr int kBatch = NT >= 1024 ? 2 : 4;  // within the 128 registers of 1024 threads
   if (threadIdx.x < hl::kPlanCounters) p.counters[threadIdx.x * hl::kCounterStride] = 0;
-  int base_u = 0, base_d = 0, base_e = 0, base_p = 0, base_m = 0;
+  int base_u = 0, base_d = 0, base_e = 0, base_p = 0, base_m = 0, base_f = 0;
+  int base_b[hl::kDecBuckets] = {};
   for (int s0 = 0; s0 < num_seqs; s0 += NT) {
     const int t = threadIdx.x, s = s0 + t;
-    int units = 0, is_dec = 0, tiles = 0, row = 0, c = 0, qlen = 0;
+    int units = 0, is_dec = 0, tiles = 0, row = 0, c = 0, qlen = 0, full = 0, bucket = -1;
     if (s < num_seqs) {
       row = q_start[s];
       qlen = q_start[s + 1] - row;
@@ -104,19 +115,32 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
         const int pages = (c + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
         units = (pages + p.split_pages - 1) / p.split_pages;
         is_dec = 1;
+        const int rem = pages % p.split_pages;
+        full = units - (rem ? 1 : 0);
+        if (rem) bucket = hl::dec_bucket(rem, p.split_pages);
       } else if (qlen > 1) {
         tiles = (qlen + QT - 1) / QT;
       }
     }
-    const int cnt[3] = {units, is_dec, tiles};
-    int off[3], tot[3];
-    block_exclusive_scan<NT, 3>(cnt, off, tot, sh.wt);
+    // the size classes two to an int (16 bits each: at most NT per round)
+    int cnt[4 + hl::kDecBuckets / 2] = {units, is_dec, tiles, full};
+#pragma unroll
+    for (int j = 0; j < hl::kDecBuckets / 2; ++j)
+      cnt[4 + j] = bucket == 2 * j ? 1 : (bucket == 2 * j + 1 ? 1 << 16 : 0);
+    int off[4 + hl::kDecBuckets / 2], tot[4 + hl::kDecBuckets / 2];
+    block_exclusive_scan<NT, 4 + hl::kDecBuckets / 2>(cnt, off, tot, sh.wt);
     sh.off_u[t] = off[0];
     sh.off_t[t] = off[2];
     sh.row[t] = row;
     sh.cached[t] = c;
     sh.kv[t] = c + qlen;
     sh.dseq[t] = base_d + off[1];
+    sh.full_rank[t] = base_f + off[3];
+    sh.last_rank[t] = -1;
+#pragma unroll
+    for (int k = 0; k < hl::kDecBuckets; ++k)
+      if (bucket == k)
+        sh.last_rank[t] = p.dec_rank_base[k] + base_b[k] + ((off[4 + k / 2] >> (16 * (k & 1))) & 0xffff);
     if (is_dec) {
       p.dec_seqs[3 * (base_d + off[1])] = s;
       p.dec_seqs[3 * (base_d + off[1]) + 1] = base_u + off[0];
@@ -150,9 +174,13 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
       for (int b = 0; b < kBatch; ++b) {
         const int k = k0 + b * NT, i = own[b];
         if (k < tot[0]) {
-          int4* r = reinterpret_cast<int4*>(p.dec_units + (size_t)hl::kDecUnitInts * (base_u + k));
-          r[0] = make_int4(s0 + i, pg[b], sh.dseq[i], sh.off_u[i + 1] - sh.off_u[i]);
-          r[1] = make_int4(sh.row[i], sh.kv[i], 0, 0);
+          const int nu = sh.off_u[i + 1] - sh.off_u[i], u = k - sh.off_u[i];
+          const int last = sh.last_rank[i];
+          const int rank = (last >= 0 && u == nu - 1) ? last : sh.full_rank[i] + u;
+          const int pos = p.dec_lpt ? hl::dec_position(rank, p.n_dec_units) : base_u + k;
+          int4* r = reinterpret_cast<int4*>(p.dec_units + (size_t)hl::kDecUnitInts * pos);
+          r[0] = make_int4(s0 + i, pg[b], sh.dseq[i], nu);
+          r[1] = make_int4(sh.row[i], sh.kv[i], base_u + k, 0);
           r[2] = make_int4(ids[b][0], ids[b][1], ids[b][2], ids[b][3]);
           r[3] = make_int4(ids[b][4], ids[b][5], ids[b][6], ids[b][7]);
         }
@@ -216,6 +244,9 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
     }
     base_u += tot[0];
     base_d += tot[1];
+    base_f += tot[3];
+#pragma unroll
+    for (int k = 0; k < hl::kDecBuckets; ++k) base_b[k] += (tot[4 + k / 2] >> (16 * (k & 1))) & 0xffff;
   }
 }
 

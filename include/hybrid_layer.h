@@ -489,7 +489,9 @@ int hl_attention_run(const hl_batch_desc* batch, const hl_bf16* q_rot, const hl_
  * receives three values per item: start and end time on the device's constant-rate clock
  * (hl_trace_clock_khz), and the workgroup that ran it. Items are numbered prefill items first
  * (entry * n_q_heads + query head, entries as hl_attention_plan's prefill_parts), then decode work
- * (unit * n_kv_heads + kv head, units as its decode_units); a path that does not run leaves its
+ * (unit * n_kv_heads + kv head, units as its decode_units, numbered in sequence order: each decode
+ * sequence's pages in order, split_pages per unit, whatever order they ran in); a path that does
+ * not run leaves its
  * records untouched. Results equal hl_attention_run's bit for bit. Errors: those of
  * hl_attention_run; HL_ERR_NULL for a NULL trace, HL_ERR_ALIGN, HL_ERR_ARG if trace_entries is
  * less than 3 * (prefill_parts * n_q_heads + decode_units * n_kv_heads). */
