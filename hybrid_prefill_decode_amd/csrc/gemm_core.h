@@ -494,6 +494,42 @@ HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot
   }
 }
 
+// The V rows of a staged fp32 tile into the Vᵀ pages. A page holds a head's values d-major
+// ([d][16 slots]), so one token's row is 128 two-byte stores 32 bytes apart, and a store
+// instruction costs one memory request per 32-byte piece it touches. Lanes go 16 rows by 4 d:
+// when the 16 rows are consecutive tokens of one page (a prompt chunk), an instruction writes 4
+// whole 32-byte pieces; lanes along 8-element runs of one row (as for q and k) made 16 requests
+// per instruction there. A decode row is alone in its page either way. `row_of(rr, blk, slot)`
+// gives staged row rr's page and slot, false for a row past the end or without a page. Every
+// thread of the workgroup calls it.
+template <int HD, class RowOf>
+HL_DEV void v_append_rows(const GemmEpi& ep, const float* st, int sstride, int rows, int gh_base,
+                          int heads, RowOf row_of) {
+  const int v0 = ep.n_q_heads + ep.n_kv_heads;  // first V head among the projection's columns
+  const int h0 = max(v0 - gh_base, 0), h1 = min(heads, v0 + ep.n_kv_heads - gh_base);
+  const int nvh = h1 - h0;
+  if (nvh <= 0) return;
+  const int groups = (rows + 15) / 16;
+  constexpr int DG = HD / 8;  // runs of 8 d per lane; the lanes of a store cover 16 rows x 4 runs
+  for (int e = threadIdx.x; e < groups * 16 * nvh * DG; e += blockDim.x) {
+    const int rl = e & 15, dq = (e >> 4) & 3, rest = e >> 6;
+    const int db = rest % (DG / 4), rest2 = rest / (DG / 4);
+    const int hv = rest2 % nvh, rr = (rest2 / nvh) * 16 + rl;
+    int blk, slot;
+    if (rr >= rows || !row_of(rr, blk, slot)) continue;
+    const int hi = h0 + hv;
+    const float* src = st + rr * sstride + hi * HD;
+    hl_bf16* dst = ep.vpool + ((size_t)blk * ep.n_kv_heads + (gh_base + hi - v0)) * HD * HL_BLOCK_SIZE + slot;
+    // run j of the lane's 8 values: d = 32 db + 4 j + dq, so one instruction's 4 lanes of a row
+    // take 4 adjacent d-rows
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = 32 * db + 4 * j + dq;
+      dst[(size_t)d * HL_BLOCK_SIZE] = (hl_bf16)f2bf(src[d]);
+    }
+  }
+}
+
 // SK: stream-K run of (tile, k-step) iterations; otherwise exactly one tile per workgroup (kept a
 // separate instantiation so the one-tile kernels carry no loop state in registers).
 template <int EPI, int BM, int BN, int HD, bool SK>
@@ -619,13 +655,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
             }
         }
         __syncthreads();
+        const int vfirst = ep.n_q_heads + ep.n_kv_heads;  // q and k heads here, V heads below
         for (int e = tid; e < PROWS * heads * chunks; e += kThreads) {
           const int c = e % chunks, rest = e / chunks, hi = rest % heads, rr = rest / heads;
           const int r = pass * PROWS + rr, gm = m0 + r;
-          if (gm >= M) continue;
+          if (gm >= M || nt * heads + hi >= vfirst) continue;
           rope_store_row<HD>(ep, gm, nt * heads + hi, blk_sh[r], pos_sh[r] & (HL_BLOCK_SIZE - 1),
                              (pos_sh[r] & hl::kDecodeBit) != 0, st + rr * SROW + hi * HD, c);
         }
+        v_append_rows<HD>(ep, st, SROW, PROWS, nt * heads, heads, [&](int rr, int& blk, int& slot) {
+          const int r = pass * PROWS + rr;
+          blk = blk_sh[r];
+          slot = pos_sh[r] & (HL_BLOCK_SIZE - 1);
+          return m0 + r < M && blk >= 0;
+        });
         if (NPASS > 1) __syncthreads();
       }
     } else {
@@ -866,14 +909,22 @@ __global__ __launch_bounds__(256) void gemm_split_rope_fixup(int M, GemmEpi ep, 
   }
   __syncthreads();
   constexpr int heads = BN / HD, chunks = HD / 16;
+  const int vfirst = ep.n_q_heads + ep.n_kv_heads;  // q and k heads here, V heads below
   for (int e = tid; e < ROWS * heads * chunks; e += 256) {
     const int c = e % chunks, rest = e / chunks, hi = rest % heads, rr = rest / heads;
     const int gm = mt * BM + r0 + rr;
-    if (gm >= M) continue;
+    if (gm >= M || nt * heads + hi >= vfirst) continue;
     const int pos = ep.tok_pos[gm];
     rope_store_row<HD>(ep, gm, nt * heads + hi, ep.tok_blk[gm], pos & (HL_BLOCK_SIZE - 1),
                        (pos & hl::kDecodeBit) != 0, st + rr * SROW + hi * HD, c);
   }
+  v_append_rows<HD>(ep, st, SROW, ROWS, nt * heads, heads, [&](int rr, int& blk, int& slot) {
+    const int gm = mt * BM + r0 + rr;
+    if (gm >= M) return false;
+    blk = ep.tok_blk[gm];
+    slot = ep.tok_pos[gm] & (HL_BLOCK_SIZE - 1);
+    return blk >= 0;
+  });
 }
 
 // Pieces of a split-K launch must fit the stream-K workspace.
