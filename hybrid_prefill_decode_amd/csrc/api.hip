@@ -30,6 +30,7 @@ struct HostPlan {
   int32_t n_pre_merge = 0, n_pre_slots = 0, pre_split = 1 << 30;
   int32_t dec_rank_base[hl::kDecBuckets] = {};  // see hl::Plan
   int32_t dec_lpt = 0;                           // see hl::Plan
+  int32_t max_seq_units = 0;                     // see hl::Plan
   bool fused = false;  // prefill and decode attention in one launch
   bool fused_prefetch = false;  // ... whose decode units prefetch their successors
   // workspace byte offsets
@@ -334,7 +335,9 @@ void make_plan(const hl_batch_desc* b, HostPlan* p) {
     const int qlen = b->h_q_start[s + 1] - b->h_q_start[s];
     if (qlen == 1) {
       const int pages = (b->h_num_cached[s] + 1 + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
-      p->n_dec_units += (pages + p->split_pages - 1) / p->split_pages;
+      const int units = (pages + p->split_pages - 1) / p->split_pages;
+      p->n_dec_units += units;
+      p->max_seq_units = std::max(p->max_seq_units, units);
       p->n_dec_seqs += 1;
       const int rem = pages % p->split_pages;
       if (rem) ++last_units[hl::dec_bucket(rem, p->split_pages)];
@@ -410,6 +413,7 @@ hl::Plan device_plan(const HostPlan& hp, void* ws) {
   p.split_pages = hp.split_pages;
   for (int k = 0; k < hl::kDecBuckets; ++k) p.dec_rank_base[k] = hp.dec_rank_base[k];
   p.dec_lpt = hp.dec_lpt;
+  p.max_seq_units = hp.max_seq_units;
   p.pre_split = hp.pre_split;
   p.fused_prefetch = hp.fused_prefetch;
   return p;

@@ -57,49 +57,69 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(hl::decode::De
 }
 
 // Merge the split partials of each multi-unit decode sequence and write its attention row.
-template <int D>
+// Two dependent rounds of loads: the (m, l) pairs of every unit and head (one 8-byte load each)
+// together with the thread's o partials of the first kPre units, which do not depend on the
+// weights; then one thread per head forms the max, the weights and l* from LDS. GMAX bounds the
+// group size g (the thread's output elements live in registers); the LDS holds the batch's most
+// units of one sequence (dynamic size: 2 * max units * g floats).
+template <int D, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ dec_seqs,
-    const float* __restrict__ part, int Hq, int Hkv, hl_bf16* __restrict__ attn_out) {
-  __shared__ float sh_w[hl::kMaxUnitsPerSeq * 16];
-  __shared__ float sh_mx[16], sh_lt[16];
+    const float* __restrict__ part, int Hq, int Hkv, int max_units,
+    hl_bf16* __restrict__ attn_out) {
+  constexpr int kPre = 8;                                   // units whose o is loaded up front
+  constexpr int kEl = (GMAX * D + kThreads - 1) / kThreads;  // output elements per thread
+  extern __shared__ float sh[];
+  __shared__ float sh_lt[16];
   const int di = blockIdx.x, kvh = blockIdx.y;
   const int s = dec_seqs[3 * di], u0 = dec_seqs[3 * di + 1], nu = dec_seqs[3 * di + 2];
   if (nu == 1) return;  // written directly by the decode kernel
   const int g = Hq / Hkv;
-  const int row = q_start[s];
+  float* sh_w = sh;                   // [max_units][g]: m, then the weights 2^(m - m*)
+  float* sh_l = sh + max_units * g;   // [max_units][g]
   const int tid = threadIdx.x;
   const size_t ustride = (size_t)Hkv * g * (D + 2);
   const float* base = part + ((size_t)u0 * Hkv + kvh) * g * (D + 2);
-  // m of every (unit, head) into LDS, then per-head max, weights and l*
+  float pre[kEl][kPre];
+#pragma unroll
+  for (int i = 0; i < kEl; ++i) {
+    const int e = tid + i * kThreads;
+    const int hh = e / D, d = e - hh * D;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      pre[i][u] = (e < g * D && u < nu) ? base[u * ustride + hh * (D + 2) + d] : 0.f;
+  }
   for (int e = tid; e < nu * g; e += kThreads) {
     const int u = e / g, hh = e - u * g;
-    sh_w[u * 16 + hh] = base[u * ustride + hh * (D + 2) + D];
+    const float2 ml = *reinterpret_cast<const float2*>(base + u * ustride + hh * (D + 2) + D);
+    sh_w[u * g + hh] = ml.x;
+    sh_l[u * g + hh] = ml.y;
   }
+  const int row = q_start[s];
   __syncthreads();
   if (tid < g) {
     float mx = -1e30f;
-    for (int u = 0; u < nu; ++u) mx = fmaxf(mx, sh_w[u * 16 + tid]);
-    sh_mx[tid] = mx;
-  }
-  __syncthreads();
-  for (int e = tid; e < nu * g; e += kThreads) {
-    const int u = e / g, hh = e - u * g;
-    sh_w[u * 16 + hh] = exp2f(sh_w[u * 16 + hh] - sh_mx[hh]);
-  }
-  __syncthreads();
-  if (tid < g) {
+    for (int u = 0; u < nu; ++u) mx = fmaxf(mx, sh_w[u * g + tid]);
     float lt = 0.f;
-    for (int u = 0; u < nu; ++u) lt += base[u * ustride + tid * (D + 2) + D + 1] * sh_w[u * 16 + tid];
+    for (int u = 0; u < nu; ++u) {
+      const float w = exp2f(sh_w[u * g + tid] - mx);
+      sh_w[u * g + tid] = w;
+      lt += sh_l[u * g + tid] * w;
+    }
     sh_lt[tid] = lt;
   }
   __syncthreads();
-  for (int e = tid; e < g * D; e += kThreads) {
+#pragma unroll
+  for (int i = 0; i < kEl; ++i) {
+    const int e = tid + i * kThreads;
+    if (e >= g * D) break;
     const int hh = e / D, d = e - hh * D;
-    const float* p = base + hh * (D + 2) + d;
     float acc = 0.f;
-#pragma unroll 8
-    for (int u = 0; u < nu; ++u) acc += p[u * ustride] * sh_w[u * 16 + hh];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      if (u < nu) acc += pre[i][u] * sh_w[u * g + hh];
+    const float* p = base + hh * (D + 2) + d;
+    for (int u = kPre; u < nu; ++u) acc += p[u * ustride] * sh_w[u * g + hh];
     attn_out[((size_t)row * Hq + kvh * g + hh) * D + d] = (hl_bf16)f2bf(acc / sh_lt[hh]);
   }
 }
@@ -114,12 +134,13 @@ hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, 
                                hl_bf16* attn_out, hipStream_t st) {
   if (plan.n_dec_seqs <= 0) return hipSuccess;
   const dim3 grid(plan.n_dec_seqs, cfg.n_kv_heads), block(kThreads);
-  if (cfg.head_dim == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, st, q_start, plan.dec_seqs,
-                       plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads, attn_out);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, st, q_start, plan.dec_seqs,
-                       plan.dec_part, cfg.n_q_heads, cfg.n_kv_heads, attn_out);
+  const int g = cfg.n_q_heads / cfg.n_kv_heads;
+  const int mu = plan.max_seq_units > 0 ? plan.max_seq_units : hl::kMaxUnitsPerSeq;
+  const size_t lds = sizeof(float) * 2 * (size_t)mu * g;
+  auto kernel = cfg.head_dim == 128 ? (g <= 8 ? decode_merge_kernel<128, 8> : decode_merge_kernel<128, 16>)
+                                    : (g <= 8 ? decode_merge_kernel<64, 8> : decode_merge_kernel<64, 16>);
+  hipLaunchKernelGGL(kernel, grid, block, lds, st, q_start, plan.dec_seqs, plan.dec_part,
+                     cfg.n_q_heads, cfg.n_kv_heads, mu, attn_out);
   return hipGetLastError();
 }
 

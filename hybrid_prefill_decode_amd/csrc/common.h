@@ -132,6 +132,7 @@ struct Plan {
   int32_t split_pages;     // pages per decode work unit
   int32_t dec_rank_base[kDecBuckets];  // first rank of each size class of last units
   int32_t dec_lpt = 0;     // 1: dec_units in largest-first dispatch order, 0: in sequence order
+  int32_t max_seq_units = 0;  // most decode units of one sequence (sizes the merge's LDS)
   int32_t pre_split;       // key tiles per prefill work part
   bool fused_prefetch = false;  // fused launch: decode units prefetch the next (decode-heavy)
   uint64_t* trace = nullptr;  // optional [items][3]: (start, end, worker) of every work item,
