@@ -414,6 +414,8 @@ ATTN_CASES = {
     "ragged": (workloads.SHAPES["tiny"], [(0, 2), (3, 129), (45, 1), (0, 1), (15, 1), (16, 1),
                                           (31, 33), (1000, 1), (511, 1)]),
     "g16_d128": (workloads.LayerShape(2048, 16, 1, 128, 512), [(100, 77), (600, 1), (17, 1)]),
+    # 16 query heads per KV head at d = 64 with multi-unit decodes (the merge's wide-group build)
+    "g16_d64": (workloads.LayerShape(2048, 32, 2, 64, 512), [(300, 40), (900, 1), (255, 1)]),
     "g5_d128": (workloads.LayerShape(1280, 10, 2, 128, 512), [(40, 300), (2047, 1), (2048, 1)]),
     # fused launch with far more decode units than prefill items, and the other way round
     "many_decodes": (workloads.SHAPES["tiny"], [(7, 200)] + [(17 * i % 1500, 1) for i in range(300)]),
