@@ -183,7 +183,7 @@ struct GemmEpi {
   const float2* rope_cs;
 };
 
-// plan: also build the attention work lists (one extra workgroup; needs ti).
+// plan: also build the attention work lists (kPlanWorkgroups extra workgroups; needs ti).
 hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float* rscale,
                        int32_t rows, int32_t cols, float eps, const TokenInfo* ti,
                        hipStream_t st, const Plan* plan = nullptr);
@@ -191,6 +191,7 @@ hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_
                        const int32_t* table, int32_t max_blocks, const Plan& plan,
                        hipStream_t st);
 constexpr int kPlanCounters = 16;
+constexpr int kPlanWorkgroups = 8;  // workgroups that build the work lists together
 constexpr int kCounterStride = 64;  // int32 slots per counter: each on its own 256-byte line
 constexpr int kMaxUnitsPerSeq = 256;  // decode work units of one sequence (merge weights in LDS)
 hipError_t launch_rmsnorm(const hl_bf16* x, const hl_bf16* g, hl_bf16* y, int32_t rows,

@@ -12,7 +12,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ table,
                                                         int max_blocks, hl::Plan p) {
   __shared__ hl::plan::Shared<kThreads> sh;
-  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, p, sh);
+  hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, p, sh, blockIdx.x,
+                            gridDim.x);
 }
 
 }  // namespace
@@ -22,8 +23,8 @@ hipError_t launch_plan(const int32_t* q_start, const int32_t* num_cached, int32_
                        const int32_t* table, int32_t max_blocks, const Plan& plan,
                        hipStream_t st) {
   if (num_seqs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, st, q_start, num_cached, num_seqs,
-                     table, max_blocks, plan);
+  hipLaunchKernelGGL(plan_kernel, dim3(hl::kPlanWorkgroups), dim3(kThreads), 0, st, q_start,
+                     num_cached, num_seqs, table, max_blocks, plan);
   return hipGetLastError();
 }
 }  // namespace hl

@@ -23,22 +23,30 @@
 namespace hl {
 namespace plan {
 
-// Exclusive scan of N counts per thread across the workgroup, all N at once: a shuffle scan
-// inside each wave, then a shuffle scan of the wave totals passed through LDS (two barriers for
-// all N).
+// Inclusive sum over the lanes of a wave, lane 0 first: four shifts within each row of 16 lanes,
+// then row 15's sum into rows 1 and 3 and row 31's into rows 2 and 3 (DPP row_shr and row_bcast
+// on the VALU; a lane with no source adds 0).
+HL_DEV int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Exclusive scan of N counts per thread across the workgroup, all N at once: a scan inside each
+// wave, then a scan of the wave totals passed through LDS (two barriers for all N).
 template <int NT, int N>
 HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[N],
                                  int (*wt)[NT / 64]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   int inc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    inc[i] = v[i];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(inc[i], d, 64);
-      if (lane >= d) inc[i] += o;
-    }
+    inc[i] = wave_incl_scan(v[i]);
     if (lane == 63) wt[i][wave] = inc[i];
   }
   __syncthreads();
@@ -46,14 +54,9 @@ HL_DEV void block_exclusive_scan(const int (&v)[N], int (&off)[N], int (&total)[
   constexpr int W = NT / 64;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    int x = lane < W ? wt[i][lane] : 0;
-#pragma unroll
-    for (int d = 1; d < W; d <<= 1) {
-      const int o = __shfl_up(x, d, 64);
-      if (lane >= d) x += o;
-    }
-    const int before = wave > 0 ? __shfl(x, wave - 1, 64) : 0;
-    total[i] = __shfl(x, W - 1, 64);
+    const int x = wave_incl_scan(lane < W ? wt[i][lane] : 0);
+    const int before = wave > 0 ? __builtin_amdgcn_readlane(x, wave - 1) : 0;
+    total[i] = __builtin_amdgcn_readlane(x, W - 1);
     off[i] = before + inc[i] - v[i];
   }
   __syncthreads();  // wt may be rewritten by the next call
@@ -89,19 +92,21 @@ HL_DEV int owner(const int* off, int n, int k) {
   return lo;
 }
 
-// The work lists of the batch, built by one workgroup of NT threads (every thread calls it).
-// Sequences are taken NT at a time: each thread classifies one and the workgroup scans the
-// counts; then the decode units and the prefill query tiles of those sequences are dealt over all
-// threads (a thread finds its item's sequence by binary search over the scanned offsets), so no
-// thread writes a long sequence's records alone. A thread gathers the block ids of up to kBatch
-// units before it stores any record: loads queued behind stores would wait for them.
+// The work lists of the batch, built by nwg workgroups of NT threads (every thread of workgroup
+// wg calls it). Sequences are taken NT at a time: each thread classifies one and the workgroup
+// scans the counts; then the decode units and the prefill query tiles of those sequences are
+// dealt over the threads of all nwg workgroups (a thread finds its item's sequence by binary
+// search over the scanned offsets), so no thread writes a long sequence's records alone and the
+// scattered table reads and record stores spread over nwg compute units. Every workgroup runs the
+// same scans (cheap) and writes only its share of the records. A thread gathers the block ids of
+// up to kBatch units before it stores any record: loads queued behind stores would wait for them.
 template <int NT>
 HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict__ num_cached,
                   int num_seqs, const int32_t* __restrict__ table, int max_blocks,
-                  const hl::Plan& p, Shared<NT>& sh) {
+                  const hl::Plan& p, Shared<NT>& sh, int wg, int nwg) {
   constexpr int QT = hl::kPrefillQTile;
   constexpr int kBatch = NT >= 1024 ? 2 : 4;  // within the 128 registers of 1024 threads
-  if (threadIdx.x < hl::kPlanCounters) p.counters[threadIdx.x * hl::kCounterStride] = 0;
+  if (wg == 0 && threadIdx.x < hl::kPlanCounters) p.counters[threadIdx.x * hl::kCounterStride] = 0;
   int base_u = 0, base_d = 0, base_e = 0, base_p = 0, base_m = 0, base_f = 0;
   int base_b[hl::kDecBuckets] = {};
   for (int s0 = 0; s0 < num_seqs; s0 += NT) {
@@ -141,7 +146,7 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
     for (int k = 0; k < hl::kDecBuckets; ++k)
       if (bucket == k)
         sh.last_rank[t] = p.dec_rank_base[k] + base_b[k] + ((off[4 + k / 2] >> (16 * (k & 1))) & 0xffff);
-    if (is_dec) {
+    if (is_dec && s % nwg == wg) {
       p.dec_seqs[3 * (base_d + off[1])] = s;
       p.dec_seqs[3 * (base_d + off[1]) + 1] = base_u + off[0];
       p.dec_seqs[3 * (base_d + off[1]) + 2] = units;
@@ -153,11 +158,12 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
     __syncthreads();
 
     // decode units: 64-byte records, kBatch per thread per round
-    for (int k0 = t; k0 < tot[0]; k0 += kBatch * NT) {
+    const int ustep = nwg * NT;  // unit k belongs to workgroup (k / NT) % nwg
+    for (int k0 = wg * NT + t; k0 < tot[0]; k0 += kBatch * ustep) {
       int ids[kBatch][8], own[kBatch], pg[kBatch];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int k = k0 + b * NT;
+        const int k = k0 + b * ustep;
         if (k < tot[0]) {
           const int i = owner(sh.off_u, NT, k);
           const int pages = (sh.kv[i] + HL_BLOCK_SIZE - 1) / HL_BLOCK_SIZE;
@@ -172,7 +178,7 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int k = k0 + b * NT, i = own[b];
+        const int k = k0 + b * ustep, i = own[b];
         if (k < tot[0]) {
           const int nu = sh.off_u[i + 1] - sh.off_u[i], u = k - sh.off_u[i];
           const int last = sh.last_rank[i];
@@ -209,7 +215,7 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
       sh.e_nkt[t] = nkt;
       sh.e_slot[t] = parts > 1 ? base_p + po[1] : -1;
       if (t == 0) sh.e_off[NT] = pt[0];
-      if (parts > 1) {
+      if (parts > 1 && k % nwg == wg) {
         int32_t* m = p.pre_merge + 4 * (size_t)(base_m + po[2]);
         m[0] = s0 + i;
         m[1] = r0;
@@ -219,7 +225,7 @@ HL_DEV void build(const int32_t* __restrict__ q_start, const int32_t* __restrict
       __syncthreads();
       // the entries of the pass, one per thread: part j of n covers key tiles
       // [j * nkt / n, (j + 1) * nkt / n) (near-equal parts)
-      for (int e = t; e < pt[0]; e += NT) {
+      for (int e = wg * NT + t; e < pt[0]; e += nwg * NT) {
         const int tl = owner(sh.e_off, NT, e);
         const int j = e - sh.e_off[tl], n = sh.e_off[tl + 1] - sh.e_off[tl];
         const int nk = sh.e_nkt[tl], slot = sh.e_slot[tl];

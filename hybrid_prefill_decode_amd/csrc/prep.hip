@@ -10,7 +10,7 @@
 // the rotary cos/sin of every pair j < d/2 at that position (angles formed in fp64), which the
 // QKV GEMM epilogue uses to rotate q and k and to append K/V ("Chunked prefill (stall-free
 // batching), explained", "How it works, step by step": new tokens write their K/V into the cache).
-// When asked, one extra workgroup of that pass builds the step's attention work lists
+// When asked, kPlanWorkgroups extra workgroups of that pass build the step's attention work lists
 // (plan_core.h), which saves the step a separate launch.
 #include "plan_core.h"
 
@@ -26,15 +26,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t* __restrict__ num_cached, int num_seqs, const int32_t* __restrict__ table,
     int max_blocks, long long num_blocks, int D, float theta, int32_t* __restrict__ tok_pos,
     int32_t* __restrict__ tok_blk, float2* __restrict__ rope_cs, hl::Plan plan, int rows) {
-  // with the work lists asked for, workgroup 0 builds them (dispatched first: its serial chain
-  // of loads and scans is the longest of the launch) and the rows follow
-  const bool lists = TOKEN_INFO && (int)gridDim.x > rows;
-  if (lists && blockIdx.x == 0) {
+  // with the work lists asked for, the first workgroups build them (dispatched first: their
+  // chain of loads and scans is the longest of the launch) and the rows follow
+  const int nlists = TOKEN_INFO ? (int)gridDim.x - rows : 0;
+  if ((int)blockIdx.x < nlists) {
     __shared__ hl::plan::Shared<kThreads> sh;
-    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, plan, sh);
+    hl::plan::build<kThreads>(q_start, num_cached, num_seqs, table, max_blocks, plan, sh,
+                              blockIdx.x, nlists);
     return;
   }
-  const int row = blockIdx.x - (lists ? 1 : 0);
+  const int row = blockIdx.x - nlists;
   if (TOKEN_INFO) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
@@ -118,7 +119,8 @@ hipError_t launch_prep(const hl_bf16* x, const hl_bf16* gain, hl_bf16* xg, float
   if (rows <= 0) return hipSuccess;
   if (ti) {
     const Plan pl = plan ? *plan : Plan{};
-    hipLaunchKernelGGL(prep_kernel<true>, dim3(rows + (plan ? 1 : 0)), dim3(kThreads), 0, st, x,
+    hipLaunchKernelGGL(prep_kernel<true>, dim3(rows + (plan ? hl::kPlanWorkgroups : 0)),
+                       dim3(kThreads), 0, st, x,
                        gain, xg, rscale, cols, eps, ti->q_start, ti->num_cached, ti->num_seqs,
                        ti->table, ti->max_blocks, (long long)ti->num_blocks, ti->head_dim,
                        ti->rope_theta, ti->tok_pos, ti->tok_blk, ti->rope_cs, pl, rows);
