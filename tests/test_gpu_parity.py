@@ -427,6 +427,10 @@ ATTN_CASES = {
     "split_long_prefix": (workloads.SHAPES["tiny"], [(3000, 100), (2500, 1), (40, 1)]),
     "split_d128": (workloads.LayerShape(1024, 8, 2, 128, 512), [(5000, 200), (70, 1)]),
     "split_causal": (workloads.LayerShape(1024, 8, 2, 128, 512), [(0, 1500)]),
+    # more sequences than one round of the list build takes (1024 at a time in the attention entry
+    # points): 1100 short decodes, then a prompt chunk in the second round
+    "rounds_1100": (workloads.SHAPES["tiny"],
+                    [((7 * i) % 300 + (2000 if i % 10 == 0 else 0), 1) for i in range(1100)] + [(50, 130)]),
     # decode-heavy at d = 128: fused, each worker runs several decode units in a row and prefetches
     # the next one (contexts 0 mod 16, 15 mod 16 and in between)
     "decode_heavy_d128": (workloads.LayerShape(1024, 8, 2, 128, 512),
