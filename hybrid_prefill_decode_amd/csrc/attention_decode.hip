@@ -32,11 +32,11 @@ namespace {
 using hl::decode::kThreads;
 
 // One workgroup per (unit, KV head), dispatched largest unit first when the plan orders the units
-// so (Plan::dec_lpt, which shortens the launch's tail); KV head fastest, so the Hkv workgroups of a unit read the Hkv
-// adjacent pieces of each block at about the same time. (Persistent workers that
-// prefetch each next unit, as the fused launch can, were measured slower for this launch alone:
-// the hardware's dispatch of one short-lived workgroup per unit already overlaps a unit's start
-// with the streaming of the others on its compute unit.)
+// so (Plan::dec_lpt, which shortens the launch's tail); KV head fastest, so the Hkv workgroups of
+// a unit read the Hkv adjacent pieces of each block at about the same time. (Persistent workers
+// that prefetch each next unit, as the fused launch can, were measured slower for this launch
+// alone: the hardware's dispatch of one short-lived workgroup per unit already overlaps a unit's
+// start with the streaming of the others on its compute unit.)
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(hl::decode::DecodeArgs a,
                                                                   uint64_t* __restrict__ trace) {
@@ -137,8 +137,9 @@ hipError_t launch_decode_merge(const hl_layer_cfg& cfg, const int32_t* q_start, 
   const int g = cfg.n_q_heads / cfg.n_kv_heads;
   const int mu = plan.max_seq_units > 0 ? plan.max_seq_units : hl::kMaxUnitsPerSeq;
   const size_t lds = sizeof(float) * 2 * (size_t)mu * g;
-  auto kernel = cfg.head_dim == 128 ? (g <= 8 ? decode_merge_kernel<128, 8> : decode_merge_kernel<128, 16>)
-                                    : (g <= 8 ? decode_merge_kernel<64, 8> : decode_merge_kernel<64, 16>);
+  auto kernel = cfg.head_dim == 128
+                    ? (g <= 8 ? decode_merge_kernel<128, 8> : decode_merge_kernel<128, 16>)
+                    : (g <= 8 ? decode_merge_kernel<64, 8> : decode_merge_kernel<64, 16>);
   hipLaunchKernelGGL(kernel, grid, block, lds, st, q_start, plan.dec_seqs, plan.dec_part,
                      cfg.n_q_heads, cfg.n_kv_heads, mu, attn_out);
   return hipGetLastError();

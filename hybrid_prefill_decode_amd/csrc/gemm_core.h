@@ -496,10 +496,11 @@ HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot
 
 // The V rows of a staged fp32 tile into the Vᵀ pages. A page holds a head's values d-major
 // ([d][16 slots]), so one token's row is 128 two-byte stores 32 bytes apart, and a store
-// instruction costs one memory request per 32-byte piece it touches. Lanes go 16 rows by 4 d:
-// when the 16 rows are consecutive tokens of one page (a prompt chunk), an instruction writes 4
-// whole 32-byte pieces; lanes along 8-element runs of one row (as for q and k) made 16 requests
-// per instruction there. A decode row is alone in its page either way. `row_of(rr, blk, slot)`
+// instruction costs one memory request per 32-byte piece it touches. Each lane stores 8 values of
+// one row, and the lanes of one store go 16 rows by 4 adjacent d: when the 16 rows are
+// consecutive tokens of one page (a prompt chunk), an instruction writes 4 whole 32-byte pieces;
+// lanes along 8-element runs of one row (as for q and k) made 16 requests per instruction there.
+// A decode row is alone in its page either way. `row_of(rr, blk, slot)`
 // gives staged row rr's page and slot, false for a row past the end or without a page. Every
 // thread of the workgroup calls it.
 template <int HD, class RowOf>

@@ -2,8 +2,8 @@
 //
 // Each sequence is either a decode (one new token) or a prompt chunk (several new tokens at
 // offset num_cached), the two kinds a chunked-prefill iteration mixes ("Chunked prefill
-// (stall-free batching), explained", "How it works, step by step"). One workgroup classifies
-// the sequences and scans their work counts:
+// (stall-free batching), explained", "How it works, step by step"). A few workgroups (build())
+// classify the sequences, scan their work counts and write:
 //   decode unit  = (sequence, first page, decode index) covering `split_pages` KV pages, stored
 //                  in sequence order or (dec_lpt) in dispatch order (largest first, dealt
 //                  round-robin to 8 runs: dec_position), with its index in sequence order as
