@@ -8,10 +8,12 @@ head_dim 128, d_ff 28672) with one 512-token prompt chunk at prefix 8192 plus 51
 contexts are log-uniform in [1024, 32768] (seeded synthetic values; paged 16-token KV, about
 19 GB of it, with a random block table). Prints ONE JSON line.
 
-Besides the whole-step throughput it times every phase through its own entry point with HIP
-events on the launch stream (attention work lists built outside the timed launches, as the step
-builds them in its first normalisation pass), reports the dominant kernel against its roofline
-(HBM bytes for attention, matrix-core flops for a GEMM), the GEMMs against the bf16 matrix-core
+Besides the whole-step throughput it times every phase inside real steps (the same steps run
+again with the library's phase marks, HIP events it records between its kernels) and through its
+own entry point with HIP events on the launch stream (attention work lists built outside the
+timed launches, as the step builds them in its first normalisation pass), reports the dominant
+kernel against its roofline (HBM bytes for attention, matrix-core flops for a GEMM; its time
+from the phase-marked steps), the GEMMs against the bf16 matrix-core
 peak, the decode attention against HBM peak, and the fp64 oracle timed on the host cores over a
 bounded sample of the same batch as a baseline.
 """
@@ -31,6 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 SPIN_CYCLES = 2_000_000     # GPU spin between a phase's set-up and its timed launch
+# the step's phases between consecutive marks of hl_batch_desc::events
+STEP_PHASES = ("qkv_rope_append", "attention", "gemm_o", "rms_scale_mlp", "gemm_gate_up",
+               "gemm_down")
 
 
 def log(msg):
@@ -177,6 +182,9 @@ def main():
                     help="steps timed one at a time after overwriting 1 GiB (evicts the 256 MB "
                          "last-level cache), reported next to the warm steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-step-events", action="store_true",
+                    help="skip the phase-marked steps (the roofline then times the dominant "
+                         "kernel's phase launched on its own)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU-baseline budget: whole prompt chunks, then decodes until spent")
     ap.add_argument("--only-phase", default=None,
@@ -240,8 +248,8 @@ def main():
     log(f"{name}: inputs resident ({T} tokens, {spec.num_seqs} sequences, KV pools "
         f"{2 * kp.numel() * 2 / 1e9:.1f} GB)")
 
-    def step():
-        B.hybrid_layer_step(cfg, batch, x, w, kp, vp, out, ws, stream=stream)
+    def step(events=None):
+        B.hybrid_layer_step(cfg, batch, x, w, kp, vp, out, ws, stream=stream, events=events)
 
     if args.only_phase is None:
         for _ in range(args.warmup):
@@ -269,6 +277,28 @@ def main():
     clocks = gpu_clocks() if args.only_phase is None else None
     if args.only_phase is None:
         log(f"{args.steps} timed steps: {ms_step:.4f} ms per step")
+
+    # The same K steps again, back to back, each with the library's phase marks
+    # (hl_batch_desc::events: events it records on the launch stream between its kernels), for
+    # the mean time of every phase inside real steps. A mark costs a few microseconds of the
+    # stream, so `value` comes from the unmarked steps above.
+    step_phase_us = None
+    if args.only_phase is None and not args.no_step_events and args.steps > 0:
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(B.HL_STEP_EVENTS)]
+                 for _ in range(args.steps)]
+        for m in marks:
+            for e in m:
+                e.record(stream)  # torch creates an event's handle at its first record
+        torch.cuda.synchronize()
+        gc.disable()
+        for m in marks:
+            step(m)
+        torch.cuda.synchronize()
+        gc.enable()
+        step_phase_us = {
+            name: sum(m[j].elapsed_time(m[j + 1]) for m in marks) * 1000.0 / len(marks)
+            for j, name in enumerate(STEP_PHASES)}
+        log(f"in-step phases: { {k: round(v, 1) for k, v in step_phase_us.items()} }")
 
     # cold steps: the last-level cache holds nothing of the previous step
     cold = []
@@ -414,11 +444,16 @@ def main():
     pre_tflops = (cnt["prefill_attn_flops"] / (phase_us["prefill_attention"] * 1e-6) / 1e12
                   if has_pre else None)
 
-    # the dominant kernel of the step and its roofline
+    # the dominant kernel of the step and its roofline, its duration the mean inside the
+    # phase-marked steps (with --no-step-events, the phase launched on its own)
     gu_flops = cnt["gemm_flops"]["gate_up"]
     gu_tflops = gu_flops / (phase_us["gemm_gate_up"] * 1e-6) / 1e12
-    fused_us = phase_us.get("hybrid_attention") if plan["fused"] else None
-    if fused_us is not None and fused_us > phase_us["gemm_gate_up"]:
+    in_step = step_phase_us or {}
+    timed_in = "phase-marked steps" if in_step else "own launches"
+    gu_us = in_step.get("gemm_gate_up", phase_us["gemm_gate_up"])
+    fused_alone = phase_us.get("hybrid_attention") if plan["fused"] else None
+    fused_us = in_step.get("attention", fused_alone) if plan["fused"] else None
+    if fused_us is not None and fused_us > gu_us:
         att_bytes = cnt["decode_attn_bytes"] + cnt["prefill_attn_bytes"]
         gbps = att_bytes / (fused_us * 1e-6) / 1e9
         src_hash = kernel_source_hash(["attention_hybrid.hip", "attn_prefill_core.h",
@@ -434,16 +469,21 @@ def main():
             "mfma_frac": round(cnt["prefill_attn_flops"] / (fused_us * 1e-6) / 1e12
                                / PEAK_BF16_TFLOPS, 4),
             "avg_launch_us": round(fused_us, 2),
+            "avg_launch_us_alone": round(fused_alone, 2),
+            "timed_in": timed_in,
         }
     else:
         src_hash = kernel_source_hash(["gemm.hip", "gemm_core.h", "gemm_swiglu.hip", "common.h"])
         roofline = {
             "kernel": "gemm_bf16_nt<SwiGLU> (gate/up projection)",
-            "bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+            "bound": "mfma", "achieved": round(gu_flops / (gu_us * 1e-6) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gu_flops / (gu_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic(f"gemm_gate_up_{name}_pmc.txt", src_hash),
             "algorithmic_flops_per_launch": gu_flops,
-            "avg_launch_us": round(phase_us["gemm_gate_up"], 2),
+            "avg_launch_us": round(gu_us, 2),
+            "avg_launch_us_alone": round(phase_us["gemm_gate_up"], 2),
+            "timed_in": timed_in,
         }
     roofline["source_hash"] = src_hash
 
@@ -467,9 +507,16 @@ def main():
         "roofline": roofline,
         "attention_plan": plan,
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
+        "step_phases_us": ({k: round(v, 2) for k, v in step_phase_us.items()}
+                           if step_phase_us else None),
         "fused_attention_trace": trace_metrics,
         "gemm_mfma_util": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "gemm_tflops": round(gemm_tflops, 1),
+        # the same four projections timed inside the phase-marked steps (their weights cold, the
+        # first norm pass and the work lists in the QKV phase)
+        "gemm_mfma_util_in_step": (round(sum(cnt["gemm_flops"].values()) / (sum(
+            step_phase_us[k] for k in ("qkv_rope_append", "gemm_o", "gemm_gate_up", "gemm_down"))
+            * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4) if step_phase_us else None),
         "gate_up_tflops": round(gu_tflops, 1),
         # decode attention alone (the step's two-part query, its work lists prebuilt)
         "decode_attn_hbm_gbps": None if dec_gbps is None else round(dec_gbps, 1),

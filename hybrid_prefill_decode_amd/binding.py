@@ -41,7 +41,10 @@ class BatchDesc(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", ctypes.c_void_p), ("tap_q_rot", ctypes.c_void_p),
                 ("tap_attn_out", ctypes.c_void_p), ("tap_h2", ctypes.c_void_p),
-                ("attention", ctypes.c_int32)]
+                ("attention", ctypes.c_int32), ("events", ctypes.c_void_p)]
+
+
+HL_STEP_EVENTS = 7  # phase marks of hybrid_layer_step (hl_batch_desc::events)
 
 
 class Weights(ctypes.Structure):
@@ -224,8 +227,25 @@ class Batch:
         self.table = torch.from_numpy(self.h_table).to(device)
 
 
+def _event_array(events):
+    """HL_STEP_EVENTS raw hipEvent_t handles from torch.cuda.Event objects (None entries stay
+    NULL). torch creates an event's handle at its first record, so each must have been recorded
+    once."""
+    if len(events) != HL_STEP_EVENTS:
+        raise ValueError(f"events: {HL_STEP_EVENTS} entries expected, got {len(events)}")
+    arr = (ctypes.c_void_p * HL_STEP_EVENTS)()
+    for i, ev in enumerate(events):
+        if ev is None:
+            continue
+        if not ev.cuda_event:
+            raise ValueError("events: record each event once before passing it (torch creates "
+                             "the underlying hipEvent_t lazily)")
+        arr[i] = ev.cuda_event
+    return arr
+
+
 def _desc(cfg: LayerCfg, b: Batch, x=None, workspace=None, stream=None, taps=None,
-          with_stream: bool = True):
+          with_stream: bool = True, events=None):
     taps = taps or {}
     d = BatchDesc()
     d.cfg = ctypes.pointer(cfg)
@@ -243,6 +263,9 @@ def _desc(cfg: LayerCfg, b: Batch, x=None, workspace=None, stream=None, taps=Non
     d.tap_attn_out = _ptr(taps.get("attn_out"))
     d.tap_h2 = _ptr(taps.get("h2"))
     d.attention = getattr(b, "attention", 0)
+    if events is not None:
+        d._event_array = _event_array(events)  # kept alive with the descriptor
+        d.events = ctypes.cast(d._event_array, ctypes.c_void_p)
     return d
 
 
@@ -398,8 +421,10 @@ def alloc_workspace(cfg: LayerCfg, b: Batch, device="cuda"):
 
 
 def hybrid_layer_step(cfg: LayerCfg, b: Batch, x, w: Dict[str, object], k_pool, v_pool, out,
-                      workspace, stream=None, taps=None) -> None:
-    d = _desc(cfg, b, x, workspace, stream, taps)
+                      workspace, stream=None, taps=None, events=None) -> None:
+    """events: optional list of HL_STEP_EVENTS torch.cuda.Event (or None) recorded at the step's
+    phase boundaries (hl_batch_desc::events)."""
+    d = _desc(cfg, b, x, workspace, stream, taps, events=events)
     wt = _weights(w)
     kv = _pages(k_pool, v_pool)
     bt = _table(b)

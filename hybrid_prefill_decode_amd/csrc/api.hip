@@ -562,22 +562,37 @@ int run_layer(const hl_batch_desc* batch, const hl_weights* w, hl_kv_pages* kv,
   const Buffers B = buffers(batch, hp);
   int rc;
   const hl::Plan dp = device_plan(hp, batch->workspace);
+  // the caller's phase marks (hl_batch_desc::events), if any
+  auto mark = [&](int i) -> int {
+    if (!batch->events || !batch->events[i]) return HL_OK;
+    return hipEventRecord(static_cast<hipEvent_t>(batch->events[i]), st) == hipSuccess
+               ? HL_OK
+               : HL_ERR_HIP;
+  };
+  if ((rc = mark(0))) return rc;
   if ((rc = run_qkv(batch, w, B.qrot, kv, bt, B, &dp))) return rc;
+  if ((rc = mark(1))) return rc;
   if ((rc = run_attention(batch, B.qrot, B.qlo, kv, bt, B.attn, hp, true, true, true))) return rc;
+  if ((rc = mark(2))) return rc;
   if ((rc = hip_rc(hl::launch_gemm(B.attn, w->w_o, B.h2, T, c.hidden, qd,
                                    plain_epi(HL_EPI_RESIDUAL, batch->x, nullptr), B.gemm_ws,
                                    B.gemm_bytes, st))))
     return rc;
+  if ((rc = mark(3))) return rc;
   if ((rc = hip_rc(hl::launch_prep(B.h2, w->mlp_norm, B.h1, B.rs, T, c.hidden, c.rms_eps,
                                    nullptr, st))))
     return rc;
+  if ((rc = mark(4))) return rc;
   if ((rc = hip_rc(hl::launch_gemm(B.h1, w->w_gate_up, B.mlp, T, 2 * c.d_ff, c.hidden,
                                    plain_epi(HL_EPI_SWIGLU, nullptr, B.rs), B.gemm_ws,
                                    B.gemm_bytes, st))))
     return rc;
-  return hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
-                                plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
-                                B.gemm_bytes, st));
+  if ((rc = mark(5))) return rc;
+  if ((rc = hip_rc(hl::launch_gemm(B.mlp, w->w_down, out, T, c.hidden, c.d_ff,
+                                   plain_epi(HL_EPI_RESIDUAL, B.h2, nullptr), B.gemm_ws,
+                                   B.gemm_bytes, st))))
+    return rc;
+  return mark(6);
 }
 
 // Model workspace: the step's workspace, then two [T, H] residual-stream buffers, the last row of
@@ -945,6 +960,7 @@ int hl_model_step(const hl_model* m, const hl_batch_desc* batch, const int32_t* 
   inner.workspace_bytes = hp.total;
   inner.x = reinterpret_cast<hl_bf16*>(base + ml.o_x0);
   inner.tap_q_rot = inner.tap_attn_out = inner.tap_h2 = nullptr;  // per-layer tensors: not kept
+  inner.events = nullptr;                                           // phase marks: one layer only
   if ((rc = prepare(&inner, &m->kv[0], bt, &hp))) return rc;
 
   const hl_layer_cfg& c = *batch->cfg;

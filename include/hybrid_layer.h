@@ -100,8 +100,17 @@ typedef struct {
  * attention are launched when the batch has both: HL_ATTN_AUTO (0, a zero-initialised
  * descriptor) lets the library choose (hl_attention_plan reports the choice), HL_ATTN_FUSED one
  * launch for both paths, HL_ATTN_SEPARATE two launches; the results are bit-identical either way.
- * The workspace size depends on it: pass the same descriptor to hl_workspace_bytes. */
+ * The workspace size depends on it: pass the same descriptor to hl_workspace_bytes.
+ * `events`, when non-NULL, points to HL_STEP_EVENTS hipEvent_t handles (any entry may be NULL)
+ * that hybrid_layer_step (and hybrid_layer_step_noalloc) records on its stream at the boundaries
+ * of its phases, so a caller can time each phase inside real steps (hipEventElapsedTime between
+ * consecutive marks): [0] before the first norm pass (token info, work lists), [1] after the QKV
+ * projection with its RoPE / KV-append epilogue, [2] after attention (its merges included),
+ * [3] after the O projection, [4] after the MLP norm pass, [5] after the gate/up projection,
+ * [6] after the down projection. A failed record is HL_ERR_HIP; the other entry points ignore
+ * the field. */
 enum { HL_ATTN_AUTO = 0, HL_ATTN_FUSED = 1, HL_ATTN_SEPARATE = 2 };
+#define HL_STEP_EVENTS 7
 typedef struct {
   const hl_layer_cfg* cfg;
   int32_t num_seqs;
@@ -118,6 +127,7 @@ typedef struct {
   hl_bf16* tap_attn_out;       /* device, optional */
   hl_bf16* tap_h2;             /* device, optional */
   int32_t attention;           /* HL_ATTN_AUTO / HL_ATTN_FUSED / HL_ATTN_SEPARATE */
+  void* const* events;         /* optional: HL_STEP_EVENTS hipEvent_t handles (phase marks) */
 } hl_batch_desc;
 
 /* Weights, all device, row-major [out_features, in_features] (each row one output feature). */

@@ -65,9 +65,9 @@ class DeviceCase:
         }
         self.ws = B.alloc_workspace(self.cfg, self.batch, device)
 
-    def step(self, taps=True):
+    def step(self, taps=True, events=None):
         B.hybrid_layer_step(self.cfg, self.batch, self.x, self.w, self.kp, self.vp, self.out,
-                            self.ws, taps=self.taps if taps else None)
+                            self.ws, taps=self.taps if taps else None, events=events)
 
     def cached_host(self, si):
         """fp64 host copies of sequence si's cached K and V [c, Hkv, d]."""

@@ -431,3 +431,26 @@ def test_attention_run_traced_argument_checks():
     assert run(tr.data_ptr() + 8, 3 * items) == B.HL_ERR_ALIGN
     assert run(tr.data_ptr(), 3 * items - 1) == B.HL_ERR_ARG
     assert B.lib().hl_trace_clock_khz(None) == B.HL_ERR_NULL
+
+
+def test_step_events_descriptor():
+    """The step's phase marks reach the descriptor as HL_STEP_EVENTS raw handles, NULL where the
+    caller passes None; a wrong count or a never-recorded event is refused before any call."""
+    class Ev:  # stands in for torch.cuda.Event: only the raw handle is read
+        def __init__(self, h):
+            self.cuda_event = h
+    spec, b, _ = _fake_batch([(20, 4), (7, 1)])
+    cfg = B.layer_cfg(spec.shape)
+    assert B._desc(cfg, b, with_stream=False).events is None
+    evs = [Ev(0x1000 + 16 * i) if i in (1, 2, 6) else None for i in range(B.HL_STEP_EVENTS)]
+    d = B._desc(cfg, b, with_stream=False, events=evs)
+    arr = ctypes.cast(d.events, ctypes.POINTER(ctypes.c_void_p))
+    got = [arr[i] for i in range(B.HL_STEP_EVENTS)]
+    assert got == [None, 0x1010, 0x1020, None, None, None, 0x1060]
+    with pytest.raises(ValueError):
+        B._desc(cfg, b, with_stream=False, events=evs[:-1])
+    with pytest.raises(ValueError):
+        B._desc(cfg, b, with_stream=False, events=[Ev(0)] + evs[1:])
+    # the C struct ends with the events pointer, after the attention mode
+    assert B.BatchDesc._fields_[-1][0] == "events"
+    assert B.BatchDesc.events.offset >= B.BatchDesc.attention.offset + 4

@@ -697,6 +697,46 @@ def test_step_deterministic_and_block_permutation_invariant():
     assert torch.equal(bits(out1), bits(c2.out))
 
 
+def test_step_phase_events():
+    """The step's phase marks (hl_batch_desc::events): every mark is recorded, in phase order,
+    the phases add up to the whole step, a list with NULL entries records only its events, and
+    the results are bit-identical to a step without marks."""
+    say("step phase events")
+    spec = workloads.make_spec(2)
+    case = DeviceCase(spec, DEV)
+    case.step(taps=False)
+    torch.cuda.synchronize()
+    out0 = case.out.clone()
+    st = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(B.HL_STEP_EVENTS)]
+    for e in evs:
+        e.record(st)  # torch creates the handle at the first record
+    torch.cuda.synchronize()
+    case.step(taps=False, events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out0), bits(case.out))
+    phases = [evs[i].elapsed_time(evs[i + 1]) for i in range(B.HL_STEP_EVENTS - 1)]
+    whole = evs[0].elapsed_time(evs[-1])
+    say(f"phases ms {[round(p, 4) for p in phases]} whole {whole:.4f}")
+    assert all(p >= 0 for p in phases) and whole > 0
+    assert abs(sum(phases) - whole) <= 1e-3 * whole + 1e-3
+    # attention and the gate/up projection are the step's two largest phases at this size
+    assert phases[1] > 0 and phases[4] > 0
+    # only the attention bracket: the other events keep their earlier timestamps
+    old = evs[0].elapsed_time(evs[3])
+    fresh = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in fresh:
+        e.record(st)
+    torch.cuda.synchronize()
+    case.step(taps=False, events=[None, fresh[0], fresh[1], None, None, None, None])
+    torch.cuda.synchronize()
+    assert fresh[0].elapsed_time(fresh[1]) > 0
+    assert evs[0].elapsed_time(evs[3]) == old
+    assert torch.equal(bits(out0), bits(case.out))
+    with pytest.raises(ValueError):
+        case.step(taps=False, events=evs[:3])
+
+
 # ------------------------------------------------------------------------------- full sizes
 
 def _decode_sample(spec, want, seed):
