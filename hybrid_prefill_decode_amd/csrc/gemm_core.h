@@ -441,7 +441,8 @@ HL_DEV void rope_store_row(const GemmEpi& ep, int gm, int gh, int blk, int slot,
 }
 
 // The same for values already in registers: a = elements 8c .. 8c+7 of the head, b = the
-// elements d/2 apart from them (their rotation partners).
+// elements d/2 apart from them (their rotation partners). q, k and v go out as non-temporal
+// stores (store_nt): attention reads them next.
 template <int HD>
 HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot, bool decode,
                             float (&a)[8], float (&b)[8], int c) {
@@ -465,8 +466,8 @@ HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot
   };
   if (gh < Hq) {
     const size_t o = ((size_t)gm * Hq + gh) * HD + 8 * c;
-    *reinterpret_cast<u32x4*>(ep.q_rot + o) = pack8(a);
-    *reinterpret_cast<u32x4*>(ep.q_rot + o + half) = pack8(b);
+    store_nt(reinterpret_cast<u32x4*>(ep.q_rot + o), pack8(a));
+    store_nt(reinterpret_cast<u32x4*>(ep.q_rot + o + half), pack8(b));
     if (ep.q_lo && decode) {  // what bf16 dropped, so decode attention can use q to ~16 bits
       float la[8], lb[8];
 #pragma unroll
@@ -474,22 +475,22 @@ HL_DEV void rope_store_vals(const GemmEpi& ep, int gm, int gh, int blk, int slot
         la[e] = a[e] - bf2f(f2bf(a[e]));
         lb[e] = b[e] - bf2f(f2bf(b[e]));
       }
-      *reinterpret_cast<u32x4*>(ep.q_lo + o) = pack8(la);
-      *reinterpret_cast<u32x4*>(ep.q_lo + o + half) = pack8(lb);
+      store_nt(reinterpret_cast<u32x4*>(ep.q_lo + o), pack8(la));
+      store_nt(reinterpret_cast<u32x4*>(ep.q_lo + o + half), pack8(lb));
     }
     return;
   }
   if (blk < 0) return;
   if (gh < Hq + Hkv) {
     hl_bf16* page = ep.kpool + ((size_t)blk * Hkv + (gh - Hq)) * HL_BLOCK_SIZE * HD;
-    *reinterpret_cast<u32x4*>(page + kpage_off(slot, c)) = pack8(a);
-    *reinterpret_cast<u32x4*>(page + kpage_off(slot, c + HD / 16)) = pack8(b);
+    store_nt(reinterpret_cast<u32x4*>(page + kpage_off(slot, c)), pack8(a));
+    store_nt(reinterpret_cast<u32x4*>(page + kpage_off(slot, c + HD / 16)), pack8(b));
   } else {
     hl_bf16* dst = ep.vpool + ((size_t)blk * Hkv + (gh - Hq - Hkv)) * HD * HL_BLOCK_SIZE + slot;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      dst[(size_t)(8 * c + e) * HL_BLOCK_SIZE] = (hl_bf16)f2bf(a[e]);
-      dst[(size_t)(half + 8 * c + e) * HL_BLOCK_SIZE] = (hl_bf16)f2bf(b[e]);
+      store_nt(dst + (size_t)(8 * c + e) * HL_BLOCK_SIZE, (hl_bf16)f2bf(a[e]));
+      store_nt(dst + (size_t)(half + 8 * c + e) * HL_BLOCK_SIZE, (hl_bf16)f2bf(b[e]));
     }
   }
 }
@@ -526,7 +527,7 @@ HL_DEV void v_append_rows(const GemmEpi& ep, const float* st, int sstride, int r
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int d = 32 * db + 4 * j + dq;
-      dst[(size_t)d * HL_BLOCK_SIZE] = (hl_bf16)f2bf(src[d]);
+      store_nt(dst + (size_t)d * HL_BLOCK_SIZE, (hl_bf16)f2bf(src[d]));
     }
   }
 }
