@@ -63,16 +63,14 @@ constexpr float kPartialRound = 0.84f;
 // against ~2 % for the constants fitted before, which under-priced stream-K's short runs at a few
 // hundred rows and over-priced the long split runs of the 256-wide tiles. Those timings had the
 // weights warm in the last-level cache; inside a step they are cold (a layer's weights exceed that
-// cache), and split runs of the 256-wide tiles then lose less than one-tile 128-wide runs, whose
-// short k-steps hide less of the weights' HBM latency. The wide split factor is refitted on every
-// tile x schedule of the 8B / 14B / 70B O and down projections at 128..4160 rows timed with the
-// weight evicted first (20 GEMMs): 0.75 leaves 0.4 % of their total over the best schedule of
-// each, against 1.1 % with the warm fit's 0.92 (the 8B O projection at 1040 rows: 66 -> 58 us).
+// cache). The wide split factor is refitted on every tile x schedule of the 8B / 14B / 70B O and
+// down projections at 128..4160 rows timed with the weight evicted before each launch (24 GEMMs):
+// 1.0 leaves 0.23 % of their total over the best schedule of each, 0.92 1.5 %.
 struct SchedCost {
   float split_step, split_step_wide, split_fixed, piece_us_per_mb, streamk_step, streamk_fixed;
 };
 constexpr SchedCost kCostEpilogue = {1.36f, 1.36f, 11.0f, 0.05f, 1.39f, 0.0f};
-constexpr SchedCost kCostPlain = {0.9f, 0.75f, 3.0f, 0.08f, 1.1f, 5.0f};
+constexpr SchedCost kCostPlain = {0.9f, 1.0f, 3.0f, 0.08f, 1.1f, 5.0f};
 constexpr int kSplitCandidates[] = {2, 3, 4, 6, 8, 12, 16};
 constexpr int kMinSplitSteps = 4;  // k-steps of 64 per split at least
 

@@ -532,6 +532,23 @@ HL_DEV void v_append_rows(const GemmEpi& ep, const float* st, int sstride, int r
   }
 }
 
+// The residual of one 16-row block row of a lane's accumulators (rows row0 + block_row(lane, r),
+// columns col0 + 16 t + lane % 16), loaded before any of the row's stores and without branches: a
+// load that follows a store to C in program order stays behind it (the two may alias), and a
+// branch around a load waits for it before the paths join, so either costs one memory round trip
+// per load. Rows past M read row M - 1 (never stored). Raw bf16 bits; the caller converts.
+template <int NT>
+HL_DEV void load_residual_row(const GemmEpi& ep, uint32_t (&res)[4][NT], int row0, int col0,
+                              int M, int N, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const hl_bf16* p =
+        ep.residual + (size_t)min(row0 + block_row(lane, r), M - 1) * N + col0 + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) res[r][t] = p[t * 16];
+  }
+}
+
 // SK: stream-K run of (tile, k-step) iterations; otherwise exactly one tile per workgroup (kept a
 // separate instantiation so the one-tile kernels carry no loop state in registers).
 template <int EPI, int BM, int BN, int HD, bool SK>
@@ -590,7 +607,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
       }
       const int m0 = (tile % sc.mtiles) * BM, nt = tile / sc.mtiles;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        uint32_t res[4][NT];
+        if constexpr (EPI == HL_EPI_RESIDUAL)
+          load_residual_row<NT>(ep, res, m0 + wm * CF::WM + i * 16, nt * BN + wn * CF::WN, M, N,
+                                lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gm = m0 + wm * CF::WM + i * 16 + block_row(lane, r);
@@ -600,10 +621,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
           for (int t = 0; t < NT; ++t) {
             const size_t o = (size_t)gm * N + nt * BN + wn * CF::WN + t * 16 + lc;
             float v = agpr_read(acc[i][t][r]) * rs;
-            if (EPI == HL_EPI_RESIDUAL) v += bf2f(ep.residual[o]);
+            if constexpr (EPI == HL_EPI_RESIDUAL) v += bf2f(res[r][t]);
             C[o] = (hl_bf16)f2bf(v);
           }
         }
+      }
     });
     return;
   } else {
@@ -674,9 +696,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
         if (NPASS > 1) __syncthreads();
       }
     } else {
-      const hl_bf16* R = ep.residual;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        uint32_t res[4][NT];
+        if constexpr (EPI == HL_EPI_RESIDUAL)
+          load_residual_row<NT>(ep, res, m0 + wm * CF::WM + i * 16, nt * BN + wn * CF::WN, M, N,
+                                lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = wm * CF::WM + i * 16 + block_row(lane, r), gm = m0 + row;
@@ -686,10 +711,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_nt_kernel(
           for (int t = 0; t < NT; ++t) {
             const size_t o = (size_t)gm * N + nt * BN + wn * CF::WN + t * 16 + lc;
             float v = acc[i][t][r] * rs;
-            if (EPI == HL_EPI_RESIDUAL) v += bf2f(R[o]);
+            if constexpr (EPI == HL_EPI_RESIDUAL) v += bf2f(res[r][t]);
             C[o] = (hl_bf16)f2bf(v);
           }
         }
+      }
     }
   }
 }
@@ -741,6 +767,15 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
 #pragma unroll
     for (int l = 0; l < 4; ++l) v[l] += src[l];
   }
+  u32x2 rres[4];  // the residual rows, loaded before any store (see load_residual_row)
+  if (ep.kind == HL_EPI_RESIDUAL) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gm = mt * BM + row0 + r;
+      rres[r] = gm < M ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)gm * N + nt * BN + col)
+                       : u32x2{0u, 0u};
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int gm = mt * BM + row0 + r;
@@ -749,7 +784,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
     const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
     float e[4] = {v[0][r] * rs, v[1][r] * rs, v[2][r] * rs, v[3][r] * rs};
     if (ep.kind == HL_EPI_RESIDUAL) {
-      const u32x2 rr = *reinterpret_cast<const u32x2*>(ep.residual + o);
+      const u32x2 rr = rres[r];
       e[0] += bf_lo(rr[0]);
       e[1] += bf_hi(rr[0]);
       e[2] += bf_lo(rr[1]);
@@ -811,6 +846,13 @@ __global__ __launch_bounds__(256) void gemm_split_fixup(hl_bf16* __restrict__ C,
   }
   const int row0 = mt * BM + (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
   const int col = nt * BN + (w & 1) * CF::WN + t * 16 + (q & 3) * 4;
+  u32x2 rres[4];  // the residual rows, loaded before any store (see load_residual_row)
+  if (ep.kind == HL_EPI_RESIDUAL) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      rres[r] = row0 + r < M ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)(row0 + r) * N + col)
+                             : u32x2{0u, 0u};
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int gm = row0 + r;
@@ -819,7 +861,7 @@ __global__ __launch_bounds__(256) void gemm_split_fixup(hl_bf16* __restrict__ C,
     const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
     float e[4] = {v[0][r] * rs, v[1][r] * rs, v[2][r] * rs, v[3][r] * rs};
     if (ep.kind == HL_EPI_RESIDUAL) {
-      const u32x2 rr = *reinterpret_cast<const u32x2*>(ep.residual + o);
+      const u32x2 rr = rres[r];
       e[0] += bf_lo(rr[0]);
       e[1] += bf_hi(rr[0]);
       e[2] += bf_lo(rr[1]);
