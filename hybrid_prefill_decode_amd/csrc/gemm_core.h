@@ -767,21 +767,23 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(hl_bf16* __restrict__ C
 #pragma unroll
     for (int l = 0; l < 4; ++l) v[l] += src[l];
   }
-  u32x2 rres[4];  // the residual rows, loaded before any store (see load_residual_row)
-  if (ep.kind == HL_EPI_RESIDUAL) {
+  // the residual rows and row scales, loaded before any store (see load_residual_row)
+  u32x2 rres[4];
+  float rsv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int gm = mt * BM + row0 + r;
-      rres[r] = gm < M ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)gm * N + nt * BN + col)
-                       : u32x2{0u, 0u};
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int gm = min(mt * BM + row0 + r, M - 1);
+    rres[r] = ep.kind == HL_EPI_RESIDUAL
+                  ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)gm * N + nt * BN + col)
+                  : u32x2{0u, 0u};
+    rsv[r] = ep.row_scale ? ep.row_scale[gm] : 1.f;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int gm = mt * BM + row0 + r;
     if (gm >= M) break;
     const size_t o = (size_t)gm * N + nt * BN + col;
-    const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
+    const float rs = rsv[r];
     float e[4] = {v[0][r] * rs, v[1][r] * rs, v[2][r] * rs, v[3][r] * rs};
     if (ep.kind == HL_EPI_RESIDUAL) {
       const u32x2 rr = rres[r];
@@ -846,19 +848,23 @@ __global__ __launch_bounds__(256) void gemm_split_fixup(hl_bf16* __restrict__ C,
   }
   const int row0 = mt * BM + (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
   const int col = nt * BN + (w & 1) * CF::WN + t * 16 + (q & 3) * 4;
-  u32x2 rres[4];  // the residual rows, loaded before any store (see load_residual_row)
-  if (ep.kind == HL_EPI_RESIDUAL) {
+  // the residual rows and row scales, loaded before any store (see load_residual_row)
+  u32x2 rres[4];
+  float rsv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rres[r] = row0 + r < M ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)(row0 + r) * N + col)
-                             : u32x2{0u, 0u};
+  for (int r = 0; r < 4; ++r) {
+    const int gm = min(row0 + r, M - 1);
+    rres[r] = ep.kind == HL_EPI_RESIDUAL
+                  ? *reinterpret_cast<const u32x2*>(ep.residual + (size_t)gm * N + col)
+                  : u32x2{0u, 0u};
+    rsv[r] = ep.row_scale ? ep.row_scale[gm] : 1.f;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int gm = row0 + r;
     if (gm >= M) break;
     const size_t o = (size_t)gm * N + col;
-    const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
+    const float rs = rsv[r];
     float e[4] = {v[0][r] * rs, v[1][r] * rs, v[2][r] * rs, v[3][r] * rs};
     if (ep.kind == HL_EPI_RESIDUAL) {
       const u32x2 rr = rres[r];
@@ -903,11 +909,14 @@ __global__ __launch_bounds__(256) void gemm_split_swiglu_fixup(hl_bf16* __restri
   const int half_n = N >> 1;
   const int row0 = mt * BM + (w >> 1) * CF::WM + i * 16 + (q >> 2) * 4;
   const int col = nt * (BN / 2) + (w & 1) * (CF::WN / 2) + t * 16 + (q & 3) * 4;
+  float rsv[4];  // row scales loaded before any store (see load_residual_row)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rsv[r] = ep.row_scale ? ep.row_scale[min(row0 + r, M - 1)] : 1.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int gm = row0 + r;
     if (gm >= M) break;
-    const float rs = ep.row_scale ? ep.row_scale[gm] : 1.f;
+    const float rs = rsv[r];
     float e[4];
 #pragma unroll
     for (int l = 0; l < 4; ++l) e[l] = silu(vg[l][r] * rs) * (vu[l][r] * rs);
