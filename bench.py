@@ -458,11 +458,19 @@ def main():
         gbps = att_bytes / (fused_us * 1e-6) / 1e9
         src_hash = kernel_source_hash(["attention_hybrid.hip", "attn_prefill_core.h",
                                        "attn_decode_core.h", "attention_decode.hip", "common.h"])
+        # the launch's bound is the larger of its two roofline terms: bytes at the HBM peak or
+        # prefill flops at the matrix-core peak (decode-heavy batches: bytes; long prompt chunks:
+        # flops), and `frac` is taken against that one
+        tflops = cnt["prefill_attn_flops"] / (fused_us * 1e-6) / 1e12
+        by_flops = cnt["prefill_attn_flops"] / PEAK_BF16_TFLOPS > att_bytes / PEAK_HBM_GBPS * 1e3
         roofline = {
             "kernel": "hybrid_attn_kernel (fused prefill + decode attention) and the decode "
                       "merge behind it: one hl_attention_run",
-            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            **({"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "hbm_gbps": round(gbps, 1)} if by_flops else
+               {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4)}),
             "traffic": read_traffic(f"hybrid_attention_{name}_pmc.txt", src_hash),
             "algorithmic_bytes_per_launch": att_bytes,
             "mfma_flops_per_launch": cnt["prefill_attn_flops"],
