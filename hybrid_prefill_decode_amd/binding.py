@@ -45,6 +45,7 @@ class BatchDesc(ctypes.Structure):
 
 
 HL_STEP_EVENTS = 7  # phase marks of hybrid_layer_step (hl_batch_desc::events)
+HL_VERSION = 2      # the hl_batch_desc layout above (with `events`)
 
 
 class Weights(ctypes.Structure):
@@ -173,6 +174,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(handle, name)
             f.argtypes = args
             f.restype = res
+        # the descriptor structs above must match the library's layout
+        if handle.hl_version() != HL_VERSION:
+            raise RuntimeError(f"{LIB_PATH} is version {handle.hl_version()}, the binding expects "
+                               f"{HL_VERSION}: rebuild it")
         _lib = handle
     return _lib
 

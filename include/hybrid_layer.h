@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HL_VERSION 1
+#define HL_VERSION 2 /* 2: hl_batch_desc gained `events` (its layout changed) */
 #define HL_BLOCK_SIZE 16 /* tokens per KV page */
 
 enum {

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().hl_version() == 1
+    assert B.lib().hl_version() == B.HL_VERSION
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         s = B.strerror(code)
         assert isinstance(s, str) and s
