@@ -123,10 +123,13 @@ int device_cus() {
 // write and its merge read), and two workgroups run per compute unit (the kernel's register
 // budget), so `slots` units run at once. With equal-length decodes the units run in whole rounds:
 // cost = rounds * (largest unit + overhead). Otherwise the grid drains as a list schedule: cost =
-// total work / slots + a quarter of the largest unit (the tail of thousands of dispatched units
-// is far shorter than a whole unit). The constants come from timing every unit size on the 70B
-// (512 decodes log-uniform in 1K..32K) and 14B (96 decodes uniform in 2K..8K) batches: the
-// overhead is ~14 page-times, and this cost tracks those timings within 2 %. Candidates are a
+// total work / slots + a tenth of the largest unit (the tail of thousands of dispatched units,
+// dealt largest first, is far shorter than a whole unit). The constants come from timing every
+// unit size on the 70B (512 decodes log-uniform in 1K..32K) and 14B (96 decodes uniform in
+// 2K..8K) batches: the overhead is ~14 page-times. The tail share was a quarter while units ran in
+// sequence order; with the largest-first order a tenth picks 681- instead of 511-page units on the
+// 70B batch (decode 2974 -> 2962 us) and leaves the 14B one as it was (a twentieth: 2952 us, but
+// the 14B batch 6 us slower). Candidates are a
 // fixed ladder plus ceil(P_max / u) for small u (which tiles equal lengths exactly); the cheapest
 // wins, ties to the larger unit (fewer partials). No sequence may need more than
 // kMaxUnitsPerSeq units (its merge weights live in LDS).
@@ -164,7 +167,7 @@ int pick_split(const hl_batch_desc* b) {
     } else {
       double work = 0.0;
       for (int64_t p : pages) work += (double)(p + kUnitOverhead * ((p + sp - 1) / sp));
-      cost = work * (double)hkv / (double)slots + 0.25 * (double)job;
+      cost = work * (double)hkv / (double)slots + 0.1 * (double)job;
     }
     if (best_cost < 0.0 || cost < best_cost - 1e-9 || (cost <= best_cost + 1e-9 && sp > best_sp)) {
       best_cost = cost;
