@@ -335,6 +335,15 @@ def main():
     lists = lambda: B.attention_build_lists(cfg, batch, kp, vp, ws, stream)
     run = lambda paths: (lambda: B.attention_run(cfg, batch, q_rot, kp, vp, attn, ws, q_lo=q_lo,
                                                  paths=paths, stream=stream))
+    # each attention path alone as the library runs it when the two are launched separately
+    # (HL_ATTN_SEPARATE: the decode and prefill work lists sized for their own launches, as for a
+    # decode-only or prefill-only batch); the fused launch's lists are sized for the fused launch
+    batch_sep = B.Batch(spec.q_start, spec.num_cached, table, dev, attention=B.HL_ATTN_SEPARATE)
+    ws_sep = B.alloc_workspace(cfg, batch_sep, dev)
+    plan_sep = B.attention_plan(cfg, batch_sep)
+    lists_sep = lambda: B.attention_build_lists(cfg, batch_sep, kp, vp, ws_sep, stream)
+    run_sep = lambda paths: (lambda: B.attention_run(cfg, batch_sep, q_rot, kp, vp, attn, ws_sep,
+                                                     q_lo=q_lo, paths=paths, stream=stream))
     # (name, launch, set-up launched before each timed launch, outside its events)
     phases = [
         ("qkv_rope_append", lambda: B.qkv_rope_append(cfg, batch, x, w, q_rot, kp, vp, ws, stream),
@@ -342,9 +351,9 @@ def main():
         ("attention_lists", lists, None),
     ]
     if has_pre:
-        phases.append(("prefill_attention", run(B.ATTN_PREFILL), lists))
+        phases.append(("prefill_attention", run_sep(B.ATTN_PREFILL), lists_sep))
     if has_dec:
-        phases.append(("decode_attention", run(B.ATTN_DECODE), lists))
+        phases.append(("decode_attention", run_sep(B.ATTN_DECODE), lists_sep))
     if has_pre and has_dec:
         # both paths as the step runs them: one fused launch when the plan fuses, else two
         phases.append(("hybrid_attention", run(B.ATTN_BOTH), lists))
@@ -514,6 +523,7 @@ def main():
         "config": {**workloads.describe(spec), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "attention_plan": plan,
+        "attention_plan_separate": plan_sep,
         "phases_us": {k: round(v, 2) for k, v in phase_us.items()},
         "step_phases_us": ({k: round(v, 2) for k, v in step_phase_us.items()}
                            if step_phase_us else None),
@@ -526,7 +536,8 @@ def main():
             step_phase_us[k] for k in ("qkv_rope_append", "gemm_o", "gemm_gate_up", "gemm_down"))
             * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4) if step_phase_us else None),
         "gate_up_tflops": round(gu_tflops, 1),
-        # decode attention alone (the step's two-part query, its work lists prebuilt)
+        # decode attention alone (the step's two-part query; the separate path's work lists,
+        # prebuilt)
         "decode_attn_hbm_gbps": None if dec_gbps is None else round(dec_gbps, 1),
         "decode_attn_hbm_frac": None if dec_gbps is None else round(dec_gbps / PEAK_HBM_GBPS, 4),
         "prefill_attn_tflops": None if pre_tflops is None else round(pre_tflops, 1),
