@@ -470,6 +470,8 @@ def gemm_bf16_nt_tiled(a, w, c, tile_m: int, tile_n: int, stream_k: int = 0, res
 
 GEMM_TILES = ((256, 256), (224, 256), (192, 256), (160, 256), (128, 256), (256, 128), (224, 128),
               (160, 128), (128, 128))
+# SwiGLU epilogue only, one tile per workgroup (stream_k 0)
+SWIGLU_TILES = ((256, 192), (128, 192))
 
 
 def gemm_workspace_bytes(m: int, n: int, k: int, epilogue: int = HL_EPI_NONE) -> int:

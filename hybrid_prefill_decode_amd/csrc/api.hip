@@ -705,6 +705,7 @@ int hl_gemm_tile_choice(int32_t m, int32_t n, int32_t k, int32_t epilogue, int32
                  ? hl::kSchedSplitK
                  : hl::kSchedStreamK | hl::kSchedSplitK | hl::kSchedWideSplit) |
             hl::kSchedTail;
+  if (epilogue == HL_EPI_SWIGLU && !qkv_head_dim) sched |= hl::kSchedSwigluTiles;
   const hl::TileChoice tc = hl::choose_tiles(m, n, k, sched, qkv_head_dim ? qkv_head_dim : 1);
   *tile_m = tc.bm;
   *tile_n = tc.bn;
@@ -751,7 +752,7 @@ int hl_gemm_bf16_nt_tiled(const hl_bf16* a, const hl_bf16* w, hl_bf16* c,
                           void* stream) {
   const int rc = check_gemm_args(a, w, c, residual, m, n, k, epilogue);
   if (rc) return rc;
-  if (!hl::gemm_tile_supported(tile_m, tile_n) || n % tile_n) return HL_ERR_ARG;
+  if (!hl::gemm_tile_supported(tile_m, tile_n, epilogue, stream_k) || n % tile_n) return HL_ERR_ARG;
   if (stream_k == -1 || stream_k < -8) return HL_ERR_ARG;
   if (stream_k && (!workspace || workspace_bytes < hl::gemm_workspace_bytes(m, n, k, epilogue)))
     return HL_ERR_ARG;

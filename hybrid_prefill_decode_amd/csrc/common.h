@@ -219,9 +219,11 @@ constexpr int kSchedStreamK = 1, kSchedSplitK = 2, kSchedTail = 4;
 // split-K on the 256-wide tiles too, priced at the k-step cost of a one-tile run (plain and
 // residual epilogues: measured faster there, slower for SwiGLU and RoPE)
 constexpr int kSchedWideSplit = 8;
+// the 192-wide tiles (SwiGLU epilogue only, one tile per workgroup)
+constexpr int kSchedSwigluTiles = 16;
 // Tile shape and schedule of a GEMM launch (gemm.hip); col_align: N-tile widths a multiple of it.
 TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align);
-bool gemm_tile_supported(int bm, int bn);
+bool gemm_tile_supported(int bm, int bn, int epilogue, int stream_k);
 bool gemm_split_fits(int m, int n, int bm, int bn, int splits);  // pieces fit the workspace
 bool gemm_tail_fits(int m, int n, int bm, int bn, int splits);  // tail-split pieces fit it
 // few-token path (gemm_skinny.hip): split-K weight streaming with fp32 partials in the workspace

@@ -47,11 +47,13 @@ struct TileCost {
   int bm, bn;
   float kstep_us;
   bool streamk;  // also considered as a stream-K run (and, if 128 wide, as split-K)
+  bool swiglu_only = false;  // one tile per workgroup, SwiGLU epilogue only
 };
 constexpr TileCost kTiles[] = {
     {256, 256, 1.579f, true},  {224, 256, 1.473f, true},  {192, 256, 1.285f, true},
     {160, 256, 1.136f, true},  {128, 256, 0.960f, true},  {256, 128, 0.929f, false},
     {224, 128, 0.853f, false}, {160, 128, 0.631f, false}, {128, 128, 0.547f, false},
+    {256, 192, 1.40f, false, true}, {128, 192, 0.87f, false, true},
 };
 constexpr int kCUs = kStreamKGrid;
 constexpr float kPartialRound = 0.84f;
@@ -143,6 +145,10 @@ TileChoice choose_tiles(int m, int n, int k, int schedules, int col_align) {
   for (const TileCost& t : kTiles) {
     if (n % t.bn || t.bn % col_align) continue;
     const float c1 = one_tile_cost(t, m, n, nk);
+    if (t.swiglu_only) {
+      if ((schedules & kSchedSwigluTiles) && c1 < best_t) best_t = c1, best = TileChoice{t.bm, t.bn, false};
+      continue;
+    }
     if (c1 < best_t) best_t = c1, best = TileChoice{t.bm, t.bn, false};
     if (schedules & kSchedTail)
       if (const int s = tail_splits(t, m, n, nk)) {
@@ -176,9 +182,10 @@ bool gemm_tail_fits(int m, int n, int bm, int bn, int splits) {
   return tail_fits(tiles - tail_full_tiles(tiles), bm, bn, splits);
 }
 
-bool gemm_tile_supported(int bm, int bn) {
+bool gemm_tile_supported(int bm, int bn, int epilogue, int stream_k) {
   for (const TileCost& t : kTiles)
-    if (t.bm == bm && t.bn == bn) return true;
+    if (t.bm == bm && t.bn == bn)
+      return !t.swiglu_only || (epilogue == HL_EPI_SWIGLU && stream_k == 0);
   return false;
 }
 
@@ -215,8 +222,9 @@ hipError_t launch_gemm(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int32_t m
                        1),
           a, w, c, m, n, k, epi, part, st);
     case HL_EPI_SWIGLU:
-      return launch_gemm_swiglu(choose_tiles(m, n, k, part ? kSchedSplitK | kSchedTail : 0, 1), a,
-                                w, c, m, n, k, epi, part, st);
+      return launch_gemm_swiglu(
+          choose_tiles(m, n, k, kSchedSwigluTiles | (part ? kSchedSplitK | kSchedTail : 0), 1), a,
+          w, c, m, n, k, epi, part, st);
     default:
       return launch_gemm_rope(
           choose_tiles(m, n, k, part ? kSchedSplitK | kSchedTail : 0, epi.head_dim), a, w, c, m,

@@ -98,7 +98,7 @@ struct Cfg {
 // tiles have the shortest k-steps and take their weights from HBM in a model iteration, so their
 // loads get an extra k-step in flight.
 template <int BM, int BN>
-constexpr int kLoadDepth = BN == 128 ? 3 : 2;
+constexpr int kLoadDepth = (BN == 128 || (BN == 192 && BM <= 128)) ? 3 : 2;
 
 // fp32 row stride (floats) of the RoPE epilogue's LDS stage of a BN-wide tile
 template <int BN>
@@ -125,7 +125,7 @@ constexpr int read_after(int q, int nm, int nr) {
 }
 
 // One tile's K range [kb, ke) into acc (acc zeroed here).
-template <int EPI, int BM, int BN, int D = kLoadDepth<BM, BN>, bool MC = BN == 128>
+template <int EPI, int BM, int BN, int D = kLoadDepth<BM, BN>, bool MC = BN != 256>
 HL_DEV void mainloop(const hl_bf16* __restrict__ A, const hl_bf16* __restrict__ W, int M, int N,
                      int K, int mt, int nt, int kb, int ke, uint8_t* smem,
                      f32x4 (&acc)[Cfg<BM, BN>::MT][Cfg<BM, BN>::NT]) {
@@ -1093,11 +1093,15 @@ hipError_t launch_tiles(const hl_bf16* a, const hl_bf16* w, hl_bf16* c, int m, i
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a, w, c, m, n, k, epi, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (tail) return launch_split<EPI, BM, BN, HD>(a, w, c, m, n, k, epi, part, tail_splits, st, true);
-  if (!streamk) return e;
-  hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN>), dim3(tiles, BM * BN / 4096), dim3(256), 0, st,
-                     c, m, n, epi, sc);
-  return hipGetLastError();
+  if constexpr (BN == 192) {
+    return e;  // the 192-wide SwiGLU tiles run one tile per workgroup only
+  } else {
+    if (tail) return launch_split<EPI, BM, BN, HD>(a, w, c, m, n, k, epi, part, tail_splits, st, true);
+    if (!streamk) return e;
+    hipLaunchKernelGGL((gemm_fixup_kernel<BM, BN>), dim3(tiles, BM * BN / 4096), dim3(256), 0, st,
+                       c, m, n, epi, sc);
+    return hipGetLastError();
+  }
 }
 
 // Launch with the chosen tile shape: every shape below is compiled for the epilogue EPI.
@@ -1134,6 +1138,16 @@ hipError_t launch_choice(const hl::TileChoice& tc, const hl_bf16* a, const hl_bf
     case 224128: return launch_tiles<EPI, 224, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
     case 160128: return launch_tiles<EPI, 160, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
     case 128128: return launch_tiles<EPI, 128, 128, HD>(a, w, c, m, n, k, epi, part, sk, st, ts);
+    case 256192:
+    case 128192:
+      // SwiGLU only, one tile per workgroup: 96 gate + 96 up rows per tile, so that 512 and 256
+      // rows of a 2 x 12288-wide gate/up projection make exactly 256 tiles
+      if constexpr (EPI == HL_EPI_SWIGLU) {
+        if (sk || ts) return hipErrorInvalidValue;
+        return tc.bm == 256 ? launch_tiles<EPI, 256, 192, HD>(a, w, c, m, n, k, epi, part, false, st)
+                            : launch_tiles<EPI, 128, 192, HD>(a, w, c, m, n, k, epi, part, false, st);
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -394,7 +394,8 @@ int hl_gemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t epilogue, s
 
 /* hl_gemm_bf16_nt with the tile shape and schedule given by the caller instead of chosen (for
  * tuning and tests). tile_m x tile_n must be one of 256x256, 224x256, 192x256, 160x256, 128x256,
- * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0. stream_k: 0 one tile per workgroup;
+ * 256x128, 224x128, 160x128, 128x128 with n % tile_n == 0, or, for HL_EPI_SWIGLU with stream_k 0
+ * only, 256x192 or 128x192 (96 gate and 96 up rows per tile). stream_k: 0 one tile per workgroup;
  * 1 a stream-K schedule (HL_EPI_NONE / HL_EPI_RESIDUAL); s >= 2 split-K into s equal K ranges
  * (any epilogue; s <= k / 64, and the s fp32 pieces per tile must fit the workspace); -s with
  * 2 <= s <= 8 one tile per workgroup for the full rounds of tiles over the compute units and the

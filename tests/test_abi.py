@@ -206,6 +206,25 @@ def test_gemm_tiled_argument_checks():
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -9, p, big, None) == B.HL_ERR_ARG  # tail > 8
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -5, p, big, None) == B.HL_ERR_ARG  # 5 > 4 k-steps
     assert g(p, p, p, None, None, 8, 256, 256, 2, 128, 256, -2, None, 0, None) == B.HL_ERR_ARG  # no workspace
+    # the 192-wide tiles: SwiGLU only, one tile per workgroup only, N a multiple of 192
+    assert g(p, p, p, None, None, 8, 384, 256, 0, 256, 192, 0, None, 0, None) == B.HL_ERR_ARG  # plain
+    assert g(p, p, p, p, None, 8, 384, 256, 1, 128, 192, 0, None, 0, None) == B.HL_ERR_ARG  # residual
+    assert g(p, p, p, None, None, 8, 384, 256, 2, 256, 192, 2, p, big, None) == B.HL_ERR_ARG  # split
+    assert g(p, p, p, None, None, 8, 384, 256, 2, 128, 192, -2, p, big, None) == B.HL_ERR_ARG  # tail
+    assert g(p, p, p, None, None, 8, 640, 256, 2, 256, 192, 0, None, 0, None) == B.HL_ERR_ARG  # N % 192
+
+
+def test_gemm_swiglu_192_wide_choice():
+    """The 192-wide SwiGLU tiles are chosen where they make exactly one round of 256 tiles: the
+    gate/up projection of the 8B-shaped layer (N = 2 x 12288, K = 4096) at 512 and 256 rows; not
+    at 128 or 1040 rows, and never for a width they do not divide (2 x 28672)."""
+    sw = B.HL_EPI_SWIGLU
+    assert B.gemm_tile_choice(512, 24576, 4096, sw, True, 0)[:3] == (256, 192, 0)
+    assert B.gemm_tile_choice(256, 24576, 4096, sw, True, 0)[:3] == (128, 192, 0)
+    assert B.gemm_tile_choice(128, 24576, 4096, sw, True, 0)[1] != 192
+    assert B.gemm_tile_choice(1040, 24576, 4096, sw, True, 0)[1] != 192
+    assert B.gemm_tile_choice(512, 57344, 8192, sw, True, 0)[1] != 192
+    assert B.gemm_tile_choice(512, 24576, 4096, B.HL_EPI_NONE, True, 0)[1] != 192
 
 
 @pytest.mark.parametrize("epi", [B.HL_EPI_NONE, B.HL_EPI_RESIDUAL, B.HL_EPI_SWIGLU])
@@ -224,7 +243,9 @@ def test_gemm_tile_choice_is_valid(epi):
         if sk == 2:  # weight-streaming path of few token rows
             assert ws and 0 < m <= 64 and bn == 64 and bm == 16 * ((m + 15) // 16), (m, n, k)
             continue
-        assert (bm, bn) in tiles and n % bn == 0, (m, n, k, bm, bn)
+        swiglu_tile = epi == B.HL_EPI_SWIGLU and (bm, bn) in B.SWIGLU_TILES
+        assert ((bm, bn) in tiles or swiglu_tile) and n % bn == 0, (m, n, k, bm, bn)
+        assert not swiglu_tile or sk == 0, (m, n, k, bm, bn, sk)  # one tile per workgroup only
         assert (sp >= 2) == (sk in (3, 4)), (sk, sp)
         if sk == 1:
             assert ws and hd == 0 and epi != B.HL_EPI_SWIGLU and k >= 256, (m, n, k)

@@ -127,6 +127,29 @@ def test_gemm_every_tile_shape(tile, epi, stream_k):
         assert_close(f64(c), ref, f"gemm {bm}x{bn} sk={stream_k}")
 
 
+@pytest.mark.parametrize("tile", B.SWIGLU_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+def test_gemm_swiglu_192_wide_tiles(tile):
+    """The 192-wide SwiGLU tiles (96 gate and 96 up rows each), one tile per workgroup, through the
+    explicit-tile entry point: 300 rows leave a ragged last M tile and K = 320 gives an odd count
+    of 5 k-steps (the deeper load pipeline of 128 x 192 starts one step early on zeros); then the
+    gate/up projection of a 512-token chunk of the 8B-shaped layer (512 x 24576 x 4096, the shape
+    these tiles exist for), checked on 48 sampled rows. Both apply a row scale."""
+    bm, bn = tile
+    for m, n, k, rows in ((300, 768, 320, None), (512, 24576, 4096, 48)):
+        say(f"gemm swiglu tile {bm}x{bn} m={m} n={n} k={k}")
+        a = _randn((m, k), 51 + m + bm)
+        w = _randn((n, k), 52 + n + bm, 0.02)
+        rs = 0.5 + torch.rand(m, generator=torch.Generator(device=DEV).manual_seed(m), device=DEV)
+        c = torch.full((m, n // 2), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.gemm_bf16_nt_tiled(a, w, c, bm, bn, 0, None, B.HL_EPI_SWIGLU, row_scale=rs)
+        torch.cuda.synchronize()
+        idx = np.arange(m) if rows is None else np.unique(np.concatenate([
+            [0, bm - 1, bm, m - 1], np.random.default_rng(m).permutation(m)[:rows - 4]]))
+        A = f64(a)[idx] * f64(rs)[idx][:, None]
+        ref = OL.swiglu(A, f64(w), n // 2)
+        assert_close(f64(c)[idx], ref, f"swiglu gemm {bm}x{bn} m={m}")
+
+
 @pytest.mark.parametrize("tile", B.GEMM_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
 @pytest.mark.parametrize("epi,splits", [(B.HL_EPI_NONE, 2), (B.HL_EPI_RESIDUAL, 3),
                                         (B.HL_EPI_SWIGLU, 2), (B.HL_EPI_SWIGLU, 3)],
