@@ -72,7 +72,10 @@ def test_model_step_vs_oracle(case):
     mc.step()
     torch.cuda.synchronize()
     ref = mc.oracle()
-    assert_close(f64(mc.hidden), ref["hidden"], "hidden after the last layer", tol=1e-2 * layers)
+    # the per-tensor bar of one layer step holds for the hidden rows after the whole stack too
+    # (measured 6.5e-3 after 3 layers of config 1's shape, 9.3e-3 after 2 of the d = 128 one;
+    # the kernels are deterministic, so these do not vary from run to run)
+    assert_close(f64(mc.hidden), ref["hidden"], "hidden after the last layer")
     assert_close(f64(mc.logits), ref["logits"], "logits")
     got = mc.next.cpu().numpy()
     want = OM.greedy(mc.logits.float().cpu().numpy())
